@@ -1,0 +1,181 @@
+"""Throughput of the fused cascaded GEMM on one MI355X.
+
+A step is one fused cascade D = rnd(rnd(A.B0).B1)[.B2] over one batch of the
+workload (one kernel launch).  Inputs are seeded synthetic tensors already in
+HBM; the timed loop rotates over enough copies of them (>= 1 GiB in total, four
+times the 256 MB Infinity Cache) that every step reads A and writes D in HBM.
+
+Prints one JSON line: TFLOP/s of the whole job, the dominant kernel's
+roofline figures (algorithmic bytes or FLOP over its measured duration), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"f16": 2516.6e12, "bf16": 2516.6e12, "f64": 78.6e12}   # dense MFMA, FLOP/s
+HBM = 8.0e12                                                   # B/s
+ELT = {"f16": 2, "bf16": 2, "f64": 8}
+
+
+def workload_numbers(c):
+    dims, b, M = c["dims"], c["batch"], c["M"]
+    flop = 2.0 * b * M * sum(dims[s] * dims[s + 1] for s in range(len(dims) - 1))
+    e = ELT[c["dtype"]]
+    wbytes = b * sum(dims[s] * dims[s + 1] for s in range(len(dims) - 1)) * e
+    byts = b * M * dims[0] * e + wbytes + b * M * dims[-1] * e
+    return flop, byts
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2)")
+    ap.add_argument("--remap", default="auto")
+    ap.add_argument("--orient-n", action="store_true")
+    ap.add_argument("--unfused", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=1 << 30)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 disables)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the cascade shards by rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chip_fusion_amd as cf
+    import synth
+
+    c = synth.CONFIGS[args.config]
+    dt = c["dtype"]
+    flop, algo_bytes = workload_numbers(c)
+    print(f"[bench] config {args.config}: {c['name']}; generating inputs", file=sys.stderr, flush=True)
+    A, Bs = synth.make_inputs(args.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[dt]
+    R = max(1, int(np.ceil(args.rotate_bytes / set_bytes)))
+    A0 = cf.to_device(A, dt)
+    B0 = [cf.to_device(b, dt) for b in Bs]
+    sets = []
+    for r in range(R):
+        Ad = A0 if r == 0 else A0.clone()
+        Bd = B0 if r == 0 else [b.clone() for b in B0]
+        D = torch.empty((c["batch"], c["M"], c["dims"][-1]), dtype=A0.dtype, device=dev)
+        sets.append((Ad, Bd, D))
+    dims = c["dims"]
+    plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
+                   remap=args.remap, orient_n=args.orient_n, unfused=args.unfused)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        Ad, Bd, D = sets[i % R]
+        plan.run(Ad, *Bd, D=D, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup}); timing {args.steps} steps over {R} buffer sets",
+          file=sys.stderr, flush=True)
+
+    # whole timed region
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # per-launch duration of the kernel: events bracketing each launch on its stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    ai = flop / algo_bytes
+    ridge = PEAK[dt] / HBM
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": algo_bytes / (launch_ms * 1e-3) / 1e9, "peak": HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flop / (launch_ms * 1e-3) / 1e12, "peak": PEAK[dt] / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_ms"] = launch_ms
+    roof["algorithmic_bytes"] = algo_bytes
+    roof["algorithmic_flop"] = flop
+
+    # check the last buffer set against the oracle on a few rows (cheap sanity)
+    import oracle
+    rows = np.linspace(0, c["batch"] * c["M"] - 1, 64).astype(np.int64)
+    got = cf.to_host(sets[(args.steps - 1) % R][2]).reshape(-1, dims[-1])[rows]
+    ref = oracle.cascade(dt, A, Bs, rows=rows)
+    g, rf = oracle.decode(dt, got).astype(np.float64), oracle.decode(dt, ref).astype(np.float64)
+    sample_err = float(np.linalg.norm(g - rf) / np.linalg.norm(rf))
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        nthreads = len(os.sched_getaffinity(0))
+        per_row = flop / (c["batch"] * c["M"])
+        n = 2048
+        t0 = time.perf_counter()
+        oracle.cascade(dt, A, Bs, rows=np.arange(n, dtype=np.int64), nthreads=nthreads)
+        dt1 = time.perf_counter() - t0
+        n2 = int(min(c["batch"] * c["M"], max(n, n * args.cpu_seconds / max(dt1, 1e-6))))
+        idx = np.linspace(0, c["batch"] * c["M"] - 1, n2).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.cascade(dt, A, Bs, rows=idx, nthreads=nthreads)
+        el = time.perf_counter() - t0
+        cpu = {"value": n2 * per_row / el / 1e12, "unit": "TFLOP/s", "cores": nthreads,
+               "kind": "oracle", "seconds": el,
+               "sample": f"{n2} of {c['batch'] * c['M']} rows spread over all batches, full cascade per row"}
+
+    out = {
+        "metric": "fused B2B-GEMM TFLOP/s (" + dt + ") + % of MI355X dense MFMA peak, 1 GPU",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "pct_of_mfma_peak": 100.0 * value * 1e12 / PEAK[dt],
+        "config": {"workload": c["name"], "batch": c["batch"], "M": c["M"], "dims": dims,
+                   "path": "unfused" if args.unfused else "fused", "remap": args.remap,
+                   "orientation": "N" if args.orient_n else "T", "rotating_buffer_sets": R,
+                   "plan": plan.info()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sample_rel_err": sample_err,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+"""Python binding of libb2b.so, the fused cascaded-GEMM library for MI355X.
+
+Argument marshalling only: every step of the cascade runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  torch is
+imported before the library is loaded so that both share one HIP runtime.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libb2b.so")
+
+F16, BF16, F64 = 0, 1, 2
+DTYPES = {"f16": F16, "bf16": BF16, "f64": F64}
+TORCH_DTYPES = {F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64}
+REMAP = {"auto": 0, "bpermute": 1, "permlane": 2, "lds": 3, "relabel": 4}
+FLAG_UNFUSED, FLAG_ORIENT_N = 1, 2
+SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x16": 3,
+          "f16_16x16x16": 4, "f64_16x16x4": 5}
+STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
+          4: "out of memory"}
+EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_gemm_destroy", "b2b_status_string",
+           "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_probe",
+           "b2b_mfma_probe")
+
+
+class B2BError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m chip_fusion_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, u32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
+        L.b2b_gemm_create.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i64, i64, i64, i64,
+                                      ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
+        L.b2b_gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.b2b_gemm_destroy.argtypes = [vp]
+        L.b2b_status_string.argtypes = [i32]
+        L.b2b_status_string.restype = ctypes.c_char_p
+        L.b2b_gemm_get_info.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
+        L.b2b_remap_relation.argtypes = [i32, i32, vp, i64, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
+        L.b2b_remap_schedule.argtypes = [i32, i32, i32, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int32)]
+        L.b2b_remap_probe.argtypes = [i32, i32, u32, vp, vp, vp]
+        L.b2b_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
+        for n in EXPORTS:
+            if n not in ("b2b_status_string",):
+                getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(st, what):
+    if st != 0:
+        raise B2BError(st, what)
+
+
+def _stream_ptr(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """A planned cascade D = rnd(rnd(A.B0).B1)[.B2] (b2b_gemm_create)."""
+
+    def __init__(self, dtype, batch, M, K, N1, N2, N3=0, ld=None, batch_stride=None,
+                 remap="auto", orient_n=False, unfused=False):
+        self.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        self.batch, self.M, self.dims = batch, M, [K, N1, N2] + ([N3] if N3 else [])
+        flags = (REMAP[remap] << 4) | (FLAG_ORIENT_N if orient_n else 0) | (FLAG_UNFUSED if unfused else 0)
+        arr = ctypes.c_int64 * 5
+        h = ctypes.c_void_p()
+        st = lib().b2b_gemm_create(ctypes.byref(h), self.dtype, batch, M, K, N1, N2, N3,
+                                   arr(*ld) if ld is not None else None,
+                                   arr(*batch_stride) if batch_stride is not None else None, flags)
+        _check(st, "b2b_gemm_create")
+        self._h = h
+
+    def run(self, A, B0, B1, B2=None, D=None, stream=None):
+        if D is None:
+            D = torch.empty((self.batch, self.M, self.dims[-1]), dtype=A.dtype, device=A.device)
+        st = lib().b2b_gemm_run(self._h, _ptr(A), _ptr(B0), _ptr(B1), _ptr(B2), _ptr(D),
+                                _stream_ptr(stream))
+        _check(st, "b2b_gemm_run")
+        return D
+
+    def info(self):
+        buf = ctypes.create_string_buffer(512)
+        _check(lib().b2b_gemm_get_info(self._h, buf, 512), "b2b_gemm_get_info")
+        return buf.value.decode()
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().b2b_gemm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def remap_relation(shape, orient_n=False):
+    """Relation table of one remap unit and elements per lane (b2b_remap_relation)."""
+    sh = SHAPES[shape] if isinstance(shape, str) else shape
+    n = ctypes.c_int64()
+    e = ctypes.c_int32()
+    _check(lib().b2b_remap_relation(sh, int(orient_n), None, 0, ctypes.byref(n), ctypes.byref(e)),
+           "b2b_remap_relation")
+    out = np.empty(n.value, np.int32)
+    _check(lib().b2b_remap_relation(sh, int(orient_n), out.ctypes.data, n.value, ctypes.byref(n),
+                                    ctypes.byref(e)), "b2b_remap_relation")
+    return out, e.value
+
+
+def remap_schedule(shape, orient_n=False, packed=False):
+    """Coordination rounds (p, q, r), each [rounds, 64] (b2b_remap_schedule)."""
+    sh = SHAPES[shape] if isinstance(shape, str) else shape
+    rounds = ctypes.c_int32()
+    _check(lib().b2b_remap_schedule(sh, int(orient_n), int(packed), None, None, None, 0,
+                                    ctypes.byref(rounds)), "b2b_remap_schedule")
+    n = rounds.value * 64
+    p, q, r = (np.empty(n, np.int32) for _ in range(3))
+    _check(lib().b2b_remap_schedule(sh, int(orient_n), int(packed), p.ctypes.data, q.ctypes.data,
+                                    r.ctypes.data, n, ctypes.byref(rounds)), "b2b_remap_schedule")
+    return p.reshape(-1, 64), q.reshape(-1, 64), r.reshape(-1, 64)
+
+
+def remap_probe(shape, mode, inp, orient_n=False, stream=None):
+    """Runs the device rearrangement executor `mode` on payload tensor `inp`."""
+    sh = SHAPES[shape] if isinstance(shape, str) else shape
+    out = torch.empty_like(inp)
+    st = lib().b2b_remap_probe(sh, int(orient_n), REMAP[mode] << 4, _ptr(inp), _ptr(out),
+                               _stream_ptr(stream))
+    _check(st, "b2b_remap_probe")
+    return out
+
+
+def mfma_probe(shape, a, b, stream=None):
+    """One matrix instruction on raw operands a, b ([64, elems] device tensors);
+    returns the [64, 4] accumulator registers (b2b_mfma_probe)."""
+    sh = SHAPES[shape] if isinstance(shape, str) else shape
+    acc_dtype = torch.float64 if a.dtype == torch.float64 else torch.float32
+    c = torch.empty((64, 4), dtype=acc_dtype, device=a.device)
+    _check(lib().b2b_mfma_probe(sh, _ptr(a), _ptr(b), _ptr(c), _stream_ptr(stream)), "b2b_mfma_probe")
+    return c
+
+
+def to_device(x, dtype, device="cuda"):
+    """numpy input (uint16 encodings or float64) -> torch tensor of the dtype."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    if dt == F64:
+        return torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TORCH_DTYPES[dt])
+    return t.to(device)
+
+
+def to_host(t):
+    """torch tensor -> numpy (uint16 encodings for 16-bit types, float64)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float64:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)

@@ -1,0 +1,68 @@
+"""Builds libb2b.so (HIP for gfx950 only) in-tree, compiling the translation
+units in parallel.  Usage: python -m chip_fusion_amd.build [-j N] [--remarks]"""
+import argparse
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libb2b.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         # no hand-written packed-fp32 VALU ops: keep the compiler from emitting them too
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def library_path():
+    return LIB
+
+
+def _compile(src, remarks):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-x", "hip", "-c", src, "-o", obj]
+    if remarks:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
+    return obj, r.stderr
+
+
+def build(jobs=None, remarks=False, verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    plan_src = os.path.join(CSRC, "plan.cpp")
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    logs = {}
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        futs = {ex.submit(_compile, s, remarks): s for s in srcs}
+        plan_obj = os.path.join(BUILD, "plan.cpp.o")
+        subprocess.check_call(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-c", plan_src, "-o", plan_obj])
+        objs = [plan_obj]
+        for f in concurrent.futures.as_completed(futs):
+            obj, log = f.result()
+            objs.append(obj)
+            logs[futs[f]] = log
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + sorted(objs)
+                          + ["-L/opt/rocm/lib", "-lamdhip64"])
+    os.replace(tmp, LIB)
+    if verbose or remarks:
+        for s, log in sorted(logs.items()):
+            if log.strip():
+                sys.stderr.write(f"== {os.path.basename(s)}\n{log}")
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-j", type=int, default=None)
+    ap.add_argument("--remarks", action="store_true")
+    a = ap.parse_args()
+    print(build(a.j, a.remarks))

@@ -1,0 +1,386 @@
+// C ABI of the fused cascaded GEMM: planning (create), execution (run).
+//
+// Page 1 ("数据处理方法、装置、设备及介质", the apparatus of Fig. 5) splits the
+// method into an operator-determination module, a relation-determination
+// module and a rearrangement module.  Here create() is the first two -- it
+// validates the cascade, picks the kernel instance and derives the
+// rearrangement relation and its coordination rounds on the host, once --
+// and run() is the third: it only enqueues the fused kernel.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "../../include/b2b.h"
+#include "plan.hpp"
+#include "registry.hpp"
+
+namespace b2b {
+
+std::vector<KernelDesc>& registry() {
+    static std::vector<KernelDesc> r;
+    return r;
+}
+std::vector<ProbeDesc>& probe_registry() {
+    static std::vector<ProbeDesc> r;
+    return r;
+}
+std::vector<MfmaProbeDesc>& mfma_probe_registry() {
+    static std::vector<MfmaProbeDesc> r;
+    return r;
+}
+
+}  // namespace b2b
+
+using b2b::KernelDesc;
+
+struct b2b_gemm_plan {
+    int dtype = 0, nst = 0, mode = 0, orn = 0;
+    int64_t batch = 0, M = 0, dims[4] = {0, 0, 0, 0};
+    int64_t ld[5] = {0, 0, 0, 0, 0}, bs[5] = {0, 0, 0, 0, 0};
+    uint32_t flags = 0;
+    bool unfused = false;
+    const KernelDesc* fused = nullptr;          // fused path
+    const KernelDesc* stage_k[3] = {nullptr, nullptr, nullptr};   // unfused path
+    void* work[2] = {nullptr, nullptr};          // unfused intermediates
+    int64_t work_bytes[2] = {0, 0};
+    uint16_t sched[2][b2bk::kMaxRounds][64];
+    std::mutex grid_mu;
+    int grid_dev = -1, grid[3] = {0, 0, 0};
+};
+
+namespace {
+
+int elt_size(int dt) { return dt == B2B_DTYPE_F64 ? 8 : 2; }
+
+b2b::Shape shape_of(int dt) {
+    return dt == B2B_DTYPE_F64 ? b2b::SH_F64_16x16x4
+                               : (dt == B2B_DTYPE_BF16 ? b2b::SH_BF16_16x16x32 : b2b::SH_F16_16x16x32);
+}
+
+const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, int orn, int km0) {
+    for (const KernelDesc& d : b2b::registry()) {
+        if (d.dtype != dt || d.nst != nst || d.orn != orn) continue;
+        if (nst > 1 && d.mode != mode) continue;
+        if (km0 >= 0 && d.km0 != km0) continue;
+        bool ok = true;
+        for (int i = 0; i <= nst; ++i) ok = ok && d.dims[i] == dims[i];
+        if (ok) return &d;
+    }
+    return nullptr;
+}
+
+// Coordination rounds in the packed per-lane form the kernels read.
+bool make_sched(int dt, bool orn, uint16_t (&tab)[b2bk::kMaxRounds][64]) {
+    std::memset(tab, 0, sizeof tab);
+    b2b::Relation rel, use;
+    if (!b2b::build_relation(shape_of(dt), orn, &rel)) return false;
+    if (dt != B2B_DTYPE_F64 && !orn) {
+        if (!b2b::pack_relation(rel, &use)) return false;    // 16-bit pairs move together
+    } else {
+        use = rel;
+    }
+    b2b::Schedule s;
+    if (!b2b::build_schedule(use, &s) || s.rounds > b2bk::kMaxRounds) return false;
+    for (int j = 0; j < s.rounds; ++j)
+        for (int l = 0; l < 64; ++l)
+            tab[j][l] = (uint16_t)(s.p[j * 64 + l] | (s.give[j * 64 + l] << 6) | (s.r[j * 64 + l] << 9));
+    return true;
+}
+
+int pick_mode(int dt, uint32_t flags) {
+    int m = (int)((flags & B2B_REMAP_MASK) >> 4);
+    if (m != 0) return m;
+    (void)dt;
+    return b2bk::MODE_RELABEL;
+}
+
+b2b_status_t grid_for(b2b_gemm_plan* p, int idx, const KernelDesc* k, int* grid) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return B2B_ERROR_HIP;
+    std::lock_guard<std::mutex> lock(p->grid_mu);
+    if (p->grid_dev != dev) {
+        p->grid_dev = dev;
+        for (int& g : p->grid) g = 0;
+    }
+    if (p->grid[idx] == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return B2B_ERROR_HIP;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k->fn, k->threads, 0) != hipSuccess)
+            return B2B_ERROR_HIP;
+        if (per < 1) per = 1;
+        p->grid[idx] = cus * per;
+    }
+    *grid = p->grid[idx];
+    return B2B_SUCCESS;
+}
+
+b2b_status_t launch_one(b2b_gemm_plan* p, int idx, const KernelDesc* k, const void* A, int64_t lda,
+                        int64_t sA, const void* const* B, const int64_t* ldb, const int64_t* sB,
+                        void* D, int64_t ldd, int64_t sD, hipStream_t stream) {
+    b2bk::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A = A;
+    a.D = D;
+    a.M = p->M;
+    a.lda = lda;
+    a.ldd = ldd;
+    a.sA = sA;
+    a.sD = sD;
+    for (int s = 0; s < k->nst; ++s) {
+        a.B[s] = B[s];
+        a.ldb[s] = ldb[s];
+        a.sB[s] = sB[s];
+    }
+    const int64_t tpb = (p->M + k->rows_wg - 1) / k->rows_wg;
+    a.tiles_per_batch = (int32_t)tpb;
+    a.total_tiles = (int32_t)(tpb * p->batch);
+    std::memcpy(a.sched, p->sched, sizeof a.sched);
+    int grid = 0;
+    b2b_status_t st = grid_for(p, idx, k, &grid);
+    if (st != B2B_SUCCESS) return st;
+    if (grid > a.total_tiles) grid = a.total_tiles;
+    if (grid < 1) grid = 1;
+    return k->launch(a, grid, stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* b2b_status_string(b2b_status_t s) {
+    switch (s) {
+        case B2B_SUCCESS: return "success";
+        case B2B_ERROR_INVALID_VALUE: return "invalid value";
+        case B2B_ERROR_NOT_SUPPORTED: return "not supported";
+        case B2B_ERROR_HIP: return "HIP runtime error";
+        case B2B_ERROR_OUT_OF_MEMORY: return "out of memory";
+    }
+    return "unknown status";
+}
+
+b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
+                             int64_t K, int64_t N1, int64_t N2, int64_t N3, const int64_t* ld,
+                             const int64_t* batch_stride, uint32_t flags) {
+    if (!plan) return B2B_ERROR_INVALID_VALUE;
+    *plan = nullptr;
+    const int dt = (int)dtype;
+    if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
+    if (batch < 1 || M < 1 || K < 1 || N1 < 1 || N2 < 1 || N3 < 0) return B2B_ERROR_INVALID_VALUE;
+    if (batch > (int64_t)1 << 30 || M > (int64_t)1 << 31) return B2B_ERROR_INVALID_VALUE;
+    const uint32_t known = B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_REMAP_MASK;
+    if (flags & ~known) return B2B_ERROR_INVALID_VALUE;
+    const int mode = pick_mode(dt, flags);
+    if (mode > b2bk::MODE_RELABEL) return B2B_ERROR_INVALID_VALUE;
+    const int orn = (flags & B2B_FLAG_ORIENT_N) ? 1 : 0;
+    if (orn && mode != b2bk::MODE_BPERM && mode != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
+
+    const int nst = N3 > 0 ? 3 : 2;
+    const int64_t dims[4] = {K, N1, N2, N3};
+    const int64_t nlast = dims[nst];
+    const int64_t dense_ld[5] = {K, N1, N2, N3 > 0 ? N3 : 0, nlast};
+    int64_t L[5], S[5];
+    for (int i = 0; i < 5; ++i) L[i] = ld ? ld[i] : dense_ld[i];
+    if (nst == 2) L[3] = 0;
+    const int64_t rows_of[5] = {M, K, N1, N2, M};
+    const int64_t width_of[5] = {K, N1, N2, N3, nlast};
+    const int es = elt_size(dt);
+    for (int i = 0; i < 5; ++i) {
+        if (i == 3 && nst == 2) { S[i] = 0; continue; }
+        if (L[i] < width_of[i]) return B2B_ERROR_INVALID_VALUE;
+        if ((L[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
+        S[i] = batch_stride ? batch_stride[i] : rows_of[i] * L[i];
+        if (S[i] < 0 || (S[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
+    }
+    if (batch > 1 && (S[0] == 0 || S[4] < M * L[4])) return B2B_ERROR_INVALID_VALUE;
+
+    b2b_gemm_plan* p = new (std::nothrow) b2b_gemm_plan();
+    if (!p) return B2B_ERROR_OUT_OF_MEMORY;
+    p->dtype = dt;
+    p->nst = nst;
+    p->mode = mode;
+    p->orn = orn;
+    p->batch = batch;
+    p->M = M;
+    for (int i = 0; i < 4; ++i) p->dims[i] = dims[i];
+    for (int i = 0; i < 5; ++i) { p->ld[i] = L[i]; p->bs[i] = S[i]; }
+    p->flags = flags;
+    p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
+    std::memset(p->sched, 0, sizeof p->sched);
+
+    if (!p->unfused) {
+        p->fused = find_kernel(dt, nst, dims, mode, orn, -1);
+        if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        if (mode == b2bk::MODE_BPERM) {
+            if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1])) {
+                delete p;
+                return B2B_ERROR_NOT_SUPPORTED;
+            }
+        }
+    } else {
+        if (orn) { delete p; return B2B_ERROR_INVALID_VALUE; }
+        for (int s = 0; s < nst; ++s) {
+            const int64_t d2[4] = {dims[s], dims[s + 1], 0, 0};
+            const int km0 = (s == 0 && dt == B2B_DTYPE_F64) ? b2bk::KM_PAIR64 : b2bk::KM_NAT;
+            p->stage_k[s] = find_kernel(dt, 1, d2, 0, 0, km0);
+            if (!p->stage_k[s]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        }
+        for (int s = 0; s + 1 < nst; ++s) {
+            p->work_bytes[s] = batch * M * dims[s + 1] * es;
+            if (hipMalloc(&p->work[s], (size_t)p->work_bytes[s]) != hipSuccess) {
+                (void)hipGetLastError();
+                for (int t = 0; t < s; ++t) (void)hipFree(p->work[t]);
+                delete p;
+                return B2B_ERROR_OUT_OF_MEMORY;
+            }
+        }
+    }
+    *plan = p;
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const void* B1,
+                          const void* B2, void* D, void* stream) {
+    if (!p || !A || !B0 || !B1 || !D) return B2B_ERROR_INVALID_VALUE;
+    if ((p->nst == 3) != (B2 != nullptr)) return B2B_ERROR_INVALID_VALUE;
+    const void* ins[4] = {A, B0, B1, B2};
+    for (const void* q : ins)
+        if (q && ((uintptr_t)q % 16 || q == (const void*)D)) return B2B_ERROR_INVALID_VALUE;
+    if ((uintptr_t)D % 16) return B2B_ERROR_INVALID_VALUE;
+    hipStream_t s = (hipStream_t)stream;
+    const void* Bs[3] = {B0, B1, B2};
+    if (!p->unfused) {
+        const int64_t ldb[3] = {p->ld[1], p->ld[2], p->ld[3]};
+        const int64_t sB[3] = {p->bs[1], p->bs[2], p->bs[3]};
+        return launch_one(p, 0, p->fused, A, p->ld[0], p->bs[0], Bs, ldb, sB, D, p->ld[4], p->bs[4], s);
+    }
+    const void* x = A;
+    int64_t ldx = p->ld[0], sx = p->bs[0];
+    for (int st = 0; st < p->nst; ++st) {
+        const bool last = st + 1 == p->nst;
+        void* y = last ? D : p->work[st];
+        const int64_t ldy = last ? p->ld[4] : p->dims[st + 1];
+        const int64_t sy = last ? p->bs[4] : p->M * p->dims[st + 1];
+        const void* Bst[1] = {Bs[st]};
+        const int64_t ldb[1] = {p->ld[st + 1]};
+        const int64_t sB[1] = {p->bs[st + 1]};
+        b2b_status_t r = launch_one(p, st, p->stage_k[st], x, ldx, sx, Bst, ldb, sB, y, ldy, sy, s);
+        if (r != B2B_SUCCESS) return r;
+        x = y;
+        ldx = ldy;
+        sx = sy;
+    }
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {
+    if (!p) return B2B_SUCCESS;
+    b2b_status_t st = B2B_SUCCESS;
+    if (p->work[0] || p->work[1]) {
+        if (hipDeviceSynchronize() != hipSuccess) st = B2B_ERROR_HIP;
+        for (void* w : p->work)
+            if (w && hipFree(w) != hipSuccess) st = B2B_ERROR_HIP;
+    }
+    delete p;
+    return st;
+}
+
+b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
+    if (!p || !buf || len == 0) return B2B_ERROR_INVALID_VALUE;
+    static const char* dts[] = {"f16", "bf16", "f64"};
+    static const char* modes[] = {"none", "bpermute", "permlane", "lds", "relabel"};
+    const KernelDesc* k = p->unfused ? p->stage_k[0] : p->fused;
+    std::string dims = std::to_string(p->dims[0]) + "x" + std::to_string(p->dims[1]) + "x" +
+                       std::to_string(p->dims[2]) + (p->nst == 3 ? "x" + std::to_string(p->dims[3]) : "");
+    std::snprintf(buf, len,
+                  "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
+                  "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld",
+                  p->unfused ? "unfused" : "fused", dts[p->dtype], (long long)p->batch,
+                  (long long)p->M, dims.c_str(), p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : "16x16x32",
+                  p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
+                  k->rows_wg, k->lds_bytes, p->grid[0],
+                  (long long)(p->work_bytes[0] + p->work_bytes[1]));
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_remap_relation(b2b_shape_t shape, int orient_n, int32_t* rel, int64_t cap,
+                                int64_t* n_out, int32_t* elems) {
+    if ((int)shape < 0 || (int)shape >= b2b::SH_COUNT) return B2B_ERROR_INVALID_VALUE;
+    b2b::Relation r;
+    if (!b2b::build_relation((b2b::Shape)shape, orient_n != 0, &r)) return B2B_ERROR_NOT_SUPPORTED;
+    const int64_t n = (int64_t)r.src_of.size();
+    if (n_out) *n_out = n;
+    if (elems) *elems = r.elems;
+    if (rel) {
+        if (cap < n) return B2B_ERROR_INVALID_VALUE;
+        for (int64_t i = 0; i < n; ++i) rel[i] = r.src_of[i];
+    }
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_remap_schedule(b2b_shape_t shape, int orient_n, int packed, int32_t* p, int32_t* q,
+                                int32_t* r, int64_t cap, int32_t* rounds) {
+    if ((int)shape < 0 || (int)shape >= b2b::SH_COUNT) return B2B_ERROR_INVALID_VALUE;
+    b2b::Relation rel, use;
+    if (!b2b::build_relation((b2b::Shape)shape, orient_n != 0, &rel)) return B2B_ERROR_NOT_SUPPORTED;
+    if (packed) {
+        if (!b2b::pack_relation(rel, &use)) return B2B_ERROR_NOT_SUPPORTED;
+    } else {
+        use = rel;
+    }
+    b2b::Schedule s;
+    if (!b2b::build_schedule(use, &s)) return B2B_ERROR_NOT_SUPPORTED;
+    if (rounds) *rounds = s.rounds;
+    const int64_t n = (int64_t)s.rounds * 64;
+    if (p || q || r) {
+        if (cap < n) return B2B_ERROR_INVALID_VALUE;
+        for (int64_t i = 0; i < n; ++i) {
+            if (p) p[i] = s.p[i];
+            if (q) q[i] = s.q[i];
+            if (r) r[i] = s.r[i];
+        }
+    }
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, const void* in, void* out,
+                             void* stream) {
+    int dt;
+    if (shape == B2B_SHAPE_F16_16X16X32) dt = B2B_DTYPE_F16;
+    else if (shape == B2B_SHAPE_BF16_16X16X32) dt = B2B_DTYPE_BF16;
+    else if (shape == B2B_SHAPE_F64_16X16X4) dt = B2B_DTYPE_F64;
+    else return B2B_ERROR_NOT_SUPPORTED;
+    if (!in || !out) return B2B_ERROR_INVALID_VALUE;
+    const int m = (int)((mode & B2B_REMAP_MASK) >> 4);
+    if ((mode & ~(uint32_t)B2B_REMAP_MASK) || m < b2bk::MODE_BPERM || m > b2bk::MODE_RELABEL)
+        return B2B_ERROR_INVALID_VALUE;
+    const int orn = orient_n ? 1 : 0;
+    if (orn && m != b2bk::MODE_BPERM && m != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
+    b2bk::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    if (m == b2bk::MODE_BPERM && !make_sched(dt, orn != 0, a.sched[0])) return B2B_ERROR_NOT_SUPPORTED;
+    for (const b2b::ProbeDesc& d : b2b::probe_registry())
+        if (d.dtype == dt && d.mode == m && d.orn == orn)
+            return d.launch(in, out, a, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+    return B2B_ERROR_NOT_SUPPORTED;
+}
+
+b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream) {
+    int dt;
+    if (shape == B2B_SHAPE_F16_16X16X32) dt = B2B_DTYPE_F16;
+    else if (shape == B2B_SHAPE_BF16_16X16X32) dt = B2B_DTYPE_BF16;
+    else if (shape == B2B_SHAPE_F64_16X16X4) dt = B2B_DTYPE_F64;
+    else return B2B_ERROR_NOT_SUPPORTED;
+    if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
+    for (const b2b::MfmaProbeDesc& d : b2b::mfma_probe_registry())
+        if (d.dtype == dt)
+            return d.launch(a, b, c, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+    return B2B_ERROR_NOT_SUPPORTED;
+}
+
+}  // extern "C"

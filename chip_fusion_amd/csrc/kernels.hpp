@@ -1,0 +1,780 @@
+// Device code of the fused cascaded GEMM for gfx950 (CDNA4).
+//
+// Page 1 ("数据处理方法、装置、设备及介质", detailed description) fuses GEMMs
+// whose output feeds the next GEMM directly, so the intermediate never makes
+// the round trip through memory; where the first GEMM's result layout in the
+// registers differs from the layout the second GEMM needs, the result is
+// rearranged in the registers (exchange rounds scheduled by the coordination
+// matrix of Fig. 4) or through shared memory, then fed to the next GEMM.
+//
+// gfx950 realisation (one wave = 64 lanes):
+//  * every GEMM is a chain of MFMA instructions: v_mfma_f32_16x16x32_{f16,bf16}
+//    (float32 accumulation) or v_mfma_f64_16x16x4_f64;
+//  * the first GEMM is computed transposed, C0^T = B0^T . A^T, so a lane's
+//    accumulators hold (part of) one row of C0; that is the layout the next
+//    GEMM's operand wants up to a move between 16-lane rows ("orientation T").
+//    The plain orientation (C0 = A . B0, lanes hold columns) is kept as an
+//    option for the coordination-matrix and LDS executors;
+//  * the weights B0, B1 (, B2) of the current batch sit in LDS, stored in
+//    fragment-major order so that every MFMA operand read is one contiguous
+//    ds_read per lane;
+//  * each wave streams a tile of 16*MT rows of A straight from HBM into
+//    operand registers (16-byte loads, the next tile prefetched while the
+//    current one computes), runs all stages, and writes its rows of D once;
+//  * workgroups are persistent; consecutive tiles (hence mostly one batch,
+//    one copy of its weights) go to workgroups on the same XCD.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace b2bk {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef double d4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F64 = 2 };
+enum { MODE_BPERM = 1, MODE_PERMLANE = 2, MODE_LDS = 3, MODE_RELABEL = 4 };
+// How the K index of a GEMM stage is laid over (K-step, lane group, slot).
+enum {
+    KM_NAT = 0,    // the MFMA's own order: k = KW*ks + (S)*g + u
+    KM_PAIR64 = 1, // fp64 A read 16 bytes at a time: K-step 2j+e holds k = 8j + 2g + e
+    KM_REL = 2     // k follows the previous stage's accumulator layout (no data movement)
+};
+
+constexpr int kMaxRounds = 8;
+
+struct KArgs {
+    const void* A;
+    const void* B[3];
+    void* D;
+    int64_t M;
+    int64_t lda, ldb[3], ldd;
+    int64_t sA, sB[3], sD;          // batch strides, elements
+    int32_t tiles_per_batch;
+    int32_t total_tiles;
+    // coordination rounds per lane, p | give<<6 | r<<9: table 0 for the first
+    // rearrangement (after GEMM0), table 1 for the later ones
+    uint16_t sched[2][kMaxRounds][64];
+};
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+template <int DT> struct Ty;
+template <> struct Ty<DT_F16> {
+    using op_t = u4_t;
+    using acc_t = f4_t;
+    static constexpr int ELT = 2, KW = 32, FB = 16;
+    __device__ static inline f4_t mma(u4_t a, u4_t b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                      __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+    }
+    // float32 -> binary16, round to nearest even (v_cvt_f16_f32), two per dword
+    __device__ static inline unsigned pack(float x, float y) {
+        h2_t v = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(unsigned, v);
+    }
+};
+template <> struct Ty<DT_BF16> {
+    using op_t = u4_t;
+    using acc_t = f4_t;
+    static constexpr int ELT = 2, KW = 32, FB = 16;
+    __device__ static inline f4_t mma(u4_t a, u4_t b, f4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a),
+                                                       __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
+    }
+    // float32 -> bfloat16, round to nearest even
+    __device__ static inline unsigned pack(float x, float y) {
+        bf2_t v = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(unsigned, v);
+    }
+};
+template <> struct Ty<DT_F64> {
+    using op_t = double;
+    using acc_t = d4_t;
+    static constexpr int ELT = 8, KW = 4, FB = 8;
+    __device__ static inline d4_t mma(double a, double b, d4_t c) {
+        return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Buffer resources: out-of-range loads return 0 and out-of-range stores are
+// dropped, which masks the ragged last tile of M without branches.
+// ---------------------------------------------------------------------------
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ inline u4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ inline u2_t ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ inline void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, u4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ inline void st64(__amdgpu_buffer_rsrc_t r, uint32_t off, u2_t v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+
+__device__ inline u2_t dsplit(double d) { return __builtin_bit_cast(u2_t, d); }
+__device__ inline double djoin(u2_t v) { return __builtin_bit_cast(double, v); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane primitives
+//  permlane32_swap(x, y): lanes 32..63 of x trade places with lanes 0..31 of y
+//  permlane16_swap(x, y): odd 16-lane rows of x trade with even rows of y
+// ---------------------------------------------------------------------------
+__device__ inline void swap32(unsigned& x, unsigned& y) {
+    auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+__device__ inline void swap16(unsigned& x, unsigned& y) {
+    auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+
+// Two accumulator tiles of 16 columns, packed to 16-bit pairs (lane group g
+// holds columns 4g..4g+3 of each: x0,x1 from the first tile, y0,y1 from the
+// second) -> lane group g holds the 8 consecutive columns 8g..8g+7 as
+// {x0, x1, y0, y1}.  Two rounds of row swaps: 32-lane halves, then 16-lane rows.
+__device__ inline void regroup_pairs(unsigned& x0, unsigned& x1, unsigned& y0, unsigned& y1) {
+    swap32(x0, y0);
+    swap32(x1, y1);
+    swap16(x0, y0);
+    swap16(x1, y1);
+}
+
+// 4 x 4 transpose of 64-bit registers across the four 16-lane rows:
+// afterwards register s of row g holds what register g of row s held.
+__device__ inline void transpose_rows64(double (&r)[4]) {
+    unsigned w[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u2_t v = dsplit(r[i]);
+        w[0][i] = v[0];
+        w[1][i] = v[1];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        swap32(w[h][0], w[h][2]);
+        swap32(w[h][1], w[h][3]);
+        swap16(w[h][0], w[h][1]);
+        swap16(w[h][2], w[h][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = djoin(u2_t{w[0][i], w[1][i]});
+}
+
+// Coordination-matrix executor (Fig. 4): in round j every lane offers element
+// give_j of its source registers and pulls, with one ds_bpermute, the value
+// offered by lane p_j, which it files as its element r_j.  No lane is asked by
+// two lanes in one round, so each round is a single permutation of the wave.
+// Lane-dependent register choices are bitwise selects over values held in
+// registers (vectors, never arrays in memory, so nothing is indexed
+// dynamically and nothing goes to scratch).
+template <int E> struct VecU;
+template <> struct VecU<4> { typedef unsigned type __attribute__((ext_vector_type(4))); };
+template <> struct VecU<8> { typedef unsigned type __attribute__((ext_vector_type(8))); };
+
+template <int E>
+__device__ inline typename VecU<E>::type exchange32(typename VecU<E>::type src,
+                                                   typename VecU<E>::type code) {
+    typename VecU<E>::type dst = {};
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const unsigned c = code[j];
+        const unsigned give = 1u << ((c >> 6) & 7u), r = 1u << ((c >> 9) & 7u);
+        unsigned v = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v |= src[e] & (0u - ((give >> e) & 1u));
+        const unsigned got = (unsigned)__builtin_amdgcn_ds_bpermute((int)((c & 63u) << 2), (int)v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const unsigned m = 0u - ((r >> e) & 1u);
+            dst[e] = (dst[e] & ~m) | (got & m);
+        }
+    }
+    return dst;
+}
+
+// 64-bit elements: the same rounds, two ds_bpermute per round.
+__device__ inline void exchange64(const double (&src)[4], double (&dst)[4], VecU<4>::type code) {
+    VecU<8>::type s, d = {};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const u2_t w = dsplit(src[e]);
+        s[2 * e] = w[0];
+        s[2 * e + 1] = w[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const unsigned c = code[j];
+        const unsigned give = 1u << ((c >> 6) & 7u), r = 1u << ((c >> 9) & 7u);
+        unsigned lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned m = 0u - ((give >> e) & 1u);
+            lo |= s[2 * e] & m;
+            hi |= s[2 * e + 1] & m;
+        }
+        const int addr = (int)((c & 63u) << 2);
+        const unsigned glo = (unsigned)__builtin_amdgcn_ds_bpermute(addr, (int)lo);
+        const unsigned ghi = (unsigned)__builtin_amdgcn_ds_bpermute(addr, (int)hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned m = 0u - ((r >> e) & 1u);
+            d[2 * e] = (d[2 * e] & ~m) | (glo & m);
+            d[2 * e + 1] = (d[2 * e + 1] & ~m) | (ghi & m);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = djoin(u2_t{d[2 * e], d[2 * e + 1]});
+}
+
+__device__ inline void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave LDS scratch for the shared-memory rearrangement: 16 rows of one
+// unit, row pitch padded by 16 bytes to spread the rows over the banks.
+template <int DT> struct LdsRemap;
+template <> struct LdsRemap<DT_F16> { static constexpr int PITCH = 32 * 2 + 16, BYTES = 16 * PITCH; };
+template <> struct LdsRemap<DT_BF16> { static constexpr int PITCH = 32 * 2 + 16, BYTES = 16 * PITCH; };
+template <> struct LdsRemap<DT_F64> { static constexpr int PITCH = 16 * 8 + 16, BYTES = 16 * PITCH; };
+
+// ---------------------------------------------------------------------------
+// 16-bit rearrangement of one unit (two accumulator tiles -> one K-step of 32)
+// acc0/acc1: tiles 2c and 2c+1. Orientation T: lane (m = l%16, g = l/16) holds
+// row m, columns 4g..4g+3 of each tile. Orientation N: lane holds column
+// l%16, rows 4g..4g+3.  Result: lane holds row l%16, columns 8g..8g+7.
+// ---------------------------------------------------------------------------
+typedef VecU<8>::type code_t;
+
+template <int DT, int MODE, bool ORN>
+__device__ inline u4_t remap_unit16(f4_t acc0, f4_t acc1, code_t code, unsigned char* scratch,
+                                    int lane) {
+    using T = Ty<DT>;
+    if constexpr (!ORN) {
+        unsigned x0 = T::pack(acc0[0], acc0[1]), x1 = T::pack(acc0[2], acc0[3]);
+        unsigned y0 = T::pack(acc1[0], acc1[1]), y1 = T::pack(acc1[2], acc1[3]);
+        if constexpr (MODE == MODE_RELABEL) {
+            return u4_t{x0, x1, y0, y1};
+        } else if constexpr (MODE == MODE_PERMLANE) {
+            regroup_pairs(x0, x1, y0, y1);
+            return u4_t{x0, x1, y0, y1};
+        } else if constexpr (MODE == MODE_BPERM) {
+            return exchange32<4>(u4_t{x0, x1, y0, y1}, code.lo);
+        } else {
+            const int m = lane & 15, g = lane >> 4;
+            unsigned char* row = scratch + m * LdsRemap<DT>::PITCH;
+            *(u2_t*)(row + (4 * g) * 2) = u2_t{x0, x1};
+            *(u2_t*)(row + (16 + 4 * g) * 2) = u2_t{y0, y1};
+            wave_lds_fence();
+            u4_t v = *(const u4_t*)(row + 16 * g);
+            wave_lds_fence();
+            return v;
+        }
+    } else {
+        // plain orientation: every element changes lane; move single 16-bit values
+        static_assert(MODE == MODE_BPERM || MODE == MODE_LDS, "orientation N needs BPERM or LDS");
+        code_t h;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            h[v] = T::pack(acc0[v], 0.0f) & 0xFFFFu;
+            h[4 + v] = T::pack(acc1[v], 0.0f) & 0xFFFFu;
+        }
+        if constexpr (MODE == MODE_BPERM) {
+            const code_t dst = exchange32<8>(h, code);
+            return u4_t{dst[0] | (dst[1] << 16), dst[2] | (dst[3] << 16), dst[4] | (dst[5] << 16),
+                        dst[6] | (dst[7] << 16)};
+        } else {
+            const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                unsigned char* r = scratch + (4 * g + v) * LdsRemap<DT>::PITCH;
+                *(unsigned short*)(r + n * 2) = (unsigned short)h[v];
+                *(unsigned short*)(r + (16 + n) * 2) = (unsigned short)h[4 + v];
+            }
+            wave_lds_fence();
+            u4_t v = *(const u4_t*)(scratch + n * LdsRemap<DT>::PITCH + 16 * g);
+            wave_lds_fence();
+            return v;
+        }
+    }
+}
+
+// fp64 rearrangement of one accumulator tile -> four K-steps of 4.
+// The fp64 accumulator interleaves rows: register v of lane group g holds row
+// g + 4v of the tile.  Orientation T (tile = C0^T): lane (m = l%16, g) holds
+// row m of C0, columns g + 4v -- which is already what K-step v of the next
+// GEMM wants from lane group g (k = 4v + g).  The rules agree and the operator
+// fuses directly; RELABEL and PERMLANE pass the registers through, BPERM runs
+// the (identity) coordination rounds, LDS goes through memory.
+// Orientation N (tile = C0): lane holds column l%16, rows g + 4v; every
+// element changes lane.
+template <int MODE, bool ORN>
+__device__ inline void remap_unit64(d4_t acc, double (&out)[4], code_t code, unsigned char* scratch,
+                                    int lane) {
+    double r[4] = {acc[0], acc[1], acc[2], acc[3]};
+    constexpr int P = LdsRemap<DT_F64>::PITCH;
+    if constexpr (!ORN) {
+        if constexpr (MODE == MODE_RELABEL || MODE == MODE_PERMLANE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = r[i];
+        } else if constexpr (MODE == MODE_BPERM) {
+            exchange64(r, out, code.lo);
+        } else {
+            const int m = lane & 15, g = lane >> 4;
+            unsigned char* row = scratch + m * P;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) *(double*)(row + (g + 4 * v) * 8) = r[v];
+            wave_lds_fence();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) out[s] = *(const double*)(row + (4 * s + g) * 8);
+            wave_lds_fence();
+        }
+    } else {
+        static_assert(MODE == MODE_BPERM || MODE == MODE_LDS, "orientation N needs BPERM or LDS");
+        if constexpr (MODE == MODE_BPERM) {
+            exchange64(r, out, code.lo);
+        } else {
+            const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) *(double*)(scratch + (g + 4 * v) * P + n * 8) = r[v];
+            wave_lds_fence();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) out[s] = *(const double*)(scratch + n * P + (4 * s + g) * 8);
+            wave_lds_fence();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weights in LDS, fragment-major: the operand fragment (tile t, K-step ks)
+// occupies 64 lanes x FB bytes; lane l = n%16 + 16*g holds B[k(ks,g,u)][16t+n%16]
+// for its slots u.  Staging reads B row-major from global memory and scatters.
+// ---------------------------------------------------------------------------
+template <int DT, int KM>
+__device__ inline void kmap16(int k4, int* ks, int* g, int* u0) {
+    // k4: first of four consecutive k (multiple of 4); returns K-step, lane
+    // group and first slot of the run (the run stays in one lane).
+    if constexpr (KM == KM_REL) {
+        const int c = k4 >> 5, r = k4 & 31;
+        *ks = c;
+        *g = (r & 15) >> 2;
+        *u0 = (r >> 4) * 4;
+    } else {
+        *ks = k4 >> 5;
+        *g = (k4 & 31) >> 3;
+        *u0 = k4 & 7;
+    }
+}
+
+template <int KM>
+__device__ inline void kmap64(int k, int* ks, int* g) {
+    if constexpr (KM == KM_PAIR64) {
+        const int j = k >> 3, r = k & 7;
+        *g = r >> 1;
+        *ks = 2 * j + (r & 1);
+    } else if constexpr (KM == KM_REL) {
+        // the fp64 accumulator's order: K-step 4j + v, lane group g holds
+        // k = 16j + g + 4v -- the same as the natural order
+        const int j = k >> 4, r = k & 15;
+        *g = r & 3;
+        *ks = 4 * j + (r >> 2);
+    } else {
+        *ks = k >> 2;
+        *g = k & 3;
+    }
+}
+
+template <int DT, int KD, int ND, int KM, int NTHREADS>
+__device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t ldb, int tid) {
+    using T = Ty<DT>;
+    constexpr int KS = KD / T::KW;
+    if constexpr (DT != DT_F64) {
+        // unit: 4 consecutive rows x 8 consecutive columns
+        constexpr int UN = ND / 8, UNITS = (KD / 4) * UN;
+        const unsigned short* B = (const unsigned short*)Bg;
+        for (int u = tid; u < UNITS; u += NTHREADS) {
+            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
+            u4_t r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
+            int ks, g, u0;
+            kmap16<DT, KM>(k4, &ks, &g, &u0);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int n = n0 + c, t = n >> 4;
+                const int sh = (c & 1) * 16;
+                const unsigned e0 = (r[0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[1][c >> 1] >> sh) & 0xFFFFu;
+                const unsigned e2 = (r[2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[3][c >> 1] >> sh) & 0xFFFFu;
+                const int lane = (n & 15) + 16 * g;
+                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) =
+                    u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+            }
+        }
+    } else {
+        constexpr int UN = ND / 2, UNITS = KD * UN;
+        const double* B = (const double*)Bg;
+        for (int u = tid; u < UNITS; u += NTHREADS) {
+            const int k = u / UN, n0 = (u % UN) * 2;
+            const u4_t v = *(const u4_t*)(B + (int64_t)k * ldb + n0);
+            int ks, g;
+            kmap64<KM>(k, &ks, &g);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
+                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{v[2 * c], v[2 * c + 1]};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Compile-time configuration of one kernel instance.
+// ---------------------------------------------------------------------------
+template <int DT_, int NST_, int D0, int D1, int D2, int D3, int MODE_, bool ORN_, int MT_,
+          int WAVES_, int KM0_ = (DT_ == DT_F64 ? KM_PAIR64 : KM_NAT)>
+struct Cfg {
+    static constexpr int DT = DT_, NST = NST_, MODE = MODE_, MT = MT_, WAVES = WAVES_;
+    static constexpr bool ORN = ORN_;
+    static constexpr int KM0 = KM0_;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS_WAVE = 16 * MT, ROWS_WG = ROWS_WAVE * WAVES;
+    static constexpr int dim(int i) { return i == 0 ? D0 : i == 1 ? D1 : i == 2 ? D2 : D3; }
+    static constexpr int KW = Ty<DT>::KW, FB = Ty<DT>::FB, ELT = Ty<DT>::ELT;
+    static constexpr int KS(int s) { return dim(s) / KW; }
+    static constexpr int NT(int s) { return dim(s + 1) / 16; }
+    static constexpr int wbytes(int s) { return s < NST ? NT(s) * KS(s) * 64 * FB : 0; }
+    static constexpr int woff(int s) { return s == 0 ? 0 : woff(s - 1) + wbytes(s - 1); }
+    static constexpr int WBYTES = woff(3) + 0;
+    static constexpr bool USES_SCRATCH = (MODE == MODE_LDS) && NST > 1;
+    static constexpr int SCRATCH = USES_SCRATCH ? WAVES * LdsRemap<DT>::BYTES : 0;
+    static constexpr int LDS_BYTES = WBYTES + SCRATCH;
+    static constexpr int KMS(int s) { return s == 0 ? KM0 : (MODE == MODE_RELABEL ? KM_REL : KM_NAT); }
+    static constexpr int NLAST = dim(NST);
+    static_assert(LDS_BYTES <= 160 * 1024, "weights do not fit in LDS");
+    static_assert(DT == DT_F64 || D0 % 32 == 0, "K must be a multiple of 32");
+    static_assert(DT != DT_F64 || D0 % 8 == 0, "fp64 K must be a multiple of 8");
+};
+
+// A operand tile of one wave: MT sub-tiles of 16 rows, all K-steps.
+template <class C>
+__device__ inline void load_a(typename Ty<C::DT>::op_t (&a)[C::MT][C::KS(0)],
+                              __amdgpu_buffer_rsrc_t rs, int64_t lda, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+    if constexpr (C::DT != DT_F64) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < C::KS(0); ++ks)
+                a[mt][ks] = ld128(rs, (uint32_t)(((16 * mt + m) * lda + 32 * ks + 8 * g) * 2));
+    } else if constexpr (C::KM0 == KM_PAIR64) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < C::dim(0) / 8; ++j) {
+                const u4_t v = ld128(rs, (uint32_t)(((16 * mt + m) * lda + 8 * j + 2 * g) * 8));
+                a[mt][2 * j] = djoin(u2_t{v[0], v[1]});
+                a[mt][2 * j + 1] = djoin(u2_t{v[2], v[3]});
+            }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < C::KS(0); ++ks)
+                a[mt][ks] = djoin(ld64(rs, (uint32_t)(((16 * mt + m) * lda + 4 * ks + g) * 8)));
+    }
+}
+
+// One GEMM stage on MFMA: acc[mt][t] = sum_ks W_s(t, ks) (x) op[mt][ks].
+template <class C, int S, bool ORN_STAGE>
+__device__ inline void gemm_stage(const unsigned char* lds,
+                                  const typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S)],
+                                  typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)], int lane) {
+    using T = Ty<C::DT>;
+    using op_t = typename T::op_t;
+    const unsigned char* w = lds + C::woff(S) + lane * C::FB;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < C::NT(S); ++t) acc[mt][t] = typename T::acc_t{};
+#pragma unroll
+    for (int t = 0; t < C::NT(S); ++t)
+#pragma unroll
+        for (int ks = 0; ks < C::KS(S); ++ks) {
+            const op_t bw = *(const op_t*)(w + (t * C::KS(S) + ks) * 64 * C::FB);
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) {
+                if constexpr (ORN_STAGE)
+                    acc[mt][t] = T::mma(op[mt][ks], bw, acc[mt][t]);   // C0 = A . B0
+                else
+                    acc[mt][t] = T::mma(bw, op[mt][ks], acc[mt][t]);   // C^T = W^T . X^T
+            }
+        }
+}
+
+// Stage output -> operands of the next stage (round, then rearrange).
+template <class C, int S, bool ORN_STAGE>
+__device__ inline void to_operands(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)],
+                                   typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S + 1)],
+                                   code_t code, unsigned char* scratch, int lane) {
+    if constexpr (C::DT != DT_F64) {
+        static_assert(C::NT(S) % 2 == 0, "intermediate width must be a multiple of 32");
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int c = 0; c < C::NT(S) / 2; ++c)
+                op[mt][c] = remap_unit16<C::DT, C::MODE, ORN_STAGE>(acc[mt][2 * c], acc[mt][2 * c + 1],
+                                                                   code, scratch, lane);
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < C::NT(S); ++t) {
+                double o[4];
+                remap_unit64<C::MODE, ORN_STAGE>(acc[mt][t], o, code, scratch, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) op[mt][4 * t + i] = o[i];
+            }
+    }
+}
+
+// Final stage output -> D (rounded), 16 bytes per lane per store.
+template <class C, int S>
+__device__ inline void store_d(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)],
+                               __amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+    if constexpr (C::DT != DT_F64) {
+        using T = Ty<C::DT>;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+            for (int c = 0; c < C::NT(S) / 2; ++c) {
+                const f4_t a0 = acc[mt][2 * c], a1 = acc[mt][2 * c + 1];
+                unsigned x0 = T::pack(a0[0], a0[1]), x1 = T::pack(a0[2], a0[3]);
+                unsigned y0 = T::pack(a1[0], a1[1]), y1 = T::pack(a1[2], a1[3]);
+                regroup_pairs(x0, x1, y0, y1);
+                st128(rs, (uint32_t)(((16 * mt + m) * ldd + 32 * c + 8 * g) * 2), u4_t{x0, x1, y0, y1});
+            }
+            if constexpr (C::NT(S) % 2) {
+                constexpr int t = C::NT(S) - 1;
+                const f4_t a0 = acc[mt][t];
+                st64(rs, (uint32_t)(((16 * mt + m) * ldd + 16 * t + 4 * g) * 2),
+                     u2_t{T::pack(a0[0], a0[1]), T::pack(a0[2], a0[3])});
+            }
+        }
+    } else {
+        // lane group g holds columns g + 4v; regroup to 4g + v (32 contiguous bytes)
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < C::NT(S); ++t) {
+                double a[4] = {acc[mt][t][0], acc[mt][t][1], acc[mt][t][2], acc[mt][t][3]};
+                transpose_rows64(a);
+                const uint32_t off = (uint32_t)(((16 * mt + m) * ldd + 16 * t + 4 * g) * 8);
+                const u2_t p0 = dsplit(a[0]), p1 = dsplit(a[1]), p2 = dsplit(a[2]), p3 = dsplit(a[3]);
+                st128(rs, off, u4_t{p0[0], p0[1], p1[0], p1[1]});
+                st128(rs, off + 16, u4_t{p2[0], p2[1], p3[0], p3[1]});
+            }
+    }
+}
+
+template <class C>
+__device__ inline void stage_all_weights(unsigned char* lds, const KArgs& args, int b, int tid) {
+    stage_weights<C::DT, C::dim(0), C::dim(1), C::KMS(0), C::THREADS>(
+        lds + C::woff(0), (const char*)args.B[0] + (int64_t)b * args.sB[0] * C::ELT, args.ldb[0], tid);
+    if constexpr (C::NST > 1)
+        stage_weights<C::DT, C::dim(1), C::dim(2), C::KMS(1), C::THREADS>(
+            lds + C::woff(1), (const char*)args.B[1] + (int64_t)b * args.sB[1] * C::ELT, args.ldb[1], tid);
+    if constexpr (C::NST > 2)
+        stage_weights<C::DT, C::dim(2), C::dim(3), C::KMS(2), C::THREADS>(
+            lds + C::woff(2), (const char*)args.B[2] + (int64_t)b * args.sB[2] * C::ELT, args.ldb[2], tid);
+}
+
+// ---------------------------------------------------------------------------
+// The fused kernel: persistent workgroups over tiles of ROWS_WG rows.
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
+    using T = Ty<C::DT>;
+    using op_t = typename T::op_t;
+    using acc_t = typename T::acc_t;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned char* scratch = lds + C::WBYTES + (C::USES_SCRATCH ? wave * LdsRemap<C::DT>::BYTES : 0);
+
+    code_t code = {}, code2 = {};
+    if constexpr (C::MODE == MODE_BPERM && C::NST > 1) {
+#pragma unroll
+        for (int j = 0; j < kMaxRounds; ++j) {
+            code[j] = args.sched[0][j][lane];
+            code2[j] = args.sched[1][j][lane];
+        }
+    }
+
+    // XCD-aware order: block i runs on XCD i % 8; give each XCD a contiguous
+    // range of logical workgroups (hence of tiles and batches).
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+    const int t0 = (int)((int64_t)args.total_tiles * lid / G);
+    const int t1 = (int)((int64_t)args.total_tiles * (lid + 1) / G);
+    if (t0 >= t1) return;
+
+    const int TB = args.tiles_per_batch;
+    auto a_rsrc = [&](int t) {
+        const int b = t / TB;
+        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        int64_t rows = args.M - row0;
+        rows = rows < 0 ? 0 : (rows > C::ROWS_WAVE ? C::ROWS_WAVE : rows);
+        const char* base = (const char*)args.A + ((int64_t)b * args.sA + (rows ? row0 : 0) * args.lda) * C::ELT;
+        return make_rsrc(base, (uint32_t)(rows * args.lda * C::ELT));
+    };
+
+    op_t a_cur[C::MT][C::KS(0)];
+    load_a<C>(a_cur, a_rsrc(t0), args.lda, lane);
+    int cur_b = -1;
+    for (int t = t0; t < t1; ++t) {
+        const int b = t / TB;
+        op_t a_nxt[C::MT][C::KS(0)];
+        if (t + 1 < t1) load_a<C>(a_nxt, a_rsrc(t + 1), args.lda, lane);
+        if (b != cur_b) {
+            __syncthreads();
+            stage_all_weights<C>(lds, args, b, tid);
+            __syncthreads();
+            cur_b = b;
+        }
+        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        int64_t rows = args.M - row0;
+        rows = rows < 0 ? 0 : (rows > C::ROWS_WAVE ? C::ROWS_WAVE : rows);
+        const auto d_rs = make_rsrc(
+            (char*)args.D + ((int64_t)b * args.sD + (rows ? row0 : 0) * args.ldd) * C::ELT,
+            (uint32_t)(rows * args.ldd * C::ELT));
+
+        acc_t acc0[C::MT][C::NT(0)];
+        gemm_stage<C, 0, C::ORN>(lds, a_cur, acc0, lane);
+        if constexpr (C::NST == 1) {
+            store_d<C, 0>(acc0, d_rs, args.ldd, lane);
+        } else {
+            op_t op1[C::MT][C::KS(1)];
+            to_operands<C, 0, C::ORN>(acc0, op1, code, scratch, lane);
+            acc_t acc1[C::MT][C::NT(1)];
+            gemm_stage<C, 1, false>(lds, op1, acc1, lane);
+            if constexpr (C::NST == 2) {
+                store_d<C, 1>(acc1, d_rs, args.ldd, lane);
+            } else {
+                op_t op2[C::MT][C::KS(2)];
+                to_operands<C, 1, false>(acc1, op2, code2, scratch, lane);
+                acc_t acc2[C::MT][C::NT(2)];
+                gemm_stage<C, 2, false>(lds, op2, acc2, lane);
+                store_d<C, 2>(acc2, d_rs, args.ldd, lane);
+            }
+        }
+        if (t + 1 < t1) {
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < C::KS(0); ++ks) a_cur[mt][ks] = a_nxt[mt][ks];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Probe: one remap unit on index payloads, through the same executors.
+// in/out: 64 lanes x E elements (uint16 for 16-bit types, uint64 for fp64).
+// ---------------------------------------------------------------------------
+template <int DT, int MODE, bool ORN>
+__global__ __launch_bounds__(64) void remap_probe_kernel(const void* in, void* out, KArgs args) {
+    __shared__ __attribute__((aligned(16))) unsigned char scratch[LdsRemap<DT>::BYTES];
+    const int lane = threadIdx.x;
+    code_t code;
+#pragma unroll
+    for (int j = 0; j < kMaxRounds; ++j) code[j] = args.sched[0][j][lane];
+    if constexpr (DT != DT_F64) {
+        const unsigned short* x = (const unsigned short*)in + lane * 8;
+        unsigned w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = x[2 * i] | ((unsigned)x[2 * i + 1] << 16);
+        u4_t v;
+        if constexpr (!ORN) {
+            // feed the pre-packed pairs through the same network as the kernel
+            unsigned x0 = w[0], x1 = w[1], y0 = w[2], y1 = w[3];
+            if constexpr (MODE == MODE_RELABEL) {
+                v = u4_t{x0, x1, y0, y1};
+            } else if constexpr (MODE == MODE_PERMLANE) {
+                regroup_pairs(x0, x1, y0, y1);
+                v = u4_t{x0, x1, y0, y1};
+            } else if constexpr (MODE == MODE_BPERM) {
+                v = exchange32<4>(u4_t{x0, x1, y0, y1}, code.lo);
+            } else {
+                const int m = lane & 15, g = lane >> 4;
+                unsigned char* row = scratch + m * LdsRemap<DT>::PITCH;
+                *(u2_t*)(row + (4 * g) * 2) = u2_t{x0, x1};
+                *(u2_t*)(row + (16 + 4 * g) * 2) = u2_t{y0, y1};
+                wave_lds_fence();
+                v = *(const u4_t*)(row + 16 * g);
+            }
+        } else {
+            code_t h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = x[i];
+            if constexpr (MODE == MODE_BPERM) {
+                const code_t dst = exchange32<8>(h, code);
+                v = u4_t{dst[0] | (dst[1] << 16), dst[2] | (dst[3] << 16), dst[4] | (dst[5] << 16),
+                         dst[6] | (dst[7] << 16)};
+            } else {
+                const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    unsigned char* r = scratch + (4 * g + q) * LdsRemap<DT>::PITCH;
+                    *(unsigned short*)(r + n * 2) = (unsigned short)h[q];
+                    *(unsigned short*)(r + (16 + n) * 2) = (unsigned short)h[4 + q];
+                }
+                wave_lds_fence();
+                v = *(const u4_t*)(scratch + n * LdsRemap<DT>::PITCH + 16 * g);
+            }
+        }
+        *(u4_t*)((unsigned short*)out + lane * 8) = v;
+    } else {
+        const double* x = (const double*)in + lane * 4;
+        d4_t acc = {x[0], x[1], x[2], x[3]};
+        double o[4];
+        remap_unit64<MODE, ORN>(acc, o, code, scratch, lane);
+        double* y = (double*)out + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = o[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Probe: one MFMA on raw operand registers; writes the accumulator registers
+// of every lane (64 x C elements).  Used to confirm the layout catalogue.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(64) void mfma_probe_kernel(const void* a, const void* b, void* c) {
+    const int lane = threadIdx.x;
+    using T = Ty<DT>;
+    if constexpr (DT != DT_F64) {
+        const u4_t av = ((const u4_t*)a)[lane], bv = ((const u4_t*)b)[lane];
+        ((f4_t*)c)[lane] = T::mma(av, bv, f4_t{0.f, 0.f, 0.f, 0.f});
+    } else {
+        const double av = ((const double*)a)[lane], bv = ((const double*)b)[lane];
+        ((d4_t*)c)[lane] = T::mma(av, bv, d4_t{0.0, 0.0, 0.0, 0.0});
+    }
+}
+
+}  // namespace b2bk

@@ -1,0 +1,94 @@
+// Table of compiled kernel instances (one per dtype / shape / rearrangement).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace b2b {
+
+struct KernelDesc {
+    int dtype, nst, dims[4], mode, orn, km0;
+    int mt, waves, threads, rows_wg, lds_bytes;
+    const void* fn;   // the __global__ function, for occupancy queries
+    hipError_t (*launch)(const b2bk::KArgs&, int grid, hipStream_t);
+};
+
+std::vector<KernelDesc>& registry();
+
+struct Registrar {
+    explicit Registrar(const KernelDesc& d) { registry().push_back(d); }
+};
+
+template <class C>
+KernelDesc describe() {
+    KernelDesc d;
+    d.dtype = C::DT;
+    d.nst = C::NST;
+    for (int i = 0; i < 4; ++i) d.dims[i] = i <= C::NST ? C::dim(i) : 0;
+    d.mode = C::NST > 1 ? C::MODE : 0;
+    d.orn = C::ORN ? 1 : 0;
+    d.km0 = C::KM0;
+    d.mt = C::MT;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::ROWS_WG;
+    d.lds_bytes = C::LDS_BYTES;
+    d.fn = (const void*)&b2bk::fused_kernel<C>;
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        hipLaunchKernelGGL(b2bk::fused_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+// Probe instances of the rearrangement executors.
+struct ProbeDesc {
+    int dtype, mode, orn;
+    hipError_t (*launch)(const void*, void*, const b2bk::KArgs&, hipStream_t);
+};
+std::vector<ProbeDesc>& probe_registry();
+struct ProbeRegistrar {
+    explicit ProbeRegistrar(const ProbeDesc& d) { probe_registry().push_back(d); }
+};
+struct MfmaProbeDesc {
+    int dtype;
+    hipError_t (*launch)(const void*, const void*, void*, hipStream_t);
+};
+std::vector<MfmaProbeDesc>& mfma_probe_registry();
+struct MfmaProbeRegistrar {
+    explicit MfmaProbeRegistrar(const MfmaProbeDesc& d) { mfma_probe_registry().push_back(d); }
+};
+template <int DT>
+MfmaProbeDesc describe_mfma_probe() {
+    MfmaProbeDesc d;
+    d.dtype = DT;
+    d.launch = [](const void* a, const void* b, void* c, hipStream_t s) -> hipError_t {
+        hipLaunchKernelGGL(b2bk::mfma_probe_kernel<DT>, dim3(1), dim3(64), 0, s, a, b, c);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+template <int DT, int MODE, bool ORN>
+ProbeDesc describe_probe() {
+    ProbeDesc d;
+    d.dtype = DT;
+    d.mode = MODE;
+    d.orn = ORN ? 1 : 0;
+    d.launch = [](const void* in, void* out, const b2bk::KArgs& a, hipStream_t s) -> hipError_t {
+        hipLaunchKernelGGL((b2bk::remap_probe_kernel<DT, MODE, ORN>), dim3(1), dim3(64), 0, s, in, out, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+}  // namespace b2b
+
+#define B2B_CAT2(a, b) a##b
+#define B2B_CAT(a, b) B2B_CAT2(a, b)
+// B2B_INSTANCE(dtype, stages, K, N1, N2, N3, mode, orientN, MT, waves, kmap0)
+#define B2B_INSTANCE(...)                                                              \
+    static ::b2b::Registrar B2B_CAT(b2b_reg_, __LINE__)(                               \
+        ::b2b::describe<::b2bk::Cfg<__VA_ARGS__>>())

@@ -1,0 +1,183 @@
+/*
+ * b2b.h -- C ABI of the fused cascaded ("back-to-back") GEMM library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page 1, "数据处理方法、装置、设备及介质", detailed description:
+ * the definition of cascaded GEMM as several GEMM operators fused into one,
+ * and the note that three or more operators may be fused):
+ *
+ *     D[b] = rnd( rnd( A[b] . B0[b] ) . B1[b] )                 (N3 == 0)
+ *     D[b] = rnd( rnd( rnd( A[b] . B0[b] ) . B1[b] ) . B2[b] )   (N3 >  0)
+ *
+ * for b in [0, batch).  Nothing sits between the operators (no scale, bias or
+ * activation; the pages fuse operators whose output feeds the next input
+ * directly).  Accumulation is float32 for fp16/bf16 inputs and float64 for
+ * fp64; rnd rounds to nearest-even into the input type (identity for fp64).
+ * The intermediates never leave the chip: the first GEMM's accumulator
+ * fragment is rearranged in registers (cross-lane exchange) or through LDS
+ * into the operand layout of the next GEMM (page 1: the rearrangement
+ * relation, the coordination matrix of Fig. 4, and the shared-memory variant).
+ *
+ * Shapes: A is M x K, B0 is K x N1, B1 is N1 x N2, B2 is N2 x N3, D is M x N_last
+ * (N_last = N3 if N3 > 0 else N2).  All matrices are row-major with leading
+ * dimensions in elements; batches are strided by batch_stride elements
+ * (0 broadcasts a weight matrix to every batch; A and D must not use 0).
+ *
+ * Ownership: the caller owns every matrix and the stream.  A plan owns only
+ * host tables and, with B2B_FLAG_UNFUSED, a device workspace for the
+ * intermediates that b2b_gemm_create allocates and b2b_gemm_destroy frees.
+ *
+ * Errors: every call returns a status and never aborts; on failure of create
+ * *plan is set to NULL.  b2b_gemm_run only enqueues work on the stream and
+ * never synchronises; launch failures are reported as B2B_ERROR_HIP, faults
+ * inside a kernel are not detectable at the call.
+ */
+#ifndef B2B_H_
+#define B2B_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    B2B_DTYPE_F16 = 0,   /* IEEE binary16 inputs and outputs, float32 accumulation */
+    B2B_DTYPE_BF16 = 1,  /* bfloat16 inputs and outputs, float32 accumulation */
+    B2B_DTYPE_F64 = 2    /* binary64 throughout */
+} b2b_dtype_t;
+
+typedef enum {
+    B2B_SUCCESS = 0,
+    B2B_ERROR_INVALID_VALUE = 1,  /* bad dimension, leading dimension, pointer or alignment */
+    B2B_ERROR_NOT_SUPPORTED = 2,  /* the cascade cannot be fused with this dtype/shape/mode */
+    B2B_ERROR_HIP = 3,            /* a HIP runtime call failed */
+    B2B_ERROR_OUT_OF_MEMORY = 4   /* host or device allocation failed */
+} b2b_status_t;
+
+/* Flags of b2b_gemm_create. */
+enum {
+    B2B_FLAG_UNFUSED = 1u << 0,    /* comparison path: one GEMM kernel per operator, the
+                                      rounded intermediates go through HBM */
+    B2B_FLAG_ORIENT_N = 1u << 1,   /* first GEMM computed as A.B0 (accumulator lanes hold
+                                      columns); default computes it transposed so that lanes
+                                      hold rows.  Only with REMAP_BPERMUTE or REMAP_LDS. */
+    B2B_REMAP_AUTO = 0u << 4,      /* the library picks the rearrangement */
+    B2B_REMAP_BPERMUTE = 1u << 4,  /* coordination-matrix rounds: one ds_bpermute per round */
+    B2B_REMAP_PERMLANE = 2u << 4,  /* fixed lane-row swaps (v_permlane16/32_swap) */
+    B2B_REMAP_LDS = 3u << 4,       /* through a wave-private LDS region */
+    B2B_REMAP_RELABEL = 4u << 4,   /* no data movement: the next GEMM's K order follows the
+                                      accumulator layout */
+    B2B_REMAP_MASK = 7u << 4
+};
+
+typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
+
+/*
+ * Plans a cascade (page 1: determining the operators to fuse and the
+ * rearrangement relation between them, done once on the host).
+ *   plan          out: the new plan, or NULL on failure
+ *   dtype         element type of A, B*, D
+ *   batch, M      batch count and rows of A / D (M may be any positive value)
+ *   K, N1, N2     inner dimensions; N3 = 0 for two GEMMs, > 0 for three
+ *   ld            leading dimensions in elements: {lda, ldb0, ldb1, ldb2, ldd};
+ *                 NULL means dense (ld = number of columns); ldb2 ignored if N3 == 0
+ *   batch_stride  batch strides in elements: {A, B0, B1, B2, D}; NULL means dense;
+ *                 0 for a B* broadcasts it
+ *   flags         B2B_FLAG_* | B2B_REMAP_*
+ * Returns INVALID_VALUE for non-positive sizes, ld below the row width, or ld
+ * not a multiple of 16 bytes; NOT_SUPPORTED for shapes the fused kernels do not
+ * cover (then the caller may retry with B2B_FLAG_UNFUSED).
+ */
+b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
+                             int64_t K, int64_t N1, int64_t N2, int64_t N3,
+                             const int64_t* ld, const int64_t* batch_stride, uint32_t flags);
+
+/*
+ * Enqueues the cascade on `stream` (a hipStream_t; NULL is the null stream).
+ * A, B0, B1, B2, D are device pointers, 16-byte aligned; B2 must be NULL iff
+ * N3 == 0; D must not alias any input.  Only enqueues; does not synchronise.
+ */
+b2b_status_t b2b_gemm_run(b2b_gemm_t plan, const void* A, const void* B0, const void* B1,
+                          const void* B2, void* D, void* stream);
+
+/* Releases a plan (and its workspace, after the device is idle). NULL is a no-op. */
+b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);
+
+/* Static description of a status code. */
+const char* b2b_status_string(b2b_status_t s);
+
+/* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
+   remap mode, tile, grid, LDS and workspace bytes) into buf (NUL-terminated). */
+b2b_status_t b2b_gemm_get_info(b2b_gemm_t plan, char* buf, size_t len);
+
+/* ------------------------------------------------------------------------- */
+/* Rearrangement tables (page 1: the relation between the first and second
+ * rearrangement group matrices, Figs. 2a/2b/3, and the coordination matrix of
+ * Fig. 4 with its per-round encoding).  Host-only calls, no GPU needed.       */
+/* ------------------------------------------------------------------------- */
+
+/* gfx950 matrix-instruction shapes whose layouts the library knows. */
+typedef enum {
+    B2B_SHAPE_F16_16X16X32 = 0,
+    B2B_SHAPE_BF16_16X16X32 = 1,
+    B2B_SHAPE_F16_32X32X16 = 2,
+    B2B_SHAPE_BF16_32X32X16 = 3,
+    B2B_SHAPE_F16_16X16X16 = 4,
+    B2B_SHAPE_F64_16X16X4 = 5
+} b2b_shape_t;
+
+/*
+ * The relation of one remap unit: for the cascade computed with `shape` in
+ * orientation `orient_n` (0: first GEMM transposed, 1: plain), the unit holds
+ * one M-tile and the smallest run of intermediate columns that is whole
+ * accumulator tiles and whole K-steps of the next GEMM.  Element e of lane l
+ * is index l*E + e; source element e = tile*C + reg, destination element
+ * e = kstep*S + slot.  rel[d] = source index feeding destination index d.
+ *   rel       out, capacity `cap` entries (may be NULL to query sizes)
+ *   n_out     out: 64*E
+ *   elems     out: E, elements per lane
+ */
+b2b_status_t b2b_remap_relation(b2b_shape_t shape, int orient_n, int32_t* rel, int64_t cap,
+                                int64_t* n_out, int32_t* elems);
+
+/*
+ * The coordination matrix the device exchange executes, at the granularity
+ * the executor moves (`packed` = 1: 32-bit pairs of 16-bit values, possible
+ * only where the relation keeps pairs together; 0: single elements).
+ * For round j and receiver lane i (index j*64 + i): p = sender lane, q =
+ * element the sender gives, r = destination element of the receiver.
+ *   p, q, r   out, capacity `cap` each (NULL to query)
+ *   rounds    out: number of rounds (= elements per lane at that granularity)
+ */
+b2b_status_t b2b_remap_schedule(b2b_shape_t shape, int orient_n, int packed, int32_t* p,
+                                int32_t* q, int32_t* r, int64_t cap, int32_t* rounds);
+
+/*
+ * Runs one device rearrangement executor on index payloads and writes what
+ * it produced (a probe of the exchange kernels, used by the parity tests).
+ *   in   device, 64*E source elements (uint16 for 16-bit shapes, uint64 for
+ *        fp64), indexed as in b2b_remap_relation
+ *   out  device, 64*E destination elements, same type
+ *   mode B2B_REMAP_BPERMUTE / PERMLANE / LDS / RELABEL (RELABEL copies the
+ *        accumulator registers unchanged, which is what it feeds the MFMA)
+ * Only the shapes the fused kernels use are accepted (16x16x32 f16/bf16,
+ * 16x16x4 f64); orient_n requires BPERMUTE or LDS.
+ */
+b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, const void* in,
+                             void* out, void* stream);
+
+/*
+ * Runs one matrix instruction of `shape` on raw operand registers and writes
+ * every lane's accumulator registers (a probe of the layout catalogue).
+ *   a, b  device, 64 lanes x operand elements (8 x 16-bit, or 1 x fp64) each
+ *   c     device, 64 lanes x accumulator elements (4 x float32, or 4 x fp64)
+ * Accumulators start at zero.  Shapes: 16x16x32 f16/bf16, 16x16x4 f64.
+ */
+b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* B2B_H_ */

@@ -19,8 +19,9 @@ This module states those steps plainly on explicit index maps.  A layout is a
 list ``coord[lane * E + e]`` giving the logical matrix coordinate held by element
 ``e`` of lane ``lane``.  The register layouts of the gfx950 matrix instructions
 are written out here from AMD's published CDNA matrix-instruction layouts, on
-their own, independently of the product library; the GPU parity tests are what
-pin them to the hardware.
+their own, independently of the product library; a one-instruction GPU probe
+with integer operands (tests/test_gpu_layouts.py) and the GPU parity tests pin
+them to the hardware.
 """
 from collections import defaultdict
 
@@ -63,10 +64,12 @@ SHAPES = {
                           lambda l, u: (l % 16, 4 * (l // 16) + u),
                           lambda l, u: (4 * (l // 16) + u, l % 16),
                           lambda l, v: (4 * (l // 16) + v, l % 16), 16),
+    # fp64: the accumulator interleaves rows -- register v of lane group g
+    # holds row g + 4v (not 4g + v as in the float32 shapes)
     "f64_16x16x4": Shape("f64_16x16x4", 16, 16, 4, 1, 4,
                          lambda l, u: (l % 16, l // 16),
                          lambda l, u: (l // 16, l % 16),
-                         lambda l, v: (4 * (l // 16) + v, l % 16), 64),
+                         lambda l, v: (l // 16 + 4 * v, l % 16), 64),
 }
 
 

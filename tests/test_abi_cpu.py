@@ -1,0 +1,116 @@
+"""C ABI checks that need no GPU: the library loads and exports every symbol
+the header declares, argument validation, and the host-side rearrangement
+tables against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import chip_fusion_amd as cf
+from oracle import remap as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "b2b.h")).read()
+    return sorted(set(re.findall(r"\b(b2b_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = cf.lib()
+    names = _declared()
+    assert "b2b_gemm_create" in names and "b2b_gemm_run" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(cf.EXPORTS)
+
+
+def _create(**kw):
+    args = dict(dtype=0, batch=1, M=128, K=64, N1=64, N2=64, N3=0, ld=None, bs=None, flags=0)
+    args.update(kw)
+    h = ctypes.c_void_p(123)
+    arr = ctypes.c_int64 * 5
+    st = cf.lib().b2b_gemm_create(ctypes.byref(h), args["dtype"], args["batch"], args["M"], args["K"],
+                                  args["N1"], args["N2"], args["N3"],
+                                  arr(*args["ld"]) if args["ld"] else None,
+                                  arr(*args["bs"]) if args["bs"] else None, args["flags"])
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), 1), (dict(K=0), 1), (dict(N1=-1), 1), (dict(batch=0), 1), (dict(N3=-2), 1),
+    (dict(dtype=7), 2),
+    (dict(ld=[60, 64, 64, 0, 64]), 1),        # lda below K
+    (dict(ld=[68, 64, 64, 0, 64]), 1),        # lda not a multiple of 16 bytes
+    (dict(flags=1 << 12), 1),                 # unknown flag
+    (dict(flags=(7 << 4)), 1),                # unknown remap mode
+    (dict(flags=2 | (2 << 4)), 1),            # orientation N with permlane
+    (dict(K=96, N1=96, N2=96), 2),            # no kernel for this shape
+    (dict(batch=2, bs=[0, 4096, 4096, 0, 8192]), 1),   # A broadcast over batches
+])
+def test_create_rejects(kw, status):
+    st, h = _create(**kw)
+    assert st == status
+    assert h.value is None
+
+
+def test_create_accepts_and_destroy():
+    st, h = _create()
+    assert st == 0 and h.value
+    buf = ctypes.create_string_buffer(256)
+    assert cf.lib().b2b_gemm_get_info(h, buf, 256) == 0
+    assert b"path=fused" in buf.value and b"remap=relabel" in buf.value
+    assert cf.lib().b2b_gemm_destroy(h) == 0
+    assert cf.lib().b2b_gemm_destroy(None) == 0
+
+
+def test_run_rejects_bad_pointers():
+    st, h = _create()
+    assert st == 0
+    L = cf.lib()
+    a = ctypes.c_void_p(0x1000)
+    assert L.b2b_gemm_run(None, a, a, a, None, ctypes.c_void_p(0x2000), None) == 1
+    assert L.b2b_gemm_run(h, None, a, a, None, ctypes.c_void_p(0x2000), None) == 1
+    assert L.b2b_gemm_run(h, a, a, a, a, ctypes.c_void_p(0x2000), None) == 1       # B2 with N3 == 0
+    assert L.b2b_gemm_run(h, ctypes.c_void_p(0x1008), a, a, None, ctypes.c_void_p(0x2000), None) == 1
+    assert L.b2b_gemm_run(h, a, a, a, None, a, None) == 1                           # D aliases A
+    L.b2b_gemm_destroy(h)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert cf.lib().b2b_status_string(s).decode() == cf.STATUS[s]
+
+
+SHAPES = ["f16_16x16x32", "bf16_16x16x32", "f16_32x32x16", "bf16_32x32x16", "f16_16x16x16",
+          "f64_16x16x4"]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("orient", ["T", "N"])
+def test_relation_tables_match_oracle(shape, orient):
+    """The library's layout catalogue and relation builder against the oracle's
+    independent enumeration, bit for bit."""
+    rel, E = cf.remap_relation(shape, orient == "N")
+    src, dst, meta = R.cascade_layouts(shape, orient)
+    assert E == meta["elems"]
+    assert np.array_equal(rel, np.array(R.relation(src, dst)))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("orient,packed", [("T", True), ("T", False), ("N", False)])
+def test_schedules_valid_and_match_oracle(shape, orient, packed):
+    if packed and shape.startswith("f64"):
+        pytest.skip("fp64 elements are already 64-bit")
+    src, dst, meta = R.cascade_layouts(shape, orient)
+    rel = R.per_lane(R.relation(src, dst), 64, meta["elems"])
+    if packed:
+        rel = R.pack_pairs(rel)
+    p, q, r = cf.remap_schedule(shape, orient == "N", packed)
+    H = [[(int(p[j, i]), int(q[j, i]), int(r[j, i])) for j in range(p.shape[0])] for i in range(64)]
+    ok, why = R.validate(H, rel)
+    assert ok, why
+    assert H == R.coordination_matrix(rel)

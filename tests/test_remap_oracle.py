@@ -98,13 +98,21 @@ def test_16x16x16_T_is_identity():
     assert R.relation(src, dst) == list(range(len(src)))
 
 
-def test_f64_T_is_lane_group_transpose():
+def test_f64_T_is_identity():
+    """fp64: the accumulator of the transposed first GEMM holds row m, column
+    g + 4v in register v of lane group g -- exactly the operand's K-step v,
+    lane group g, k = 4v + g.  The rules are equal: fuse directly."""
     src, dst, meta = R.cascade_layouts("f64_16x16x4", "T")
+    assert R.relation(src, dst) == list(range(len(src)))
+
+
+def test_f64_N_moves_every_element_between_lane_groups():
+    src, dst, meta = R.cascade_layouts("f64_16x16x4", "N")
     rel = R.per_lane(R.relation(src, dst), 64, 4)
     for l in range(64):
         m, g = l % 16, l // 16
-        for s in range(4):     # K-step s wants column 4s + g: lane group s, register g
-            assert rel[l][s] == (m + 16 * s, g)
+        for s in range(4):     # wants column 4s + g of row m = (m % 4) + 4 (m // 4)
+            assert rel[l][s] == ((4 * s + g) + 16 * (m % 4), m // 4)
 
 
 @pytest.mark.parametrize("seed", range(6))
