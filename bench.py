@@ -46,7 +46,20 @@ def main():
     ap.add_argument("--rotate-bytes", type=float, default=1 << 30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run device-to-device copies of BYTES (scale for HBM counters)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -66,7 +79,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[dt]
-    R = max(1, int(np.ceil(args.rotate_bytes / set_bytes)))
+    R = max(1, min(64, int(np.ceil(args.rotate_bytes / set_bytes))))
     A0 = cf.to_device(A, dt)
     B0 = [cf.to_device(b, dt) for b in Bs]
     sets = []

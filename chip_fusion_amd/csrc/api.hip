@@ -15,7 +15,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/b2b.h"
+#include "b2b.h"
 #include "plan.hpp"
 #include "registry.hpp"
 
@@ -214,8 +214,19 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     std::memset(p->sched, 0, sizeof p->sched);
 
     if (!p->unfused) {
-        p->fused = find_kernel(dt, nst, dims, mode, orn, -1);
+        if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
+            // the cheapest rearrangement compiled for this shape
+            static const int order[] = {b2bk::MODE_RELABEL, b2bk::MODE_PERMLANE, b2bk::MODE_LDS,
+                                        b2bk::MODE_BPERM};
+            for (int m : order) {
+                p->fused = find_kernel(dt, nst, dims, m, orn, -1);
+                if (p->fused) { p->mode = m; break; }
+            }
+        } else {
+            p->fused = find_kernel(dt, nst, dims, mode, orn, -1);
+        }
         if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        const int mode = p->mode;
         if (mode == b2bk::MODE_BPERM) {
             if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1])) {
                 delete p;

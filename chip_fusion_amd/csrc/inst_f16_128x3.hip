@@ -1,9 +1,9 @@
 // Kernel instances: fp16 three-GEMM cascade, K = N1 = N2 = 128, N3 = 64.
 #include "registry.hpp"
 using namespace b2bk;
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_RELABEL, false, 2, 8, KM_NAT);
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_PERMLANE, false, 2, 8, KM_NAT);
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_BPERM, false, 2, 8, KM_NAT);
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_LDS, false, 2, 8, KM_NAT);
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_BPERM, true, 2, 8, KM_NAT);
-B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_LDS, true, 2, 8, KM_NAT);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_RELABEL, false, 2, 8, KM_NAT, 1);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_PERMLANE, false, 2, 8, KM_NAT, 1);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_BPERM, false, 2, 8, KM_NAT, 1);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_LDS, false, 2, 8, KM_NAT, 1);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_BPERM, true, 2, 8, KM_NAT, 1);
+B2B_INSTANCE(DT_F16, 3, 128, 128, 128, 64, MODE_LDS, true, 2, 8, KM_NAT, 1);

@@ -118,8 +118,12 @@ __device__ inline u4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline u2_t ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
+// Cache policy of the streaming accesses: A is read once and D written once,
+// so both go non-temporal (nt) and do not displace the weights from the caches.
+constexpr int kStreamPolicy = 2;
+
 __device__ inline void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, u4_t v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamPolicy);
 }
 __device__ inline void st64(__amdgpu_buffer_rsrc_t r, uint32_t off, u2_t v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
@@ -448,9 +452,15 @@ __device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
 template <int DT_, int NST_, int D0, int D1, int D2, int D3, int MODE_, bool ORN_, int MT_,
-          int WAVES_, int KM0_ = (DT_ == DT_F64 ? KM_PAIR64 : KM_NAT)>
+          int WAVES_, int KM0_ = (DT_ == DT_F64 ? KM_PAIR64 : KM_NAT), int PF_ = 2, int FW_ = 3,
+          bool RW_ = false>
 struct Cfg {
     static constexpr int DT = DT_, NST = NST_, MODE = MODE_, MT = MT_, WAVES = WAVES_;
+    static constexpr int PF = PF_;   // A tiles loaded ahead of the one being computed
+    static constexpr int FW = FW_;   // weight fragments in flight from LDS
+    // RW: every wave keeps all weight fragments in its registers (loaded from
+    // LDS once per batch); the MFMA loops then read no LDS at all
+    static constexpr bool RW = RW_;
     static constexpr bool ORN = ORN_;
     static constexpr int KM0 = KM0_;
     static constexpr int THREADS = 64 * WAVES;
@@ -459,11 +469,16 @@ struct Cfg {
     static constexpr int KW = Ty<DT>::KW, FB = Ty<DT>::FB, ELT = Ty<DT>::ELT;
     static constexpr int KS(int s) { return dim(s) / KW; }
     static constexpr int NT(int s) { return dim(s + 1) / 16; }
+    static constexpr int NF(int s) { return s < NST ? NT(s) * KS(s) : 1; }   // fragments per stage
     static constexpr int wbytes(int s) { return s < NST ? NT(s) * KS(s) * 64 * FB : 0; }
     static constexpr int woff(int s) { return s == 0 ? 0 : woff(s - 1) + wbytes(s - 1); }
     static constexpr int WBYTES = woff(3) + 0;
-    static constexpr bool USES_SCRATCH = (MODE == MODE_LDS) && NST > 1;
-    static constexpr int SCRATCH = USES_SCRATCH ? WAVES * LdsRemap<DT>::BYTES : 0;
+    // per-wave LDS region: the D staging tile, shared with the LDS rearrangement
+    static constexpr int NLAST_ = (NST == 1 ? D1 : NST == 2 ? D2 : D3);
+    static constexpr int DSTAGE = 16 * MT * NLAST_ * Ty<DT>::ELT;
+    static constexpr int WSCRATCH = (MODE == MODE_LDS && NST > 1 && LdsRemap<DT>::BYTES > DSTAGE)
+                                        ? LdsRemap<DT>::BYTES : DSTAGE;
+    static constexpr int SCRATCH = WAVES * WSCRATCH;
     static constexpr int LDS_BYTES = WBYTES + SCRATCH;
     static constexpr int KMS(int s) { return s == 0 ? KM0 : (MODE == MODE_RELABEL ? KM_REL : KM_NAT); }
     static constexpr int NLAST = dim(NST);
@@ -502,30 +517,46 @@ __device__ inline void load_a(typename Ty<C::DT>::op_t (&a)[C::MT][C::KS(0)],
 }
 
 // One GEMM stage on MFMA: acc[mt][t] = sum_ks W_s(t, ks) (x) op[mt][ks].
+// Weight fragments come either from LDS -- read a window of FW fragments ahead
+// of the MFMAs that use them, so LDS latency overlaps the matrix pipe -- or
+// from registers (RW).  Each fragment feeds MT MFMAs (one per 16-row sub-tile).
 template <class C, int S, bool ORN_STAGE>
 __device__ inline void gemm_stage(const unsigned char* lds,
+                                  const typename Ty<C::DT>::op_t (&wreg)[C::NF(S)],
                                   const typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S)],
                                   typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)], int lane) {
     using T = Ty<C::DT>;
     using op_t = typename T::op_t;
+    constexpr int KS = C::KS(S), NF = C::NT(S) * KS, FW = C::RW ? 1 : C::FW;
     const unsigned char* w = lds + C::woff(S) + lane * C::FB;
+    auto frag = [&](int i) {
+        if constexpr (C::RW) return wreg[i];
+        else return *(const op_t*)(w + i * 64 * C::FB);
+    };
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int t = 0; t < C::NT(S); ++t) acc[mt][t] = typename T::acc_t{};
+    op_t fr[FW];
 #pragma unroll
-    for (int t = 0; t < C::NT(S); ++t)
+    for (int i = 0; i < FW - 1; ++i)
+        if (i < NF) fr[i] = frag(i);
 #pragma unroll
-        for (int ks = 0; ks < C::KS(S); ++ks) {
-            const op_t bw = *(const op_t*)(w + (t * C::KS(S) + ks) * 64 * C::FB);
-#pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) {
-                if constexpr (ORN_STAGE)
-                    acc[mt][t] = T::mma(op[mt][ks], bw, acc[mt][t]);   // C0 = A . B0
-                else
-                    acc[mt][t] = T::mma(bw, op[mt][ks], acc[mt][t]);   // C^T = W^T . X^T
-            }
+    for (int i = 0; i < NF; ++i) {
+        if constexpr (FW > 1) {
+            if (i + FW - 1 < NF) fr[(i + FW - 1) % FW] = frag(i + FW - 1);
+        } else {
+            fr[0] = frag(i);
         }
+        const int t = i / KS, ks = i % KS;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+            if constexpr (ORN_STAGE)
+                acc[mt][t] = T::mma(op[mt][ks], fr[i % FW], acc[mt][t]);   // C0 = A . B0
+            else
+                acc[mt][t] = T::mma(fr[i % FW], op[mt][ks], acc[mt][t]);   // C^T = W^T . X^T
+        }
+    }
 }
 
 // Stage output -> operands of the next stage (round, then rearrange).
@@ -554,28 +585,47 @@ __device__ inline void to_operands(const typename Ty<C::DT>::acc_t (&acc)[C::MT]
     }
 }
 
-// Final stage output -> D (rounded), 16 bytes per lane per store.
+// Final stage output -> D (rounded).  The accumulator layout spreads a row of
+// D over four lane groups (16 rows per store instruction, 64 bytes of each),
+// which the memory system handles poorly; the wave therefore writes its tile
+// into its private LDS region (16-byte chunks, XOR-swizzled by row to avoid
+// bank conflicts) and reads it back so that consecutive lanes store
+// consecutive 16-byte chunks of whole rows.
+template <class C>
+struct DStage {
+    static constexpr int RB = C::NLAST * C::ELT;            // bytes per row of D
+    static constexpr int CPR = RB / 16;                      // 16-byte chunks per row
+    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;    // swizzle mask
+    static constexpr int BYTES = C::ROWS_WAVE * RB;
+    static_assert(RB % 16 == 0 && 64 % CPR == 0 || CPR % 64 == 0, "row width not supported");
+    __device__ static inline int pos(int row, int chunk) {
+        return row * RB + ((chunk ^ (row & SWZ)) << 4);
+    }
+};
+
 template <class C, int S>
 __device__ inline void store_d(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)],
-                               __amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane) {
+                               __amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane, unsigned char* scratch) {
+    using DS = DStage<C>;
     const int m = lane & 15, g = lane >> 4;
     if constexpr (C::DT != DT_F64) {
         using T = Ty<C::DT>;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
+            const int row = 16 * mt + m;
 #pragma unroll
             for (int c = 0; c < C::NT(S) / 2; ++c) {
                 const f4_t a0 = acc[mt][2 * c], a1 = acc[mt][2 * c + 1];
                 unsigned x0 = T::pack(a0[0], a0[1]), x1 = T::pack(a0[2], a0[3]);
                 unsigned y0 = T::pack(a1[0], a1[1]), y1 = T::pack(a1[2], a1[3]);
-                regroup_pairs(x0, x1, y0, y1);
-                st128(rs, (uint32_t)(((16 * mt + m) * ldd + 32 * c + 8 * g) * 2), u4_t{x0, x1, y0, y1});
+                regroup_pairs(x0, x1, y0, y1);          // lane group g: columns 32c + 8g ..+7
+                *(u4_t*)(scratch + DS::pos(row, 4 * c + g)) = u4_t{x0, x1, y0, y1};
             }
             if constexpr (C::NT(S) % 2) {
-                constexpr int t = C::NT(S) - 1;
+                constexpr int t = C::NT(S) - 1;         // columns 16t + 4g ..+3
                 const f4_t a0 = acc[mt][t];
-                st64(rs, (uint32_t)(((16 * mt + m) * ldd + 16 * t + 4 * g) * 2),
-                     u2_t{T::pack(a0[0], a0[1]), T::pack(a0[2], a0[3])});
+                *(u2_t*)(scratch + DS::pos(row, 2 * t + (g >> 1)) + (g & 1) * 8) =
+                    u2_t{T::pack(a0[0], a0[1]), T::pack(a0[2], a0[3])};
             }
         }
     } else {
@@ -586,12 +636,22 @@ __device__ inline void store_d(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::
             for (int t = 0; t < C::NT(S); ++t) {
                 double a[4] = {acc[mt][t][0], acc[mt][t][1], acc[mt][t][2], acc[mt][t][3]};
                 transpose_rows64(a);
-                const uint32_t off = (uint32_t)(((16 * mt + m) * ldd + 16 * t + 4 * g) * 8);
+                const int row = 16 * mt + m;
                 const u2_t p0 = dsplit(a[0]), p1 = dsplit(a[1]), p2 = dsplit(a[2]), p3 = dsplit(a[3]);
-                st128(rs, off, u4_t{p0[0], p0[1], p1[0], p1[1]});
-                st128(rs, off + 16, u4_t{p2[0], p2[1], p3[0], p3[1]});
+                *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * g)) = u4_t{p0[0], p0[1], p1[0], p1[1]};
+                *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * g + 1)) = u4_t{p2[0], p2[1], p3[0], p3[1]};
             }
     }
+    wave_lds_fence();
+    constexpr int CHUNKS = C::ROWS_WAVE * DS::CPR;
+    static_assert(CHUNKS % 64 == 0, "tile must be whole store instructions");
+#pragma unroll
+    for (int i = 0; i < CHUNKS / 64; ++i) {
+        const int idx = i * 64 + lane, row = idx / DS::CPR, q = idx % DS::CPR;
+        const u4_t v = *(const u4_t*)(scratch + DS::pos(row, q));
+        st128(rs, (uint32_t)(row * ldd * C::ELT + q * 16), v);
+    }
+    wave_lds_fence();
 }
 
 template <class C>
@@ -610,13 +670,16 @@ __device__ inline void stage_all_weights(unsigned char* lds, const KArgs& args, 
 // The fused kernel: persistent workgroups over tiles of ROWS_WG rows.
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
+__device__ __forceinline__ void fused_body(const KArgs& args) {
     using T = Ty<C::DT>;
     using op_t = typename T::op_t;
     using acc_t = typename T::acc_t;
     __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    unsigned char* scratch = lds + C::WBYTES + (C::USES_SCRATCH ? wave * LdsRemap<C::DT>::BYTES : 0);
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index is uniform across the wave: keep it (and every tile address
+    // derived from it) in scalar registers so buffer resources stay uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* scratch = lds + C::WBYTES + wave * C::WSCRATCH;
 
     code_t code = {}, code2 = {};
     if constexpr (C::MODE == MODE_BPERM && C::NST > 1) {
@@ -631,33 +694,51 @@ __global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
     // range of logical workgroups (hence of tiles and batches).
     const int G = gridDim.x, bid = blockIdx.x;
     const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int t0 = (int)((int64_t)args.total_tiles * lid / G);
-    const int t1 = (int)((int64_t)args.total_tiles * (lid + 1) / G);
+    const int per = args.total_tiles / G, extra = args.total_tiles % G;
+    const int t0 = lid * per + (lid < extra ? lid : extra);
+    const int t1 = t0 + per + (lid < extra ? 1 : 0);
     if (t0 >= t1) return;
 
     const int TB = args.tiles_per_batch;
+    // Tiles past the workgroup's range get an empty resource: their loads
+    // return zeros without touching memory.  Issuing them unconditionally
+    // keeps the count of loads in flight the same on every path, so the
+    // compiler's wait counts let the prefetched tiles stay in flight.
+    int t_end = t1;   // end of the current batch segment
     auto a_rsrc = [&](int t) {
-        const int b = t / TB;
-        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        const bool live = t < t_end;
+        const int tc = live ? t : t0;
+        const int b = tc / TB;
+        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
         int64_t rows = args.M - row0;
         rows = rows < 0 ? 0 : (rows > C::ROWS_WAVE ? C::ROWS_WAVE : rows);
+        if (!live) rows = 0;
         const char* base = (const char*)args.A + ((int64_t)b * args.sA + (rows ? row0 : 0) * args.lda) * C::ELT;
         return make_rsrc(base, (uint32_t)(rows * args.lda * C::ELT));
     };
 
-    op_t a_cur[C::MT][C::KS(0)];
-    load_a<C>(a_cur, a_rsrc(t0), args.lda, lane);
-    int cur_b = -1;
-    for (int t = t0; t < t1; ++t) {
-        const int b = t / TB;
-        op_t a_nxt[C::MT][C::KS(0)];
-        if (t + 1 < t1) load_a<C>(a_nxt, a_rsrc(t + 1), args.lda, lane);
-        if (b != cur_b) {
-            __syncthreads();
-            stage_all_weights<C>(lds, args, b, tid);
-            __syncthreads();
-            cur_b = b;
+    // weight fragments held in registers (RW); unused otherwise
+    op_t wr0[C::NF(0)], wr1[C::NF(1)], wr2[C::NF(2)];
+    auto weights_to_regs = [&]() {
+        if constexpr (C::RW) {
+#pragma unroll
+            for (int i = 0; i < C::NF(0); ++i)
+                wr0[i] = *(const op_t*)(lds + C::woff(0) + (i * 64 + lane) * C::FB);
+            if constexpr (C::NST > 1) {
+#pragma unroll
+                for (int i = 0; i < C::NF(1); ++i)
+                    wr1[i] = *(const op_t*)(lds + C::woff(1) + (i * 64 + lane) * C::FB);
+            }
+            if constexpr (C::NST > 2) {
+#pragma unroll
+                for (int i = 0; i < C::NF(2); ++i)
+                    wr2[i] = *(const op_t*)(lds + C::woff(2) + (i * 64 + lane) * C::FB);
+            }
         }
+    };
+
+    auto process = [&](int t, const op_t (&a)[C::MT][C::KS(0)]) {
+        const int b = t / TB;
         const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
         int64_t rows = args.M - row0;
         rows = rows < 0 ? 0 : (rows > C::ROWS_WAVE ? C::ROWS_WAVE : rows);
@@ -666,31 +747,90 @@ __global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
             (uint32_t)(rows * args.ldd * C::ELT));
 
         acc_t acc0[C::MT][C::NT(0)];
-        gemm_stage<C, 0, C::ORN>(lds, a_cur, acc0, lane);
+        gemm_stage<C, 0, C::ORN>(lds, wr0, a, acc0, lane);
         if constexpr (C::NST == 1) {
-            store_d<C, 0>(acc0, d_rs, args.ldd, lane);
+            store_d<C, 0>(acc0, d_rs, args.ldd, lane, scratch);
         } else {
             op_t op1[C::MT][C::KS(1)];
             to_operands<C, 0, C::ORN>(acc0, op1, code, scratch, lane);
             acc_t acc1[C::MT][C::NT(1)];
-            gemm_stage<C, 1, false>(lds, op1, acc1, lane);
+            gemm_stage<C, 1, false>(lds, wr1, op1, acc1, lane);
             if constexpr (C::NST == 2) {
-                store_d<C, 1>(acc1, d_rs, args.ldd, lane);
+                store_d<C, 1>(acc1, d_rs, args.ldd, lane, scratch);
             } else {
                 op_t op2[C::MT][C::KS(2)];
                 to_operands<C, 1, false>(acc1, op2, code2, scratch, lane);
                 acc_t acc2[C::MT][C::NT(2)];
-                gemm_stage<C, 2, false>(lds, op2, acc2, lane);
-                store_d<C, 2>(acc2, d_rs, args.ldd, lane);
+                gemm_stage<C, 2, false>(lds, wr2, op2, acc2, lane);
+                store_d<C, 2>(acc2, d_rs, args.ldd, lane, scratch);
             }
         }
-        if (t + 1 < t1) {
+    };
+
+    const auto no_rsrc = make_rsrc(args.D, 0u);
+    acc_t zero[C::MT][C::NT(C::NST - 1)];
 #pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt)
+    for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < C::KS(0); ++ks) a_cur[mt][ks] = a_nxt[mt][ks];
+        for (int n = 0; n < C::NT(C::NST - 1); ++n) zero[mt][n] = acc_t{};
+
+    // The workgroup's tiles, one batch (one set of weights) at a time.  Within
+    // a batch, A tiles stream through a ring of PF+1 register sets; the loop is
+    // unrolled by the ring size so every set keeps its registers (no copies,
+    // which would wait on loads still in flight) and PF tiles are always being
+    // fetched.  Weights are loaded before the segment, so inside it they are
+    // loop-invariant (in registers for RW, in LDS otherwise).
+    constexpr int RING = C::PF + 1;
+    op_t ring[RING][C::MT][C::KS(0)];
+    int t = t0;
+    while (t < t1) {
+        const int b = t / TB;
+        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+        __syncthreads();
+        // weights first: the wait for them then does not include the A
+        // prefetches issued after them (memory counters are in order)
+        stage_all_weights<C>(lds, args, b, tid);
+        // Prologue: each prefetched tile is followed by one tile's worth of
+        // stores to an empty resource (dropped by the hardware), so that on
+        // entry to the loop the loads in flight sit behind as many memory
+        // operations as in the steady state and the first rounds wait no
+        // longer than the later ones.
+#pragma unroll
+        for (int i = 0; i < C::PF; ++i) {
+            load_a<C>(ring[i], a_rsrc(t + i), args.lda, lane);
+            store_d<C, C::NST - 1>(zero, no_rsrc, args.ldd, lane, scratch);
+        }
+        __syncthreads();
+        weights_to_regs();
+        // Every phase either runs or leaves the loop, so no path reaches a
+        // later phase (or the next round) with fewer loads in flight than the
+        // steady state.
+        for (;;) {
+            bool done = false;
+#pragma unroll
+            for (int ph = 0; ph < RING; ++ph) {
+                if (!done) {
+                    load_a<C>(ring[(ph + C::PF) % RING], a_rsrc(t + C::PF), args.lda, lane);
+                    process(t, ring[ph]);
+                    done = ++t >= t_end;
+                }
+            }
+            if (done) break;
         }
     }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
+    fused_body<C>(args);
+}
+
+// Register-resident weights need the whole register file of a SIMD: one wave
+// per SIMD, up to 512 registers (256 VGPRs + 256 AGPRs).
+template <class C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fused_kernel_rw(KArgs args) {
+    fused_body<C>(args);
 }
 
 // ---------------------------------------------------------------------------

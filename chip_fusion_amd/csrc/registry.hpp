@@ -5,6 +5,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "kernels_cs.hpp"
 
 namespace b2b {
 
@@ -35,9 +36,44 @@ KernelDesc describe() {
     d.threads = C::THREADS;
     d.rows_wg = C::ROWS_WG;
     d.lds_bytes = C::LDS_BYTES;
-    d.fn = (const void*)&b2bk::fused_kernel<C>;
+    if constexpr (C::RW) {
+        d.fn = (const void*)&b2bk::fused_kernel_rw<C>;
+        d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+            hipLaunchKernelGGL(b2bk::fused_kernel_rw<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+            return hipGetLastError();
+        };
+    } else {
+        d.fn = (const void*)&b2bk::fused_kernel<C>;
+        d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+            hipLaunchKernelGGL(b2bk::fused_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+            return hipGetLastError();
+        };
+    }
+    return d;
+}
+
+// Column-split instances (weights larger than LDS): the rearrangement between
+// the GEMMs goes through LDS across the workgroup's waves.
+template <class C>
+KernelDesc describe_cs() {
+    KernelDesc d;
+    d.dtype = C::DT;
+    d.nst = 2;
+    d.dims[0] = C::K;
+    d.dims[1] = C::N1;
+    d.dims[2] = C::N2;
+    d.dims[3] = 0;
+    d.mode = b2bk::MODE_LDS;
+    d.orn = 0;
+    d.km0 = b2bk::KM_NAT;
+    d.mt = C::MT;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::R;
+    d.lds_bytes = C::LDS_BYTES;
+    d.fn = (const void*)&b2bk::cs_kernel<C>;
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
-        hipLaunchKernelGGL(b2bk::fused_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+        hipLaunchKernelGGL(b2bk::cs_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
         return hipGetLastError();
     };
     return d;
@@ -89,6 +125,9 @@ ProbeDesc describe_probe() {
 #define B2B_CAT2(a, b) a##b
 #define B2B_CAT(a, b) B2B_CAT2(a, b)
 // B2B_INSTANCE(dtype, stages, K, N1, N2, N3, mode, orientN, MT, waves, kmap0)
+#define B2B_CS_INSTANCE(...)                                                           \
+    static ::b2b::Registrar B2B_CAT(b2b_cs_reg_, __LINE__)(                            \
+        ::b2b::describe_cs<::b2bk::CsCfg<__VA_ARGS__>>())
 #define B2B_INSTANCE(...)                                                              \
     static ::b2b::Registrar B2B_CAT(b2b_reg_, __LINE__)(                               \
         ::b2b::describe<::b2bk::Cfg<__VA_ARGS__>>())

@@ -119,7 +119,7 @@ def _sample_rows(batch, M, n=384, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_full_size_sampled(cfg):
     c = synth.CONFIGS[cfg]
     dt, dims = c["dtype"], c["dims"]
@@ -137,3 +137,65 @@ def test_full_size_sampled(cfg):
     ref = oracle.cascade(dt, A, Bs, rows=rows)
     assert_close(dt, got, ref, f"cfg{cfg} full size")
     p.close()
+
+
+# ---------------------------------------------------------------------------
+# Rounding of the intermediate and of D: round to nearest, ties to even
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rounding_is_nearest_even(dtype):
+    """C0 = x + f*ulp(x) with f in {1/4, 1/2, 3/4} (exact in float32), B1 = I:
+    then D = rnd(C0) exactly.  Round-to-nearest-even gives the oracle's bits;
+    truncation (RTZ) or ties-away differ on the quarter and half cases."""
+    M, K, N = 64, 32, 32
+    sig = 11 if dtype == "f16" else 8
+    rng = np.random.default_rng(9)
+    A = np.zeros((M, K)); B0 = np.zeros((K, N))
+    # x = (1 + j/2^(sig-1)) * 2^e on the diagonal-like first column, fraction via the second
+    e = rng.integers(-3, 4, (M, 1))
+    A[:, 0] = 2.0 ** e[:, 0]
+    frac = rng.choice([0.25, 0.5, 0.75], size=M)
+    A[:, 1] = frac * 2.0 ** (e[:, 0] - (sig - 1))
+    B0[0, :] = 1.0 + rng.integers(0, 2 ** (sig - 1), N) / 2.0 ** (sig - 1)
+    B0[1, :] = 1.0
+    # the supported widths: embed the 32-wide problem in the 64-wide kernel with zero padding
+    Ap = np.zeros((1, M, 64), np.float64); Ap[0, :, :K] = A
+    B0p = np.zeros((64, 64)); B0p[:K, :N] = B0
+    B1p = np.eye(64)
+    Ae = synth.to_dtype(Ap, dtype)
+    Be = [synth.to_dtype(B0p, dtype)[None], synth.to_dtype(B1p, dtype)[None]]
+    ref = oracle.cascade(dtype, Ae, Be)
+    assert np.array_equal(oracle.decode(dtype, Ae).astype(np.float64), Ap)    # exact inputs
+    for mode in (MODES_T if dtype == "f16" else ["relabel", "permlane"]):
+        got = run_plan(dtype, Ae, Be, remap=mode)
+        assert np.array_equal(got, ref), mode
+    vals = oracle.decode(dtype, ref[0, :, :N]).astype(np.float64)
+    exact = (A[:, :1] * B0[:1, :] + A[:, 1:2] * B0[1:2, :])
+    assert np.any(vals != exact)          # rounding really happened
+
+
+# ---------------------------------------------------------------------------
+# Weights larger than LDS (two 256x256 matrices): column-split kernel whose
+# rearrangement goes through LDS across the workgroup's waves
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,batch", [(1000, 1), (777, 2), (32, 1), (1, 1)])
+def test_wide_cascade_parity(M, batch):
+    _flush(f"wide cascade bf16 256^3 M={M} batch={batch}")
+    A, Bs = synth.make_inputs(3, M=M, batch=batch)
+    got = run_plan("bf16", A, Bs)
+    ref = oracle.cascade("bf16", A, Bs)
+    assert_close("bf16", got, ref, f"bf16 256^3 M={M}")
+
+
+def test_wide_cascade_ternary_bit_exact():
+    _flush("wide cascade ternary")
+    A, Bs = synth.make_inputs(3, M=500, batch=2, dist="ternary")
+    assert np.array_equal(run_plan("bf16", A, Bs), oracle.cascade("bf16", A, Bs))
+
+
+def test_wide_cascade_f16_parity():
+    """The same column-split kernel instantiated for fp16."""
+    A, Bs = synth.make_inputs(dict(synth.CONFIGS[3], dtype="f16"), M=600, batch=1)
+    f = run_plan("f16", A, Bs)
+    ref = oracle.cascade("f16", A, Bs)
+    assert_close("f16", f, ref, "f16 256^3")
