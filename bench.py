@@ -135,7 +135,20 @@ def main():
         roof = {"bound": "mfma", "achieved": flop / (launch_ms * 1e-3) / 1e12, "peak": PEAK[dt] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # HBM bytes per launch from the committed rocprofv3 counters, valid only
+    # while the kernel sources are the ones they were taken with
     roof["traffic"] = None
+    try:
+        from chip_fusion_amd import build as _b
+        tr = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        ent = tr["configs"].get(str(args.config))
+        if (ent and tr["source_digest"] == _b.source_digest() and not args.unfused
+                and args.remap == "auto" and not args.orient_n):
+            roof["traffic"] = ent["hbm_bytes"]
+            roof["traffic_unit"] = "bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f)" % (
+                tr["fetch_scale"], tr["write_scale"])
+    except (OSError, ValueError, KeyError):
+        pass
     roof["kernel_ms"] = launch_ms
     roof["algorithmic_bytes"] = algo_bytes
     roof["algorithmic_flop"] = flop

@@ -23,6 +23,18 @@ def library_path():
     return LIB
 
 
+def source_digest():
+    """sha256 over the kernel and host sources the library is built from (used
+    to tell whether stored profiler counters still describe the current kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def _compile(src, remarks):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-x", "hip", "-c", src, "-o", obj]
