@@ -53,6 +53,7 @@ struct KArgs {
     const void* A;
     const void* B[3];
     void* D;
+    const void* W;                  // pre-packed weights (column-split kernel), else null
     int64_t M;
     int64_t lda, ldb[3], ldd;
     int64_t sA, sB[3], sD;          // batch strides, elements
@@ -410,39 +411,64 @@ __device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t
     using T = Ty<DT>;
     constexpr int KS = KD / T::KW;
     if constexpr (DT != DT_F64) {
-        // unit: 4 consecutive rows x 8 consecutive columns
+        // unit: 4 consecutive rows x 8 consecutive columns; the loads of a
+        // batch of units are all issued before any of them is written
         constexpr int UN = ND / 8, UNITS = (KD / 4) * UN;
+        constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS, BATCH = ITERS < 4 ? ITERS : 4;
         const unsigned short* B = (const unsigned short*)Bg;
-        for (int u = tid; u < UNITS; u += NTHREADS) {
-            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
-            u4_t r[4];
+        for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
+            u4_t r[BATCH][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
-            int ks, g, u0;
-            kmap16<DT, KM>(k4, &ks, &g, &u0);
+            for (int q = 0; q < BATCH; ++q) {
+                const int u = tid + (i0 + q) * NTHREADS;
+                if (u < UNITS) {
+                    const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int n = n0 + c, t = n >> 4;
-                const int sh = (c & 1) * 16;
-                const unsigned e0 = (r[0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[1][c >> 1] >> sh) & 0xFFFFu;
-                const unsigned e2 = (r[2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[3][c >> 1] >> sh) & 0xFFFFu;
-                const int lane = (n & 15) + 16 * g;
-                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) =
-                    u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+                    for (int i = 0; i < 4; ++i) r[q][i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < BATCH; ++q) {
+                const int u = tid + (i0 + q) * NTHREADS;
+                if (u >= UNITS) continue;
+                const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
+                int ks, g, u0;
+                kmap16<DT, KM>(k4, &ks, &g, &u0);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int n = n0 + c, t = n >> 4;
+                    const int sh = (c & 1) * 16;
+                    const unsigned e0 = (r[q][0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[q][1][c >> 1] >> sh) & 0xFFFFu;
+                    const unsigned e2 = (r[q][2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[q][3][c >> 1] >> sh) & 0xFFFFu;
+                    const int lane = (n & 15) + 16 * g;
+                    *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) =
+                        u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+                }
             }
         }
     } else {
         constexpr int UN = ND / 2, UNITS = KD * UN;
+        constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS, BATCH = ITERS < 2 ? ITERS : 2;
         const double* B = (const double*)Bg;
-        for (int u = tid; u < UNITS; u += NTHREADS) {
-            const int k = u / UN, n0 = (u % UN) * 2;
-            const u4_t v = *(const u4_t*)(B + (int64_t)k * ldb + n0);
-            int ks, g;
-            kmap64<KM>(k, &ks, &g);
+        for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
+            u4_t v[BATCH];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
-                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{v[2 * c], v[2 * c + 1]};
+            for (int q = 0; q < BATCH; ++q) {
+                const int u = tid + (i0 + q) * NTHREADS;
+                if (u < UNITS) v[q] = *(const u4_t*)(B + (int64_t)(u / UN) * ldb + (u % UN) * 2);
+            }
+#pragma unroll
+            for (int q = 0; q < BATCH; ++q) {
+                const int u = tid + (i0 + q) * NTHREADS;
+                if (u >= UNITS) continue;
+                const int k = u / UN, n0 = (u % UN) * 2;
+                int ks, g;
+                kmap64<KM>(k, &ks, &g);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
+                    *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{v[q][2 * c], v[q][2 * c + 1]};
+                }
             }
         }
     }

@@ -12,6 +12,9 @@
 // relation between the first GEMM's result layout and the second GEMM's
 // operand layout is realised by the LDS addresses.  Nothing leaves the chip.
 //
+// The weights are first re-laid out by a small kernel into fragment order in
+// a workspace (every workgroup needs all of them; reading them as contiguous
+// 16-byte fragments avoids staging 256 KB through LDS in every workgroup).
 // Per 32-row tile: A is loaded with whole-row 16-byte accesses into LDS
 // (XOR-swizzled 16-byte chunks), GEMM0 (each wave: 32 rows x N1/4 columns),
 // C0 -> LDS, GEMM1 (each wave: 32 rows x N2/4 columns), D -> LDS, row-wise
@@ -32,8 +35,7 @@ struct CsCfg {
     static constexpr int KS0 = K / 32, KS1 = N1 / 32;           // K-steps of each GEMM
     static constexpr int ABYTES = R * K * ELT, CBYTES = R * N1 * ELT, DBYTES = R * N2 * ELT;
     static constexpr int LDS_TILES = ABYTES + CBYTES + DBYTES;
-    static constexpr int WSTAGE = (K * N1 > N1 * N2 ? K * N1 : N1 * N2) * ELT;  // one weight matrix
-    static constexpr int LDS_BYTES = LDS_TILES > WSTAGE ? LDS_TILES : WSTAGE;
+    static constexpr int LDS_BYTES = LDS_TILES;
     static constexpr int A_CHUNKS = ABYTES / 16 / THREADS;      // 16-byte A loads per thread per tile
     static_assert(N1W % 32 == 0 && N2W % 32 == 0, "column slices must be whole 32-column pairs");
     static_assert(ABYTES % (16 * THREADS) == 0, "A tile must split evenly over the threads");
@@ -44,6 +46,39 @@ struct CsCfg {
     __device__ static inline int cpos(int row, int chunk) { return row * N1 * ELT + ((chunk ^ (row & 15)) << 4); }
     __device__ static inline int dpos(int row, int chunk) { return row * N2 * ELT + ((chunk ^ (row & 15)) << 4); }
 };
+
+// ---------------------------------------------------------------------------
+// Weight pre-pack: B (row-major) -> fragment-major order in a workspace, one
+// 16-byte slot (8 k of one column, natural K order) per lane and fragment, so
+// that every wave of the fused kernel loads its weight fragments with plain
+// contiguous 16-byte loads.  Slot (fragment f = t*KS + ks, lane l = i + 16g)
+// of matrix s, batch b lives at ((b * PER_BATCH) + base_s + f*64 + l) * 16.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Packed {
+    static constexpr int SLOTS0 = (C::N1 / 16) * C::KS0 * 64;   // 16-byte slots of B0
+    static constexpr int SLOTS1 = (C::N2 / 16) * C::KS1 * 64;
+    static constexpr int PER_BATCH = SLOTS0 + SLOTS1;
+};
+
+template <class C>
+__global__ __launch_bounds__(256) void cs_pack_kernel(KArgs args, u4_t* ws, int64_t batch) {
+    using P = Packed<C>;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= batch * P::PER_BATCH) return;
+    const int64_t b = gid / P::PER_BATCH;
+    int sl = (int)(gid % P::PER_BATCH);
+    const int mat = sl < P::SLOTS0 ? 0 : 1;
+    if (mat) sl -= P::SLOTS0;
+    const int KS = mat ? C::KS1 : C::KS0;
+    const int f = sl >> 6, l = sl & 63, t = f / KS, ks = f % KS, i = l & 15, g = l >> 4;
+    const unsigned short* B = (const unsigned short*)args.B[mat] + b * args.sB[mat] + 16 * t + i;
+    const int64_t ldb = args.ldb[mat];
+    unsigned h[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) h[u] = B[(int64_t)(32 * ks + 8 * g + u) * ldb];
+    ws[gid] = u4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
 
 template <class C>
 __device__ __forceinline__ void cs_body(const KArgs& args) {
@@ -182,26 +217,25 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
     while (t < t1) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
-        // weights of batch b: each matrix staged in LDS (fragment-major), then
-        // every wave copies the fragments of its column slices to registers
-        __syncthreads();
-        stage_weights<C::DT, C::K, C::N1, KM_NAT, C::THREADS>(
-            lds, (const char*)args.B[0] + (int64_t)b * args.sB[0] * C::ELT, args.ldb[0], tid);
-        __syncthreads();
+        // weights of batch b: this wave's column slices, straight from the
+        // pre-packed workspace (contiguous 16-byte loads, no LDS, no barrier);
+        // the A prefetch below is issued behind them
+        {
+            using P = Packed<C>;
+            const auto wrs = make_rsrc((const u4_t*)args.W + (int64_t)b * P::PER_BATCH,
+                                       (uint32_t)(P::PER_BATCH * 16));
+            __syncthreads();   // previous segment's LDS reads are over
 #pragma unroll
-        for (int n = 0; n < C::NT0; ++n)
+            for (int n = 0; n < C::NT0; ++n)
 #pragma unroll
-            for (int ks = 0; ks < C::KS0; ++ks)
-                w0[n][ks] = *(const u4_t*)(lds + (((wave * C::NT0 + n) * C::KS0 + ks) * 64 + lane) * 16);
-        __syncthreads();
-        stage_weights<C::DT, C::N1, C::N2, KM_NAT, C::THREADS>(
-            lds, (const char*)args.B[1] + (int64_t)b * args.sB[1] * C::ELT, args.ldb[1], tid);
-        __syncthreads();
+                for (int ks = 0; ks < C::KS0; ++ks)
+                    w0[n][ks] = ld128(wrs, (uint32_t)((((wave * C::NT0 + n) * C::KS0 + ks) * 64 + lane) * 16));
 #pragma unroll
-        for (int n = 0; n < C::NT1; ++n)
+            for (int n = 0; n < C::NT1; ++n)
 #pragma unroll
-            for (int kc = 0; kc < C::KS1; ++kc)
-                w1[n][kc] = *(const u4_t*)(lds + (((wave * C::NT1 + n) * C::KS1 + kc) * 64 + lane) * 16);
+                for (int kc = 0; kc < C::KS1; ++kc)
+                    w1[n][kc] = ld128(wrs, (uint32_t)((P::SLOTS0 + ((wave * C::NT1 + n) * C::KS1 + kc) * 64 + lane) * 16));
+        }
 #pragma unroll
         for (int i = 0; i < C::PF; ++i) load_tile(ring[i], t + i);
         // A tiles: registers hold the next PF tiles; the current one is written
