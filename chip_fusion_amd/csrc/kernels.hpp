@@ -406,70 +406,76 @@ __device__ inline void kmap64(int k, int* ks, int* g) {
     }
 }
 
+// One weight matrix (KD x ND, row-major in global memory) -> LDS, cut into
+// units of 16-byte loads: 4 consecutive rows x 8 columns for 16-bit types
+// (four loads), 2 columns of one row for fp64 (one load).  Unit u of the
+// matrix is handled by thread u mod NTHREADS.
 template <int DT, int KD, int ND, int KM, int NTHREADS>
-__device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t ldb, int tid) {
-    using T = Ty<DT>;
-    constexpr int KS = KD / T::KW;
-    if constexpr (DT != DT_F64) {
-        // unit: 4 consecutive rows x 8 consecutive columns; the loads of a
-        // batch of units are all issued before any of them is written
-        constexpr int UN = ND / 8, UNITS = (KD / 4) * UN;
-        constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS, BATCH = ITERS < 4 ? ITERS : 4;
-        const unsigned short* B = (const unsigned short*)Bg;
-        for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
-            u4_t r[BATCH][4];
+struct WStage {
+    static constexpr bool H = DT != DT_F64;
+    static constexpr int KS = KD / Ty<DT>::KW;
+    static constexpr int UN = H ? ND / 8 : ND / 2;              // units per row (group)
+    static constexpr int UNITS = H ? (KD / 4) * UN : KD * UN;
+    static constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS;
+    static constexpr int LPU = H ? 4 : 1;                       // loads per unit
+    static constexpr int VGPRS = ITERS * LPU * 4;               // to hold all of a thread's units
+    typedef u4_t unit_t[LPU];
+
+    __device__ static inline void load(unit_t& r, const void* Bg, int64_t ldb, int u) {
+        if constexpr (H) {
+            const unsigned short* B = (const unsigned short*)Bg;
+            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
 #pragma unroll
-            for (int q = 0; q < BATCH; ++q) {
-                const int u = tid + (i0 + q) * NTHREADS;
-                if (u < UNITS) {
-                    const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
+            for (int i = 0; i < 4; ++i) r[i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
+        } else {
+            const double* B = (const double*)Bg;
+            r[0] = *(const u4_t*)(B + (int64_t)(u / UN) * ldb + (u % UN) * 2);
+        }
+    }
+    __device__ static inline void store(unsigned char* lds, const unit_t& r, int u) {
+        if constexpr (H) {
+            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
+            int ks, g, u0;
+            kmap16<DT, KM>(k4, &ks, &g, &u0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) r[q][i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
-                }
+            for (int c = 0; c < 8; ++c) {
+                const int n = n0 + c, t = n >> 4;
+                const int sh = (c & 1) * 16;
+                const unsigned e0 = (r[0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[1][c >> 1] >> sh) & 0xFFFFu;
+                const unsigned e2 = (r[2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[3][c >> 1] >> sh) & 0xFFFFu;
+                const int lane = (n & 15) + 16 * g;
+                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) = u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
             }
+        } else {
+            const int k = u / UN, n0 = (u % UN) * 2;
+            int ks, g;
+            kmap64<KM>(k, &ks, &g);
 #pragma unroll
-            for (int q = 0; q < BATCH; ++q) {
-                const int u = tid + (i0 + q) * NTHREADS;
-                if (u >= UNITS) continue;
-                const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
-                int ks, g, u0;
-                kmap16<DT, KM>(k4, &ks, &g, &u0);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int n = n0 + c, t = n >> 4;
-                    const int sh = (c & 1) * 16;
-                    const unsigned e0 = (r[q][0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[q][1][c >> 1] >> sh) & 0xFFFFu;
-                    const unsigned e2 = (r[q][2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[q][3][c >> 1] >> sh) & 0xFFFFu;
-                    const int lane = (n & 15) + 16 * g;
-                    *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) =
-                        u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-                }
+            for (int c = 0; c < 2; ++c) {
+                const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
+                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{r[0][2 * c], r[0][2 * c + 1]};
             }
         }
-    } else {
-        constexpr int UN = ND / 2, UNITS = KD * UN;
-        constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS, BATCH = ITERS < 2 ? ITERS : 2;
-        const double* B = (const double*)Bg;
-        for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
-            u4_t v[BATCH];
+    }
+};
+
+// Stage one matrix in batches: the loads of a batch of units are all issued
+// before any of them is written.
+template <int DT, int KD, int ND, int KM, int NTHREADS>
+__device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t ldb, int tid) {
+    using W = WStage<DT, KD, ND, KM, NTHREADS>;
+    constexpr int BMAX = W::H ? 4 : 2, BATCH = W::ITERS < BMAX ? W::ITERS : BMAX;
+    for (int i0 = 0; i0 < W::ITERS; i0 += BATCH) {
+        typename W::unit_t r[BATCH];
 #pragma unroll
-            for (int q = 0; q < BATCH; ++q) {
-                const int u = tid + (i0 + q) * NTHREADS;
-                if (u < UNITS) v[q] = *(const u4_t*)(B + (int64_t)(u / UN) * ldb + (u % UN) * 2);
-            }
+        for (int q = 0; q < BATCH; ++q) {
+            const int u = tid + (i0 + q) * NTHREADS;
+            if (u < W::UNITS) W::load(r[q], Bg, ldb, u);
+        }
 #pragma unroll
-            for (int q = 0; q < BATCH; ++q) {
-                const int u = tid + (i0 + q) * NTHREADS;
-                if (u >= UNITS) continue;
-                const int k = u / UN, n0 = (u % UN) * 2;
-                int ks, g;
-                kmap64<KM>(k, &ks, &g);
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
-                    *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{v[q][2 * c], v[q][2 * c + 1]};
-                }
-            }
+        for (int q = 0; q < BATCH; ++q) {
+            const int u = tid + (i0 + q) * NTHREADS;
+            if (u < W::UNITS) W::store(lds, r[q], u);
         }
     }
 }
@@ -510,6 +516,8 @@ struct Cfg {
     static constexpr int NLAST = dim(NST);
     static_assert(LDS_BYTES <= 160 * 1024, "weights do not fit in LDS");
     static_assert(DT == DT_F64 || D0 % 32 == 0, "K must be a multiple of 32");
+    static_assert(DT == DT_F64 || NST < 2 || (D1 % 32 == 0 && (NST < 3 || D2 % 32 == 0)),
+                  "intermediate widths must be multiples of 32");
     static_assert(DT != DT_F64 || D0 % 8 == 0, "fp64 K must be a multiple of 8");
 };
 
@@ -546,23 +554,29 @@ __device__ inline void load_a(typename Ty<C::DT>::op_t (&a)[C::MT][C::KS(0)],
 // Weight fragments come either from LDS -- read a window of FW fragments ahead
 // of the MFMAs that use them, so LDS latency overlaps the matrix pipe -- or
 // from registers (RW).  Each fragment feeds MT MFMAs (one per 16-row sub-tile).
-template <class C, int S, bool ORN_STAGE>
+// Output tiles are finished in order and handed, a group at a time, to
+// sink(first_tile, group): a group is one K-step of the next stage (two
+// 16-column tiles for 16-bit types, one for fp64) or the last, partial group.
+// Only one group of accumulators is live at a time, which leaves the
+// registers to the A tiles in flight.
+template <class C> struct Grp { static constexpr int G = C::DT == DT_F64 ? 1 : 2; };
+
+template <class C, int S, bool ORN_STAGE, class Sink>
 __device__ inline void gemm_stage(const unsigned char* lds,
                                   const typename Ty<C::DT>::op_t (&wreg)[C::NF(S)],
-                                  const typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S)],
-                                  typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)], int lane) {
+                                  const typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S)], int lane,
+                                  Sink&& sink) {
     using T = Ty<C::DT>;
     using op_t = typename T::op_t;
-    constexpr int KS = C::KS(S), NF = C::NT(S) * KS, FW = C::RW ? 1 : C::FW;
+    using acc_t = typename T::acc_t;
+    constexpr int KS = C::KS(S), NT = C::NT(S), NF = NT * KS, FW = C::RW ? 1 : C::FW;
+    constexpr int G = Grp<C>::G;
     const unsigned char* w = lds + C::woff(S) + lane * C::FB;
     auto frag = [&](int i) {
         if constexpr (C::RW) return wreg[i];
         else return *(const op_t*)(w + i * 64 * C::FB);
     };
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < C::NT(S); ++t) acc[mt][t] = typename T::acc_t{};
+    acc_t acc[C::MT][G];
     op_t fr[FW];
 #pragma unroll
     for (int i = 0; i < FW - 1; ++i)
@@ -575,39 +589,39 @@ __device__ inline void gemm_stage(const unsigned char* lds,
             fr[0] = frag(i);
         }
         const int t = i / KS, ks = i % KS;
+        if (ks == 0) {
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) acc[mt][t % G] = acc_t{};
+        }
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
             if constexpr (ORN_STAGE)
-                acc[mt][t] = T::mma(op[mt][ks], fr[i % FW], acc[mt][t]);   // C0 = A . B0
+                acc[mt][t % G] = T::mma(op[mt][ks], fr[i % FW], acc[mt][t % G]);   // C0 = A . B0
             else
-                acc[mt][t] = T::mma(fr[i % FW], op[mt][ks], acc[mt][t]);   // C^T = W^T . X^T
+                acc[mt][t % G] = T::mma(fr[i % FW], op[mt][ks], acc[mt][t % G]);   // C^T = W^T . X^T
         }
+        if (ks == KS - 1 && (t % G == G - 1 || t == NT - 1)) sink(t - t % G, acc);
     }
 }
 
-// Stage output -> operands of the next stage (round, then rearrange).
-template <class C, int S, bool ORN_STAGE>
-__device__ inline void to_operands(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)],
-                                   typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S + 1)],
-                                   code_t code, unsigned char* scratch, int lane) {
+// One finished group of a stage -> operands of the next stage (round, then
+// rearrange): K-step t/2 (16-bit) or K-steps 4t..4t+3 (fp64).
+template <class C, bool ORN_STAGE, int KSN>
+__device__ inline void group_to_operands(int t, const typename Ty<C::DT>::acc_t (&g)[C::MT][Grp<C>::G],
+                                         typename Ty<C::DT>::op_t (&op)[C::MT][KSN], code_t code,
+                                         unsigned char* scratch, int lane) {
     if constexpr (C::DT != DT_F64) {
-        static_assert(C::NT(S) % 2 == 0, "intermediate width must be a multiple of 32");
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-            for (int c = 0; c < C::NT(S) / 2; ++c)
-                op[mt][c] = remap_unit16<C::DT, C::MODE, ORN_STAGE>(acc[mt][2 * c], acc[mt][2 * c + 1],
-                                                                   code, scratch, lane);
+            op[mt][t / 2] = remap_unit16<C::DT, C::MODE, ORN_STAGE>(g[mt][0], g[mt][1], code, scratch, lane);
     } else {
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
+        for (int mt = 0; mt < C::MT; ++mt) {
+            double o[4];
+            remap_unit64<C::MODE, ORN_STAGE>(g[mt][0], o, code, scratch, lane);
 #pragma unroll
-            for (int t = 0; t < C::NT(S); ++t) {
-                double o[4];
-                remap_unit64<C::MODE, ORN_STAGE>(acc[mt][t], o, code, scratch, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) op[mt][4 * t + i] = o[i];
-            }
+            for (int i = 0; i < 4; ++i) op[mt][4 * t + i] = o[i];
+        }
     }
 }
 
@@ -615,8 +629,8 @@ __device__ inline void to_operands(const typename Ty<C::DT>::acc_t (&acc)[C::MT]
 // D over four lane groups (16 rows per store instruction, 64 bytes of each),
 // which the memory system handles poorly; the wave therefore writes its tile
 // into its private LDS region (16-byte chunks, XOR-swizzled by row to avoid
-// bank conflicts) and reads it back so that consecutive lanes store
-// consecutive 16-byte chunks of whole rows.
+// bank conflicts), group by group as the tiles finish, and then reads it back
+// so that consecutive lanes store consecutive 16-byte chunks of whole rows.
 template <class C>
 struct DStage {
     static constexpr int RB = C::NLAST * C::ELT;            // bytes per row of D
@@ -630,44 +644,45 @@ struct DStage {
 };
 
 template <class C, int S>
-__device__ inline void store_d(const typename Ty<C::DT>::acc_t (&acc)[C::MT][C::NT(S)],
-                               __amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane, unsigned char* scratch) {
+__device__ inline void group_to_dstage(int t, const typename Ty<C::DT>::acc_t (&g)[C::MT][Grp<C>::G],
+                                       unsigned char* scratch, int lane) {
     using DS = DStage<C>;
-    const int m = lane & 15, g = lane >> 4;
+    const int m = lane & 15, grp = lane >> 4;
     if constexpr (C::DT != DT_F64) {
         using T = Ty<C::DT>;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
             const int row = 16 * mt + m;
-#pragma unroll
-            for (int c = 0; c < C::NT(S) / 2; ++c) {
-                const f4_t a0 = acc[mt][2 * c], a1 = acc[mt][2 * c + 1];
+            if (t + 1 < C::NT(S)) {
+                const f4_t a0 = g[mt][0], a1 = g[mt][1];
                 unsigned x0 = T::pack(a0[0], a0[1]), x1 = T::pack(a0[2], a0[3]);
                 unsigned y0 = T::pack(a1[0], a1[1]), y1 = T::pack(a1[2], a1[3]);
-                regroup_pairs(x0, x1, y0, y1);          // lane group g: columns 32c + 8g ..+7
-                *(u4_t*)(scratch + DS::pos(row, 4 * c + g)) = u4_t{x0, x1, y0, y1};
-            }
-            if constexpr (C::NT(S) % 2) {
-                constexpr int t = C::NT(S) - 1;         // columns 16t + 4g ..+3
-                const f4_t a0 = acc[mt][t];
-                *(u2_t*)(scratch + DS::pos(row, 2 * t + (g >> 1)) + (g & 1) * 8) =
+                regroup_pairs(x0, x1, y0, y1);          // lane group grp: columns 16t + 8grp ..+7
+                *(u4_t*)(scratch + DS::pos(row, 2 * t + grp)) = u4_t{x0, x1, y0, y1};
+            } else {                                    // odd last tile: columns 16t + 4grp ..+3
+                const f4_t a0 = g[mt][0];
+                *(u2_t*)(scratch + DS::pos(row, 2 * t + (grp >> 1)) + (grp & 1) * 8) =
                     u2_t{T::pack(a0[0], a0[1]), T::pack(a0[2], a0[3])};
             }
         }
     } else {
-        // lane group g holds columns g + 4v; regroup to 4g + v (32 contiguous bytes)
+        // lane group grp holds columns grp + 4v; regroup to 4grp + v (32 contiguous bytes)
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-            for (int t = 0; t < C::NT(S); ++t) {
-                double a[4] = {acc[mt][t][0], acc[mt][t][1], acc[mt][t][2], acc[mt][t][3]};
-                transpose_rows64(a);
-                const int row = 16 * mt + m;
-                const u2_t p0 = dsplit(a[0]), p1 = dsplit(a[1]), p2 = dsplit(a[2]), p3 = dsplit(a[3]);
-                *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * g)) = u4_t{p0[0], p0[1], p1[0], p1[1]};
-                *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * g + 1)) = u4_t{p2[0], p2[1], p3[0], p3[1]};
-            }
+        for (int mt = 0; mt < C::MT; ++mt) {
+            double a[4] = {g[mt][0][0], g[mt][0][1], g[mt][0][2], g[mt][0][3]};
+            transpose_rows64(a);
+            const int row = 16 * mt + m;
+            const u2_t p0 = dsplit(a[0]), p1 = dsplit(a[1]), p2 = dsplit(a[2]), p3 = dsplit(a[3]);
+            *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * grp)) = u4_t{p0[0], p0[1], p1[0], p1[1]};
+            *(u4_t*)(scratch + DS::pos(row, 8 * t + 2 * grp + 1)) = u4_t{p2[0], p2[1], p3[0], p3[1]};
+        }
     }
+}
+
+// The staged tile -> whole-row, non-temporal 16-byte stores.
+template <class C>
+__device__ inline void flush_d(__amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane, unsigned char* scratch) {
+    using DS = DStage<C>;
     wave_lds_fence();
     constexpr int CHUNKS = C::ROWS_WAVE * DS::CPR;
     static_assert(CHUNKS % 64 == 0, "tile must be whole store instructions");
@@ -691,6 +706,55 @@ __device__ inline void stage_all_weights(unsigned char* lds, const KArgs& args, 
         stage_weights<C::DT, C::dim(2), C::dim(3), C::KMS(2), C::THREADS>(
             lds + C::woff(2), (const char*)args.B[2] + (int64_t)b * args.sB[2] * C::ELT, args.ldb[2], tid);
 }
+
+// Weights held in registers between their loads and their LDS writes, so the
+// A prefetches can be issued in between and the two latencies overlap.  Used
+// when every stage's share of a thread fits in a few registers.
+template <class C, int S> struct WSt {
+    static constexpr bool LIVE = S < C::NST;
+    using W = WStage<C::DT, LIVE ? C::dim(S) : 32, LIVE ? C::dim(S + 1) : 16, C::KMS(S), C::THREADS>;
+    static constexpr int VGPRS = LIVE ? W::VGPRS : 0;
+};
+template <class C> struct WHeld {
+    static constexpr bool FITS = WSt<C, 0>::VGPRS + WSt<C, 1>::VGPRS + WSt<C, 2>::VGPRS <= 32;
+    typename WSt<C, 0>::W::unit_t h0[WSt<C, 0>::W::ITERS];
+    typename WSt<C, 1>::W::unit_t h1[WSt<C, 1>::W::ITERS];
+    typename WSt<C, 2>::W::unit_t h2[WSt<C, 2>::W::ITERS];
+
+    template <int S, class H>
+    __device__ static inline void load1(H& h, const KArgs& args, int b, int tid) {
+        if constexpr (WSt<C, S>::LIVE) {
+            using W = typename WSt<C, S>::W;
+            const char* Bg = (const char*)args.B[S] + (int64_t)b * args.sB[S] * C::ELT;
+#pragma unroll
+            for (int i = 0; i < W::ITERS; ++i) {
+                const int u = tid + i * C::THREADS;
+                if (u < W::UNITS) W::load(h[i], Bg, args.ldb[S], u);
+            }
+        }
+    }
+    template <int S, class H>
+    __device__ static inline void store1(const H& h, unsigned char* lds, int tid) {
+        if constexpr (WSt<C, S>::LIVE) {
+            using W = typename WSt<C, S>::W;
+#pragma unroll
+            for (int i = 0; i < W::ITERS; ++i) {
+                const int u = tid + i * C::THREADS;
+                if (u < W::UNITS) W::store(lds + C::woff(S), h[i], u);
+            }
+        }
+    }
+    __device__ inline void load(const KArgs& args, int b, int tid) {
+        load1<0>(h0, args, b, tid);
+        load1<1>(h1, args, b, tid);
+        load1<2>(h2, args, b, tid);
+    }
+    __device__ inline void store(unsigned char* lds, int tid) const {
+        store1<0>(h0, lds, tid);
+        store1<1>(h1, lds, tid);
+        store1<2>(h2, lds, tid);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // The fused kernel: persistent workgroups over tiles of ROWS_WG rows.
@@ -772,33 +836,30 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
             (char*)args.D + ((int64_t)b * args.sD + (rows ? row0 : 0) * args.ldd) * C::ELT,
             (uint32_t)(rows * args.ldd * C::ELT));
 
-        acc_t acc0[C::MT][C::NT(0)];
-        gemm_stage<C, 0, C::ORN>(lds, wr0, a, acc0, lane);
+        auto to_d = [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
+            group_to_dstage<C, C::NST - 1>(tg, g, scratch, lane);
+        };
         if constexpr (C::NST == 1) {
-            store_d<C, 0>(acc0, d_rs, args.ldd, lane, scratch);
+            gemm_stage<C, 0, C::ORN>(lds, wr0, a, lane, to_d);
         } else {
             op_t op1[C::MT][C::KS(1)];
-            to_operands<C, 0, C::ORN>(acc0, op1, code, scratch, lane);
-            acc_t acc1[C::MT][C::NT(1)];
-            gemm_stage<C, 1, false>(lds, wr1, op1, acc1, lane);
+            gemm_stage<C, 0, C::ORN>(lds, wr0, a, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
+                group_to_operands<C, C::ORN>(tg, g, op1, code, scratch, lane);
+            });
             if constexpr (C::NST == 2) {
-                store_d<C, 1>(acc1, d_rs, args.ldd, lane, scratch);
+                gemm_stage<C, 1, false>(lds, wr1, op1, lane, to_d);
             } else {
                 op_t op2[C::MT][C::KS(2)];
-                to_operands<C, 1, false>(acc1, op2, code2, scratch, lane);
-                acc_t acc2[C::MT][C::NT(2)];
-                gemm_stage<C, 2, false>(lds, wr2, op2, acc2, lane);
-                store_d<C, 2>(acc2, d_rs, args.ldd, lane, scratch);
+                gemm_stage<C, 1, false>(lds, wr1, op1, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
+                    group_to_operands<C, false>(tg, g, op2, code2, scratch, lane);
+                });
+                gemm_stage<C, 2, false>(lds, wr2, op2, lane, to_d);
             }
         }
+        flush_d<C>(d_rs, args.ldd, lane, scratch);
     };
 
     const auto no_rsrc = make_rsrc(args.D, 0u);
-    acc_t zero[C::MT][C::NT(C::NST - 1)];
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int n = 0; n < C::NT(C::NST - 1); ++n) zero[mt][n] = acc_t{};
 
     // The workgroup's tiles, one batch (one set of weights) at a time.  Within
     // a batch, A tiles stream through a ring of PF+1 register sets; the loop is
@@ -813,18 +874,30 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         __syncthreads();
-        // weights first: the wait for them then does not include the A
-        // prefetches issued after them (memory counters are in order)
-        stage_all_weights<C>(lds, args, b, tid);
         // Prologue: each prefetched tile is followed by one tile's worth of
         // stores to an empty resource (dropped by the hardware), so that on
         // entry to the loop the loads in flight sit behind as many memory
         // operations as in the steady state and the first rounds wait no
         // longer than the later ones.
+        auto prologue = [&]() {
 #pragma unroll
-        for (int i = 0; i < C::PF; ++i) {
-            load_a<C>(ring[i], a_rsrc(t + i), args.lda, lane);
-            store_d<C, C::NST - 1>(zero, no_rsrc, args.ldd, lane, scratch);
+            for (int i = 0; i < C::PF; ++i) {
+                load_a<C>(ring[i], a_rsrc(t + i), args.lda, lane);
+                flush_d<C>(no_rsrc, args.ldd, lane, scratch);
+            }
+        };
+        if constexpr (WHeld<C>::FITS) {
+            // weight loads, then the A prefetches, then the weights' LDS
+            // writes: the wait for the weights (memory counters are in
+            // order) leaves the A loads in flight
+            WHeld<C> wh;
+            wh.load(args, b, tid);
+            prologue();
+            wh.store(lds, tid);
+        } else {
+            // weights first, so that their wait does not include the A loads
+            stage_all_weights<C>(lds, args, b, tid);
+            prologue();
         }
         __syncthreads();
         weights_to_regs();
