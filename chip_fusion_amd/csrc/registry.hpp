@@ -81,8 +81,8 @@ KernelDesc describe_cs() {
     };
     d.ws_elems_per_batch = (int64_t)b2bk::Packed<C>::PER_BATCH * 8;
     d.pack = [](const b2bk::KArgs& a, void* ws, int64_t batch, hipStream_t s) -> hipError_t {
-        const int64_t n = batch * b2bk::Packed<C>::PER_BATCH;
-        hipLaunchKernelGGL(b2bk::cs_pack_kernel<C>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+        const int64_t n = batch * b2bk::PackGrid<C>::PER_BATCH;
+        hipLaunchKernelGGL(b2bk::cs_pack_kernel<C>, dim3((unsigned)n), dim3(256), 0, s, a,
                            (b2bk::u4_t*)ws, batch);
         return hipGetLastError();
     };

@@ -178,7 +178,9 @@ def test_rounding_is_nearest_even(dtype):
 # Weights larger than LDS (two 256x256 matrices): column-split kernel whose
 # rearrangement goes through LDS across the workgroup's waves
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("M,batch", [(1000, 1), (777, 2), (32, 1), (1, 1)])
+# (4000, 3): 375 tiles over 256 workgroups, so some workgroups run two
+# tiles that straddle a batch boundary (two weight segments)
+@pytest.mark.parametrize("M,batch", [(1000, 1), (777, 2), (32, 1), (1, 1), (4000, 3)])
 def test_wide_cascade_parity(M, batch):
     _flush(f"wide cascade bf16 256^3 M={M} batch={batch}")
     A, Bs = synth.make_inputs(3, M=M, batch=batch)
