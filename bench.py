@@ -129,15 +129,14 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # per-launch duration of the kernel: events bracketing each launch on its stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # Duration of the launch(es) of one step, from the events around the timed
+    # region on the stream the kernels run on.  Bracketing each launch with its
+    # own events instead adds the event packets' gaps (about 3 us a launch).
+    # Where a run is more than one launch (the column-split path packs its
+    # weights first), this is the whole step, so the roofline figure below
+    # understates the fused kernel alone.
+    launch_ms = ms_per_step
+    launches = int(dict(kv.split("=") for kv in plan.info().split()).get("launches", 1))
 
     value = flop / (ms_per_step * 1e-3) / 1e12
     ai = flop / algo_bytes
@@ -164,6 +163,7 @@ def main():
     except (OSError, ValueError, KeyError):
         pass
     roof["kernel_ms"] = launch_ms
+    roof["launches_per_step"] = launches
     roof["algorithmic_bytes"] = algo_bytes
     roof["algorithmic_flop"] = flop
 

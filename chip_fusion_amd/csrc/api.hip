@@ -323,12 +323,13 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
                        std::to_string(p->dims[2]) + (p->nst == 3 ? "x" + std::to_string(p->dims[3]) : "");
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
-                  "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld",
+                  "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d",
                   p->unfused ? "unfused" : "fused", dts[p->dtype], (long long)p->batch,
                   (long long)p->M, dims.c_str(), p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : "16x16x32",
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, k->lds_bytes, p->grid[0],
-                  (long long)(p->work_bytes[0] + p->work_bytes[1] + p->wpack_bytes));
+                  (long long)(p->work_bytes[0] + p->work_bytes[1] + p->wpack_bytes),
+                  p->unfused ? p->nst : (p->fused->pack ? 2 : 1));
     return B2B_SUCCESS;
 }
 

@@ -113,7 +113,8 @@ b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);
 const char* b2b_status_string(b2b_status_t s);
 
 /* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
-   remap mode, tile, grid, LDS and workspace bytes) into buf (NUL-terminated). */
+   remap mode, tile, grid, LDS and workspace bytes, kernel launches per run)
+   into buf (NUL-terminated). */
 b2b_status_t b2b_gemm_get_info(b2b_gemm_t plan, char* buf, size_t len);
 
 /* ------------------------------------------------------------------------- */
