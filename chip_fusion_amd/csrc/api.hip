@@ -48,8 +48,6 @@ struct b2b_gemm_plan {
     const KernelDesc* stage_k[3] = {nullptr, nullptr, nullptr};   // unfused path
     void* work[2] = {nullptr, nullptr};          // unfused intermediates
     int64_t work_bytes[2] = {0, 0};
-    void* wpack = nullptr;                       // pre-packed weights (column-split path)
-    int64_t wpack_bytes = 0;
     uint16_t sched[2][b2bk::kMaxRounds][64];
     std::mutex grid_mu;
     int grid_dev = -1, grid[3] = {0, 0, 0};
@@ -128,7 +126,6 @@ b2b_status_t launch_one(b2b_gemm_plan* p, int idx, const KernelDesc* k, const vo
     b2bk::KArgs a;
     std::memset(&a, 0, sizeof a);
     a.A = A;
-    a.W = p->wpack;
     a.D = D;
     a.M = p->M;
     a.lda = lda;
@@ -149,7 +146,6 @@ b2b_status_t launch_one(b2b_gemm_plan* p, int idx, const KernelDesc* k, const vo
     if (st != B2B_SUCCESS) return st;
     if (grid > a.total_tiles) grid = a.total_tiles;
     if (grid < 1) grid = 1;
-    if (k->pack && k->pack(a, p->wpack, p->batch, stream) != hipSuccess) return B2B_ERROR_HIP;
     return k->launch(a, grid, stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
 }
 
@@ -231,14 +227,6 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
         }
         if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         const int mode = p->mode;
-        if (p->fused->pack) {
-            p->wpack_bytes = batch * p->fused->ws_elems_per_batch * es;
-            if (hipMalloc(&p->wpack, (size_t)p->wpack_bytes) != hipSuccess) {
-                (void)hipGetLastError();
-                delete p;
-                return B2B_ERROR_OUT_OF_MEMORY;
-            }
-        }
         if (mode == b2bk::MODE_BPERM) {
             if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1])) {
                 delete p;
@@ -304,11 +292,10 @@ b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const voi
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {
     if (!p) return B2B_SUCCESS;
     b2b_status_t st = B2B_SUCCESS;
-    if (p->work[0] || p->work[1] || p->wpack) {
+    if (p->work[0] || p->work[1]) {
         if (hipDeviceSynchronize() != hipSuccess) st = B2B_ERROR_HIP;
         for (void* w : p->work)
             if (w && hipFree(w) != hipSuccess) st = B2B_ERROR_HIP;
-        if (p->wpack && hipFree(p->wpack) != hipSuccess) st = B2B_ERROR_HIP;
     }
     delete p;
     return st;
@@ -328,8 +315,7 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
                   (long long)p->M, dims.c_str(), p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : "16x16x32",
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, k->lds_bytes, p->grid[0],
-                  (long long)(p->work_bytes[0] + p->work_bytes[1] + p->wpack_bytes),
-                  p->unfused ? p->nst : (p->fused->pack ? 2 : 1));
+                  (long long)(p->work_bytes[0] + p->work_bytes[1]), p->unfused ? p->nst : 1);
     return B2B_SUCCESS;
 }
 

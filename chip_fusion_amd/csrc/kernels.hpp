@@ -53,7 +53,6 @@ struct KArgs {
     const void* A;
     const void* B[3];
     void* D;
-    const void* W;                  // pre-packed weights (column-split kernel), else null
     int64_t M;
     int64_t lda, ldb[3], ldd;
     int64_t sA, sB[3], sD;          // batch strides, elements
@@ -637,7 +636,7 @@ struct DStage {
     static constexpr int CPR = RB / 16;                      // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;    // swizzle mask
     static constexpr int BYTES = C::ROWS_WAVE * RB;
-    static_assert(RB % 16 == 0 && 64 % CPR == 0 || CPR % 64 == 0, "row width not supported");
+    static_assert(RB % 16 == 0 && (64 % CPR == 0 || CPR % 64 == 0), "row width not supported");
     __device__ static inline int pos(int row, int chunk) {
         return row * RB + ((chunk ^ (row & SWZ)) << 4);
     }

@@ -22,9 +22,13 @@
 // passing through registers.  Each second-GEMM wave stages its 32 x 64 slice
 // of D in a private LDS region and writes it as whole 128-byte row segments.
 //
-// The weights are first re-laid out by a small kernel into fragment order in
-// a workspace (every workgroup needs all of them; reading them as contiguous
-// 16-byte fragments avoids staging 256 KB through LDS in every workgroup).
+// The weights reach the registers through LDS at the start of each batch
+// segment: 64-row chunks of B0 and B1 are copied row-major into LDS (buffer
+// loads that write LDS, three chunks in flight, in the space the A ring and
+// the C0 buffers use later), and each wave picks its fragments out of them
+// with transposing LDS reads (ds_read_b64_tr_b16: a 4 x 16 block of 16-bit
+// values comes back one column per lane), so the MFMA operand's K-contiguous
+// layout needs no separate re-layout pass over the weights.
 #pragma once
 #include "kernels.hpp"
 
@@ -54,6 +58,17 @@ struct CsCfg {
     static_assert(DCH == 8, "D slices are written as 128-byte row segments");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(PF <= 5 && A_LOADS == 4, "wait counts");
+    // weight staging: chunks of 64 rows (32 KB) of B0 then B1, row-major, 16-byte
+    // chunks swizzled so the transposing fragment reads are conflict-free
+    static constexpr int WROWS = 64, WCH = WROWS * N1 * ELT;      // rows and bytes per chunk
+    static constexpr int NCH0 = K / WROWS, NCH = NCH0 + N1 / WROWS;
+    static constexpr int W_LOADS = WCH / (16 * 64 * WAVES);       // 1 KB loads per wave per chunk
+    static_assert(N1 * ELT == 512 && N2 * ELT == 512 && K % WROWS == 0 && N1 % WROWS == 0,
+                  "weight staging is written for rows of 512 bytes");
+    static_assert(NCH0 == 4 && NCH == 8 && W_LOADS == 4 && NA >= 6,
+                  "staging buffers: ring slots 2-3, 4-5 and the C0 buffers");
+    __device__ static inline int wswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 3) << 2)); }
+    __device__ static inline int wpos(int r, int chunk) { return r * 512 + ((chunk ^ wswz(r)) << 4); }
     // row-major A and C0 tiles, 16-byte chunks XOR-swizzled by row
     // (conflict-free fragment reads of 16 consecutive rows)
     __device__ static inline int apos(int row, int chunk) { return row * ROW_A + ((chunk ^ (row & 15)) << 4); }
@@ -61,66 +76,6 @@ struct CsCfg {
     // D slice: 32 rows x 128 B, chunk swizzled so 16 consecutive rows cover all banks
     __device__ static inline int dpos(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 };
-
-// ---------------------------------------------------------------------------
-// Weight pre-pack: B (row-major) -> fragment-major order in a workspace, one
-// 16-byte slot (8 k of one column, natural K order) per lane and fragment, so
-// that every wave of the fused kernel loads its weight fragments with plain
-// contiguous 16-byte loads.  Slot (fragment f = t*KS + ks, lane l = i + 16g)
-// of matrix s, batch b lives at ((b * PER_BATCH) + base_s + f*64 + l) * 16.
-// ---------------------------------------------------------------------------
-template <class C>
-struct Packed {
-    static constexpr int SLOTS0 = (C::N1 / 16) * C::KS0 * 64;   // 16-byte slots of B0
-    static constexpr int SLOTS1 = (C::N2 / 16) * C::KS1 * 64;
-    static constexpr int PER_BATCH = SLOTS0 + SLOTS1;
-};
-
-// One workgroup packs a 32 (k) x 64 (n) block of one matrix: coalesced
-// 16-byte row loads into LDS, then each thread gathers the 8 k of one column
-// for one slot and writes the slots of the block as contiguous 1 KB runs.
-template <class C>
-struct PackGrid {
-    static constexpr int NB0 = C::N1 / 64, NB1 = C::N2 / 64;      // 64-column blocks per matrix
-    static constexpr int BLOCKS0 = C::KS0 * NB0, BLOCKS1 = C::KS1 * NB1;
-    static constexpr int PER_BATCH = BLOCKS0 + BLOCKS1;           // workgroups per batch
-    static_assert(C::N1 % 64 == 0 && C::N2 % 64 == 0, "pack blocks are 64 columns wide");
-};
-
-template <class C>
-__global__ __launch_bounds__(256) void cs_pack_kernel(KArgs args, u4_t* ws, int64_t batch) {
-    using P = Packed<C>;
-    using PG = PackGrid<C>;
-    constexpr int PITCH = 64 + 4;                                  // halfs per LDS row (padded)
-    __shared__ unsigned short tile[32 * PITCH];
-    const int tid = threadIdx.x;
-    const int64_t b = blockIdx.x / PG::PER_BATCH;
-    int blk = blockIdx.x % PG::PER_BATCH;
-    const int mat = blk < PG::BLOCKS0 ? 0 : 1;
-    if (mat) blk -= PG::BLOCKS0;
-    const int NB = mat ? PG::NB1 : PG::NB0, KS = mat ? C::KS1 : C::KS0;
-    const int ks = blk / NB, nb = blk % NB;
-    const unsigned short* B = (const unsigned short*)args.B[mat] + b * args.sB[mat];
-    const int64_t ldb = args.ldb[mat];
-    {
-        const int r = tid >> 3, c = tid & 7;                       // row of the block, 8-column chunk
-        const u4_t v = *(const u4_t*)(B + (int64_t)(32 * ks + r) * ldb + 64 * nb + 8 * c);
-        unsigned short* d = tile + r * PITCH + 8 * c;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            d[2 * i] = (unsigned short)(v[i] & 0xFFFFu);
-            d[2 * i + 1] = (unsigned short)(v[i] >> 16);
-        }
-    }
-    __syncthreads();
-    const int t = tid >> 6, l = tid & 63, i = l & 15, g = l >> 4;  // slot: tile t of the block, lane l
-    unsigned h[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) h[u] = tile[(8 * g + u) * PITCH + 16 * t + i];
-    const int f = (4 * nb + t) * KS + ks;                          // fragment (16-column tile, K-step)
-    ws[b * P::PER_BATCH + (mat ? P::SLOTS0 : 0) + f * 64 + l] =
-        u4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-}
 
 // Workgroup barrier with explicit waits: "s_waitcnt" for the given counts,
 // then s_barrier.  The A ring is written by buffer loads that go straight to
@@ -150,11 +105,32 @@ __device__ inline void barrier_tiles_in_flight(int tiles) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+
+// Buffer load of 16 bytes per lane that writes LDS (lane i -> lds_dst + 16 i;
+// lds_dst uniform).  Issued from inline asm so that the compiler does not add
+// a full wait for it before every later LDS read (it cannot tell which LDS
+// bytes are still in flight); the callers wait for it explicitly (vmcnt).
+// M0 carries the LDS address; nothing else in these kernels keeps a value in
+// M0 (no LDS-DMA builtins, no dynamic register indexing), so clobbering it,
+// which the compiler warns about in general, is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, const unsigned char* lds_dst, int voff) {
+    const unsigned a = (unsigned)(uintptr_t)(lds_ptr_t)lds_dst;
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 template <class C>
 __device__ __forceinline__ void cs_body(const KArgs& args) {
     using T = Ty<C::DT>;
-    using P = Packed<C>;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,9 +173,7 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
             const int q = sw * C::A_LOADS + j;                       // 1 KB piece of the slot
             const int row = q * C::ROWS_LOAD + lane / C::CPR_A, pos = lane % C::CPR_A;
             const int chunk = pos ^ (row & 15);                      // lands at apos(row, chunk)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (lds_ptr_t)(dst + q * 1024), 16, row * (int)args.lda * C::ELT + chunk * 16, 0, 0,
-                kStreamPolicy);
+            lds_dma16<true>(rs, dst + q * 1024, row * (int)args.lda * C::ELT + chunk * 16);
         }
     };
 
@@ -209,33 +183,85 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         const int nseg = t_end - t;
         B2B_BARRIER();   // the previous segment's LDS reads are over
-        {
-            // this wave's weight fragments, straight from the pre-packed workspace
-            const auto wrs = make_rsrc((const u4_t*)args.W + (int64_t)b * P::PER_BATCH,
-                                       (uint32_t)(P::PER_BATCH * 16));
-            const int base = first ? 0 : P::SLOTS0;
-#pragma unroll
-            for (int n = 0; n < C::NT0; ++n)
-#pragma unroll
-                for (int ks = 0; ks < C::KS0; ++ks)
-                    w[n][ks] = ld128(wrs, (uint32_t)((base + ((sw * C::NT0 + n) * C::KS0 + ks) * 64 + lane) * 16));
-        }
         // A prefetch depth ramps up: tiles 0..last(-1) before the first step,
         // then up to two more per step until PF tiles are ahead.  Issuing all
         // PF tiles at once delays tile 0 (every workgroup asks for its whole
         // ring at the same moment and the memory system serves them
         // interleaved); tile 0 first lets the pipeline start about as soon
         // as the weights are in.
-        auto last = [&](int s) { return s < 0 ? (C::PF - 1 < 1 ? C::PF - 1 : 1) : (2 * s + 3 < s + C::PF ? 2 * s + 3 : s + C::PF); };
-        if (first) {
+        auto last = [&](int s) { return s < 0 ? 1 : (2 * s + 3 < s + C::PF ? 2 * s + 3 : s + C::PF); };
+
+        // Weights: chunk c (64 rows of B0 for c < 4, of B1 after) goes to
+        // staging buffer c % 3 -- ring slots 2-3, ring slots 4-5, the C0
+        // buffers -- while ring slots 0-1 receive A tiles 0 and 1.  Order of
+        // issue: chunks 0-2, A tiles 0-1 (first-GEMM waves), then chunk c+3
+        // once chunk c has been read.
+        auto buf = [&](int c) -> unsigned char* {
+            const int i = c % 3;
+            return lds + (i == 0 ? 2 * C::ABYTES : i == 1 ? 4 * C::ABYTES : C::OFF_C);
+        };
+        auto load_chunk = [&](int c) {
+            const int mat = c < C::NCH0 ? 0 : 1, c4 = mat ? c - C::NCH0 : c;
+            const int64_t rows = mat ? C::N1 : C::K;
+            const auto rs = make_rsrc((const char*)args.B[mat] + (int64_t)b * args.sB[mat] * C::ELT,
+                                      (uint32_t)(rows * args.ldb[mat] * C::ELT));
+            unsigned char* dst = buf(c);
+#pragma unroll
+            for (int i = 0; i < C::W_LOADS; ++i) {
+                const int q = wave * C::W_LOADS + i;                 // 1 KB piece: rows 2q, 2q+1 of the chunk
+                const int r = 2 * q + lane / 32, pos = lane % 32;
+                const int chunk = pos ^ C::wswz(r);                  // lands at wpos(r, chunk)
+                lds_dma16<false>(rs, dst + q * 1024, (int)((C::WROWS * c4 + r) * args.ldb[mat] * C::ELT) + chunk * 16);
+            }
+        };
+        // fragment (16-column tile at n0, 32 rows from k0 of the chunk) of this
+        // wave: two transposing reads, rows k0+8g+0..3 and k0+8g+4..7
+        auto frag = [&](unsigned char* src, int n0, int k0) {
+            const int j = (lane >> 2) & 3, q = lane & 3;
+            const int chunk = (n0 >> 3) + (q >> 1);
+            u4_t out;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = k0 + 8 * g + 4 * h + j;
+                auto* p = (__attribute__((address_space(3))) unsigned char*)(lds_ptr_t)src +
+                          C::wpos(r, chunk) + (q & 1) * 8;
+                const tr4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)p);
+                out[2 * h] = ((unsigned)(unsigned short)v[0]) | ((unsigned)(unsigned short)v[1] << 16);
+                out[2 * h + 1] = ((unsigned)(unsigned short)v[2]) | ((unsigned)(unsigned short)v[3] << 16);
+            }
+            return out;
+        };
+        load_chunk(0);
+        load_chunk(1);
+        load_chunk(2);
+        if (first)
             for (int k = 0; k <= last(-1); ++k) load_tile(t + k, k);
-            barrier_tiles_in_flight<C::A_LOADS>(last(-1));   // tile 0 of the segment is in LDS
-        } else {
-            // the weights are this wave's only loads: wait for them here, in a
-            // form the compiler sees, so it adds no full wait at the step loop
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            B2B_BARRIER();
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+            // wait for chunk c: chunks min(2, 7 - c) later, and (first-GEMM
+            // waves, c <= 2) the two A tiles issued after chunk 2, stay in flight
+            if (first) {
+                if (c <= 2) VmWait<2 * C::W_LOADS + 2 * C::A_LOADS>::barrier();
+                else if (c <= 5) VmWait<2 * C::W_LOADS>::barrier();
+                else if (c == 6) VmWait<C::W_LOADS>::barrier();
+                else VmWait<0>::barrier();
+            } else {
+                if (c <= 5) VmWait<2 * C::W_LOADS>::barrier();
+                else if (c == 6) VmWait<C::W_LOADS>::barrier();
+                else VmWait<0>::barrier();
+            }
+            if (first == (c < C::NCH0)) {
+                const int c4 = c < C::NCH0 ? c : c - C::NCH0;
+#pragma unroll
+                for (int n = 0; n < C::NT0; ++n)
+#pragma unroll
+                    for (int kl = 0; kl < C::WROWS / 32; ++kl)
+                        w[n][(C::WROWS / 32) * c4 + kl] = frag(buf(c), C::N1W * sw + 16 * n, 32 * kl);
+            }
+            B2B_BARRIER();   // chunk c has been read: its buffer is free
+            if (c + 3 < C::NCH) load_chunk(c + 3);
         }
+        // here the weights are in registers and A tiles 0 and 1 are in LDS
         for (int s = 0; s <= nseg; ++s) {
             if (first) {
                 if (s < nseg) {

@@ -14,9 +14,6 @@ struct KernelDesc {
     int mt, waves, threads, rows_wg, lds_bytes;
     const void* fn;   // the __global__ function, for occupancy queries
     hipError_t (*launch)(const b2bk::KArgs&, int grid, hipStream_t);
-    // optional weight pre-pack into a workspace of ws_elems_per_batch elements per batch
-    int64_t ws_elems_per_batch = 0;
-    hipError_t (*pack)(const b2bk::KArgs&, void* ws, int64_t batch, hipStream_t) = nullptr;
 };
 
 std::vector<KernelDesc>& registry();
@@ -77,13 +74,6 @@ KernelDesc describe_cs() {
     d.fn = (const void*)&b2bk::cs_kernel<C>;
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
         hipLaunchKernelGGL(b2bk::cs_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
-        return hipGetLastError();
-    };
-    d.ws_elems_per_batch = (int64_t)b2bk::Packed<C>::PER_BATCH * 8;
-    d.pack = [](const b2bk::KArgs& a, void* ws, int64_t batch, hipStream_t s) -> hipError_t {
-        const int64_t n = batch * b2bk::PackGrid<C>::PER_BATCH;
-        hipLaunchKernelGGL(b2bk::cs_pack_kernel<C>, dim3((unsigned)n), dim3(256), 0, s, a,
-                           (b2bk::u4_t*)ws, batch);
         return hipGetLastError();
     };
     return d;
