@@ -23,13 +23,11 @@
  * dimensions in elements; batches are strided by batch_stride elements
  * (0 broadcasts a weight matrix to every batch; A and D must not use 0).
  *
- * Ownership: the caller owns every matrix and the stream.  A plan owns host
- * tables and, where its kernel needs one, a device workspace that
- * b2b_gemm_create allocates and b2b_gemm_destroy frees: the intermediates of
- * B2B_FLAG_UNFUSED, or the weights re-packed into register-fragment order for
- * the column-split kernel (weights too large for LDS).  b2b_gemm_run rewrites
- * that workspace on every call, so two runs of one plan that overlap on
- * different streams race; runs of different plans never share memory.
+ * Ownership: the caller owns every matrix and the stream.  A plan owns only
+ * host tables and, with B2B_FLAG_UNFUSED, a device workspace for the
+ * intermediates that b2b_gemm_create allocates and b2b_gemm_destroy frees
+ * (b2b_gemm_run rewrites it on every call, so two unfused runs of one plan
+ * that overlap on different streams race; fused runs share no memory).
  *
  * Errors: every call returns a status and never aborts; on failure of create
  * *plan is set to NULL.  b2b_gemm_run only enqueues work on the stream and
