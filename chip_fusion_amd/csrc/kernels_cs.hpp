@@ -78,29 +78,28 @@ struct CsCfg {
 };
 
 // Workgroup barrier with explicit waits: "s_waitcnt" for the given counts,
-// then s_barrier.  The A ring is written by buffer loads that go straight to
-// LDS and complete through vmcnt, so the wait for the tile needed next is
-// written out (the tiles behind it stay in flight); the asm also keeps the
-// compiler from moving memory accesses across the barrier.
-#define B2B_BARRIER_VM(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define B2B_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-
-template <int N> struct VmWait;
-#define B2B_VMWAIT(n) template <> struct VmWait<n> { __device__ static inline void barrier() { B2B_BARRIER_VM(n); } };
-B2B_VMWAIT(0) B2B_VMWAIT(2) B2B_VMWAIT(4) B2B_VMWAIT(6) B2B_VMWAIT(8) B2B_VMWAIT(10) B2B_VMWAIT(12)
-B2B_VMWAIT(16) B2B_VMWAIT(20) B2B_VMWAIT(24) B2B_VMWAIT(28) B2B_VMWAIT(32)
-#undef B2B_VMWAIT
+// then s_barrier.  The A ring and the weight chunks are written by buffer
+// loads that go straight to LDS and complete through vmcnt, so the wait for
+// the data needed next is written out (the loads behind it stay in flight);
+// the asm also keeps the compiler from moving memory accesses across the
+// barrier.
+template <int N>
+__device__ inline void barrier_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+__device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Barrier that first waits until at most `tiles` A tiles (L loads each) of
 // this wave are still in flight; `tiles` is uniform, 0 <= tiles <= 4.
 template <int L>
 __device__ inline void barrier_tiles_in_flight(int tiles) {
     switch (tiles) {
-        case 0: VmWait<0>::barrier(); break;
-        case 1: VmWait<L>::barrier(); break;
-        case 2: VmWait<2 * L>::barrier(); break;
-        case 3: VmWait<3 * L>::barrier(); break;
-        default: VmWait<4 * L>::barrier(); break;
+        case 0: barrier_vm<0>(); break;
+        case 1: barrier_vm<L>(); break;
+        case 2: barrier_vm<2 * L>(); break;
+        case 3: barrier_vm<3 * L>(); break;
+        default: barrier_vm<4 * L>(); break;
     }
 }
 
@@ -182,7 +181,7 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         const int nseg = t_end - t;
-        B2B_BARRIER();   // the previous segment's LDS reads are over
+        barrier_lds();   // the previous segment's LDS reads are over
         // A prefetch depth ramps up: tiles 0..last(-1) before the first step,
         // then up to two more per step until PF tiles are ahead.  Issuing all
         // PF tiles at once delays tile 0 (every workgroup asks for its whole
@@ -241,14 +240,14 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
             // wait for chunk c: chunks min(2, 7 - c) later, and (first-GEMM
             // waves, c <= 2) the two A tiles issued after chunk 2, stay in flight
             if (first) {
-                if (c <= 2) VmWait<2 * C::W_LOADS + 2 * C::A_LOADS>::barrier();
-                else if (c <= 5) VmWait<2 * C::W_LOADS>::barrier();
-                else if (c == 6) VmWait<C::W_LOADS>::barrier();
-                else VmWait<0>::barrier();
+                if (c <= 2) barrier_vm<2 * C::W_LOADS + 2 * C::A_LOADS>();
+                else if (c <= 5) barrier_vm<2 * C::W_LOADS>();
+                else if (c == 6) barrier_vm<C::W_LOADS>();
+                else barrier_vm<0>();
             } else {
-                if (c <= 5) VmWait<2 * C::W_LOADS>::barrier();
-                else if (c == 6) VmWait<C::W_LOADS>::barrier();
-                else VmWait<0>::barrier();
+                if (c <= 5) barrier_vm<2 * C::W_LOADS>();
+                else if (c == 6) barrier_vm<C::W_LOADS>();
+                else barrier_vm<0>();
             }
             if (first == (c < C::NCH0)) {
                 const int c4 = c < C::NCH0 ? c : c - C::NCH0;
@@ -258,7 +257,7 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
                     for (int kl = 0; kl < C::WROWS / 32; ++kl)
                         w[n][(C::WROWS / 32) * c4 + kl] = frag(buf(c), C::N1W * sw + 16 * n, 32 * kl);
             }
-            B2B_BARRIER();   // chunk c has been read: its buffer is free
+            barrier_lds();   // chunk c has been read: its buffer is free
             if (c + 3 < C::NCH) load_chunk(c + 3);
         }
         // here the weights are in registers and A tiles 0 and 1 are in LDS
@@ -347,7 +346,7 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
                         st128(d_rs, (uint32_t)((row * args.ldd + sw * C::N2W) * C::ELT + ch * 16), v);
                     }
                 }
-                B2B_BARRIER();
+                barrier_lds();
             }
         }
         t = t_end;
