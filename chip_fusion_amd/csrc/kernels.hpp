@@ -26,6 +26,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 namespace b2bk {
 
@@ -246,6 +247,56 @@ __device__ inline void exchange64(const double (&src)[4], double (&dst)[4], VecU
     for (int e = 0; e < 4; ++e) dst[e] = djoin(u2_t{d[2 * e], d[2 * e + 1]});
 }
 
+// Workgroup barrier with explicit waits: "s_waitcnt" for the given counts,
+// then s_barrier.  The A ring and the weight chunks are written by buffer
+// loads that go straight to LDS and complete through vmcnt, so the wait for
+// the data needed next is written out (the loads behind it stay in flight);
+// the asm also keeps the compiler from moving memory accesses across the
+// barrier.
+template <int N>
+__device__ inline void barrier_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+__device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Barrier that first waits until at most `tiles` A tiles (L loads each) of
+// this wave are still in flight; `tiles` is uniform, 0 <= tiles <= 4.
+template <int L>
+__device__ inline void barrier_tiles_in_flight(int tiles) {
+    switch (tiles) {
+        case 0: barrier_vm<0>(); break;
+        case 1: barrier_vm<L>(); break;
+        case 2: barrier_vm<2 * L>(); break;
+        case 3: barrier_vm<3 * L>(); break;
+        default: barrier_vm<4 * L>(); break;
+    }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+
+// Buffer load of 16 bytes per lane that writes LDS (lane i -> lds_dst + 16 i;
+// lds_dst uniform).  Issued from inline asm so that the compiler does not add
+// a full wait for it before every later LDS read (it cannot tell which LDS
+// bytes are still in flight); the callers wait for it explicitly (vmcnt).
+// M0 carries the LDS address; nothing else in these kernels keeps a value in
+// M0 (no LDS-DMA builtins, no dynamic register indexing), so clobbering it,
+// which the compiler warns about in general, is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, const unsigned char* lds_dst, int voff) {
+    const unsigned a = (unsigned)(uintptr_t)(lds_ptr_t)lds_dst;
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ inline void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -369,24 +420,9 @@ __device__ inline void remap_unit64(d4_t acc, double (&out)[4], code_t code, uns
 // ---------------------------------------------------------------------------
 // Weights in LDS, fragment-major: the operand fragment (tile t, K-step ks)
 // occupies 64 lanes x FB bytes; lane l = n%16 + 16*g holds B[k(ks,g,u)][16t+n%16]
-// for its slots u.  Staging reads B row-major from global memory and scatters.
+// for its slots u.
 // ---------------------------------------------------------------------------
-template <int DT, int KM>
-__device__ inline void kmap16(int k4, int* ks, int* g, int* u0) {
-    // k4: first of four consecutive k (multiple of 4); returns K-step, lane
-    // group and first slot of the run (the run stays in one lane).
-    if constexpr (KM == KM_REL) {
-        const int c = k4 >> 5, r = k4 & 31;
-        *ks = c;
-        *g = (r & 15) >> 2;
-        *u0 = (r >> 4) * 4;
-    } else {
-        *ks = k4 >> 5;
-        *g = (k4 & 31) >> 3;
-        *u0 = k4 & 7;
-    }
-}
-
+// fp64 K order: K-step and lane group of row k (one slot per lane and K-step).
 template <int KM>
 __device__ inline void kmap64(int k, int* ks, int* g) {
     if constexpr (KM == KM_PAIR64) {
@@ -405,55 +441,31 @@ __device__ inline void kmap64(int k, int* ks, int* g) {
     }
 }
 
-// One weight matrix (KD x ND, row-major in global memory) -> LDS, cut into
-// units of 16-byte loads: 4 consecutive rows x 8 columns for 16-bit types
-// (four loads), 2 columns of one row for fp64 (one load).  Unit u of the
-// matrix is handled by thread u mod NTHREADS.
+// fp64 weights: one matrix (KD x ND, row-major in global memory) -> LDS, cut
+// into units of 2 columns of one row (one 16-byte load, two 8-byte slots).
+// Unit u of the matrix is handled by thread u mod NTHREADS.
 template <int DT, int KD, int ND, int KM, int NTHREADS>
 struct WStage {
-    static constexpr bool H = DT != DT_F64;
+    static_assert(DT == DT_F64, "16-bit weights are staged by stage_tr16");
     static constexpr int KS = KD / Ty<DT>::KW;
-    static constexpr int UN = H ? ND / 8 : ND / 2;              // units per row (group)
-    static constexpr int UNITS = H ? (KD / 4) * UN : KD * UN;
+    static constexpr int UN = ND / 2;                           // units per row
+    static constexpr int UNITS = KD * UN;
     static constexpr int ITERS = (UNITS + NTHREADS - 1) / NTHREADS;
-    static constexpr int LPU = H ? 4 : 1;                       // loads per unit
-    static constexpr int VGPRS = ITERS * LPU * 4;               // to hold all of a thread's units
-    typedef u4_t unit_t[LPU];
+    static constexpr int VGPRS = ITERS * 4;                     // to hold all of a thread's units
+    typedef u4_t unit_t[1];
 
     __device__ static inline void load(unit_t& r, const void* Bg, int64_t ldb, int u) {
-        if constexpr (H) {
-            const unsigned short* B = (const unsigned short*)Bg;
-            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = *(const u4_t*)(B + (int64_t)(k4 + i) * ldb + n0);
-        } else {
-            const double* B = (const double*)Bg;
-            r[0] = *(const u4_t*)(B + (int64_t)(u / UN) * ldb + (u % UN) * 2);
-        }
+        const double* B = (const double*)Bg;
+        r[0] = *(const u4_t*)(B + (int64_t)(u / UN) * ldb + (u % UN) * 2);
     }
     __device__ static inline void store(unsigned char* lds, const unit_t& r, int u) {
-        if constexpr (H) {
-            const int k4 = (u / UN) * 4, n0 = (u % UN) * 8;
-            int ks, g, u0;
-            kmap16<DT, KM>(k4, &ks, &g, &u0);
+        const int k = u / UN, n0 = (u % UN) * 2;
+        int ks, g;
+        kmap64<KM>(k, &ks, &g);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int n = n0 + c, t = n >> 4;
-                const int sh = (c & 1) * 16;
-                const unsigned e0 = (r[0][c >> 1] >> sh) & 0xFFFFu, e1 = (r[1][c >> 1] >> sh) & 0xFFFFu;
-                const unsigned e2 = (r[2][c >> 1] >> sh) & 0xFFFFu, e3 = (r[3][c >> 1] >> sh) & 0xFFFFu;
-                const int lane = (n & 15) + 16 * g;
-                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 16 + u0 * 2) = u2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
-            }
-        } else {
-            const int k = u / UN, n0 = (u % UN) * 2;
-            int ks, g;
-            kmap64<KM>(k, &ks, &g);
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
-                *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{r[0][2 * c], r[0][2 * c + 1]};
-            }
+        for (int c = 0; c < 2; ++c) {
+            const int n = n0 + c, t = n >> 4, lane = (n & 15) + 16 * g;
+            *(u2_t*)(lds + ((t * KS + ks) * 64 + lane) * 8) = u2_t{r[0][2 * c], r[0][2 * c + 1]};
         }
     }
 };
@@ -463,7 +475,7 @@ struct WStage {
 template <int DT, int KD, int ND, int KM, int NTHREADS>
 __device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t ldb, int tid) {
     using W = WStage<DT, KD, ND, KM, NTHREADS>;
-    constexpr int BMAX = W::H ? 4 : 2, BATCH = W::ITERS < BMAX ? W::ITERS : BMAX;
+    constexpr int BATCH = W::ITERS < 2 ? W::ITERS : 2;
     for (int i0 = 0; i0 < W::ITERS; i0 += BATCH) {
         typename W::unit_t r[BATCH];
 #pragma unroll
@@ -510,9 +522,17 @@ struct Cfg {
     static constexpr int WSCRATCH = (MODE == MODE_LDS && NST > 1 && LdsRemap<DT>::BYTES > DSTAGE)
                                         ? LdsRemap<DT>::BYTES : DSTAGE;
     static constexpr int SCRATCH = WAVES * WSCRATCH;
-    static constexpr int LDS_BYTES = WBYTES + SCRATCH;
+    // 16-bit weights are staged row-major through the area after the weight
+    // slots before the first tile: widen it to hold all of them at once where
+    // LDS allows (their row-major size equals their fragment-major size)
+    static constexpr int STAGE = (DT != DT_F64 && WBYTES > SCRATCH && 2 * WBYTES <= 160 * 1024)
+                                     ? WBYTES : SCRATCH;
+    static constexpr int LDS_BYTES = WBYTES + STAGE;
     static constexpr int KMS(int s) { return s == 0 ? KM0 : (MODE == MODE_RELABEL ? KM_REL : KM_NAT); }
     static constexpr int NLAST = dim(NST);
+    // memory operations of the A prefetch prologue (16-bit): per tile MT x KS(0)
+    // 16-byte loads and one flush of dummy D stores (16-byte, whole rows)
+    static constexpr int PROLOGUE_OPS = PF * (MT * (D0 / 32) + 16 * MT * NLAST_ * ELT / 16 / 64);
     static_assert(LDS_BYTES <= 160 * 1024, "weights do not fit in LDS");
     static_assert(DT == DT_F64 || D0 % 32 == 0, "K must be a multiple of 32");
     static_assert(DT == DT_F64 || NST < 2 || (D1 % 32 == 0 && (NST < 3 || D2 % 32 == 0)),
@@ -692,6 +712,132 @@ __device__ inline void flush_d(__amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane,
         st128(rs, (uint32_t)(row * ldd * C::ELT + q * 16), v);
     }
     wave_lds_fence();
+}
+
+// 16-bit weights -> fragment-major LDS, by way of the wave-scratch area (free
+// before the first tile): rounds of RCH rows of B_s are copied row-major into
+// the scratch area (buffer loads that write LDS, 16-byte chunks swizzled by
+// row), then each wave turns whole fragments into their slots with two
+// transposing reads (ds_read_b64_tr_b16: every 16-lane group gets a 4 x 16
+// block back one column per lane) and one contiguous 16-byte write per lane.
+// Loads, reads and writes are all conflict-free; nothing is scattered.
+template <class C>
+struct Tr16 {
+    // swizzle of row r's 16-byte chunks (CPR per row) such that the 16 rows
+    // one transposing read touches (8g + j, or 4g + j for the relabelled
+    // order, plus 0 or 4/16) spread their 32-byte pieces over all banks
+    template <int CPR>
+    __device__ static inline int swz(int r) {
+        if constexpr (CPR >= 32) return 2 * ((r & 3) | (((r >> 3) & 3) << 2));
+        else if constexpr (CPR == 16) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+        else return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+    }
+    // row (within a 32-row K-step) of slot element u of lane group g
+    template <int KM>
+    __device__ static inline int krow(int g, int u) {
+        if constexpr (KM == KM_REL) return 4 * g + 16 * (u >> 2) + (u & 3);
+        else return 8 * g + u;
+    }
+};
+
+template <class C, int S>
+struct Tr16Geom {
+    static constexpr int KD = C::dim(S), ND = C::dim(S + 1), KM = C::KMS(S);
+    static constexpr int PITCH = ND * 2, CPR = PITCH / 16, RPP = 1024 / PITCH;   // rows per 1 KB piece
+    static constexpr int RCH0 = (C::STAGE / PITCH) / 32 * 32;
+    static constexpr int RCH = RCH0 < KD ? RCH0 : KD;                            // rows per round
+    static constexpr int KS = KD / 32, NT = ND / 16, BYTES = KD * PITCH;
+    static_assert(ND % 16 == 0 && 1024 % PITCH == 0 && CPR >= 8 && RCH >= 32 && KD % 32 == 0,
+                  "16-bit weight staging");
+};
+
+// rows [r0, r0 + rows) of B_S -> scratch area at byte offset off (row-major, swizzled)
+template <class C, int S>
+__device__ inline void tr16_copy(unsigned char* scr, int off, const KArgs& args, int b, int r0, int rows,
+                                 int wave, int lane) {
+    using G = Tr16Geom<C, S>;
+    const auto rs = make_rsrc((const char*)args.B[S] + (int64_t)b * args.sB[S] * C::ELT,
+                              (uint32_t)(G::KD * args.ldb[S] * C::ELT));
+    for (int p = wave; p < rows / G::RPP; p += C::WAVES) {
+        const int r = p * G::RPP + lane / G::CPR, pos = lane % G::CPR;
+        lds_dma16<false>(rs, scr + off + p * 1024,
+                         (int)((r0 + r) * args.ldb[S] * C::ELT) +
+                             ((pos ^ Tr16<C>::template swz<G::CPR>(r)) << 4));
+    }
+}
+
+// the fragments of those rows (whole K-steps) -> their slots in the weight area
+template <class C, int S>
+__device__ inline void tr16_slots(unsigned char* lds, const unsigned char* scr, int off, int r0, int rows,
+                                  int wave, int lane) {
+    using G = Tr16Geom<C, S>;
+    using TR = Tr16<C>;
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3, kst = rows / 32;
+    for (int f = wave; f < G::NT * kst; f += C::WAVES) {
+        const int t = f / kst, ksl = f % kst;
+        const int chunk = 2 * t + (q >> 1);           // 16-byte chunk holding columns 16t + 4q ..
+        u4_t out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 32 * ksl + TR::template krow<G::KM>(g, 4 * h + j);
+            auto* a = (__attribute__((address_space(3))) unsigned char*)(lds_ptr_t)scr + off + r * G::PITCH +
+                      ((chunk ^ TR::template swz<G::CPR>(r)) << 4) + (q & 1) * 8;
+            const tr4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)a);
+            out[2 * h] = ((unsigned)(unsigned short)v[0]) | ((unsigned)(unsigned short)v[1] << 16);
+            out[2 * h + 1] = ((unsigned)(unsigned short)v[2]) | ((unsigned)(unsigned short)v[3] << 16);
+        }
+        *(u4_t*)(lds + C::woff(S) + ((t * G::KS + r0 / 32 + ksl) * 64 + lane) * 16) = out;
+    }
+}
+
+// All stages' weights.  `issue_a` issues the A prefetch (NA_OPS memory
+// operations); it goes out right after the first copies, so its latency
+// overlaps the staging, and the waits for the copies leave it in flight.
+template <class C, int NA_OPS, class F>
+__device__ inline void stage_tr16_all(unsigned char* lds, const KArgs& args, int b, int wave, int lane,
+                                      F&& issue_a) {
+    using G0 = Tr16Geom<C, 0>;
+    using G1 = Tr16Geom<C, (C::NST > 1 ? 1 : 0)>;
+    using G2 = Tr16Geom<C, (C::NST > 2 ? 2 : 0)>;
+    unsigned char* scr = lds + C::WBYTES;
+    constexpr int TOTAL = G0::BYTES + (C::NST > 1 ? G1::BYTES : 0) + (C::NST > 2 ? G2::BYTES : 0);
+    if constexpr (TOTAL <= C::STAGE) {
+        // everything at once: one wait, one pass
+        tr16_copy<C, 0>(scr, 0, args, b, 0, G0::KD, wave, lane);
+        if constexpr (C::NST > 1) tr16_copy<C, 1>(scr, G0::BYTES, args, b, 0, G1::KD, wave, lane);
+        if constexpr (C::NST > 2) tr16_copy<C, 2>(scr, G0::BYTES + G1::BYTES, args, b, 0, G2::KD, wave, lane);
+        issue_a();
+        barrier_vm<NA_OPS>();
+        tr16_slots<C, 0>(lds, scr, 0, 0, G0::KD, wave, lane);
+        if constexpr (C::NST > 1) tr16_slots<C, 1>(lds, scr, G0::BYTES, 0, G1::KD, wave, lane);
+        if constexpr (C::NST > 2) tr16_slots<C, 2>(lds, scr, G0::BYTES + G1::BYTES, 0, G2::KD, wave, lane);
+        barrier_lds();
+    } else {
+        // round by round through the scratch area; the A prefetch follows the
+        // first round's copies
+        bool first = true;
+        auto rounds = [&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            using G = Tr16Geom<C, S>;
+#pragma unroll 1
+            for (int r0 = 0; r0 < G::KD; r0 += G::RCH) {
+                const int rows = G::KD - r0 < G::RCH ? G::KD - r0 : G::RCH;
+                tr16_copy<C, S>(scr, 0, args, b, r0, rows, wave, lane);
+                if (first) {
+                    issue_a();
+                    barrier_vm<NA_OPS>();
+                    first = false;
+                } else {
+                    barrier_vm<0>();
+                }
+                tr16_slots<C, S>(lds, scr, 0, r0, rows, wave, lane);
+                barrier_lds();
+            }
+        };
+        rounds(std::integral_constant<int, 0>{});
+        if constexpr (C::NST > 1) rounds(std::integral_constant<int, 1>{});
+        if constexpr (C::NST > 2) rounds(std::integral_constant<int, 2>{});
+    }
 }
 
 template <class C>
@@ -885,7 +1031,9 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
                 flush_d<C>(no_rsrc, args.ldd, lane, scratch);
             }
         };
-        if constexpr (WHeld<C>::FITS) {
+        if constexpr (C::DT != DT_F64) {
+            stage_tr16_all<C, C::PROLOGUE_OPS>(lds, args, b, wave, lane, prologue);
+        } else if constexpr (WHeld<C>::FITS) {
             // weight loads, then the A prefetches, then the weights' LDS
             // writes: the wait for the weights (memory counters are in
             // order) leaves the A loads in flight

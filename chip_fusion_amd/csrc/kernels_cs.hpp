@@ -77,56 +77,6 @@ struct CsCfg {
     __device__ static inline int dpos(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 };
 
-// Workgroup barrier with explicit waits: "s_waitcnt" for the given counts,
-// then s_barrier.  The A ring and the weight chunks are written by buffer
-// loads that go straight to LDS and complete through vmcnt, so the wait for
-// the data needed next is written out (the loads behind it stay in flight);
-// the asm also keeps the compiler from moving memory accesses across the
-// barrier.
-template <int N>
-__device__ inline void barrier_vm() {
-    static_assert(N >= 0 && N <= 63, "vmcnt");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-__device__ inline void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Barrier that first waits until at most `tiles` A tiles (L loads each) of
-// this wave are still in flight; `tiles` is uniform, 0 <= tiles <= 4.
-template <int L>
-__device__ inline void barrier_tiles_in_flight(int tiles) {
-    switch (tiles) {
-        case 0: barrier_vm<0>(); break;
-        case 1: barrier_vm<L>(); break;
-        case 2: barrier_vm<2 * L>(); break;
-        case 3: barrier_vm<3 * L>(); break;
-        default: barrier_vm<4 * L>(); break;
-    }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef short tr4_t __attribute__((ext_vector_type(4)));
-
-// Buffer load of 16 bytes per lane that writes LDS (lane i -> lds_dst + 16 i;
-// lds_dst uniform).  Issued from inline asm so that the compiler does not add
-// a full wait for it before every later LDS read (it cannot tell which LDS
-// bytes are still in flight); the callers wait for it explicitly (vmcnt).
-// M0 carries the LDS address; nothing else in these kernels keeps a value in
-// M0 (no LDS-DMA builtins, no dynamic register indexing), so clobbering it,
-// which the compiler warns about in general, is safe here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-template <bool NT>
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, const unsigned char* lds_dst, int voff) {
-    const unsigned a = (unsigned)(uintptr_t)(lds_ptr_t)lds_dst;
-    if constexpr (NT)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     : : "s"(a), "v"(voff), "s"(rs) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 template <class C>
 __device__ __forceinline__ void cs_body(const KArgs& args) {
     using T = Ty<C::DT>;
