@@ -495,15 +495,11 @@ __device__ inline void stage_weights(unsigned char* lds, const void* Bg, int64_t
 // Compile-time configuration of one kernel instance.
 // ---------------------------------------------------------------------------
 template <int DT_, int NST_, int D0, int D1, int D2, int D3, int MODE_, bool ORN_, int MT_,
-          int WAVES_, int KM0_ = (DT_ == DT_F64 ? KM_PAIR64 : KM_NAT), int PF_ = 2, int FW_ = 3,
-          bool RW_ = false>
+          int WAVES_, int KM0_ = (DT_ == DT_F64 ? KM_PAIR64 : KM_NAT), int PF_ = 2, int FW_ = 3>
 struct Cfg {
     static constexpr int DT = DT_, NST = NST_, MODE = MODE_, MT = MT_, WAVES = WAVES_;
     static constexpr int PF = PF_;   // A tiles loaded ahead of the one being computed
     static constexpr int FW = FW_;   // weight fragments in flight from LDS
-    // RW: every wave keeps all weight fragments in its registers (loaded from
-    // LDS once per batch); the MFMA loops then read no LDS at all
-    static constexpr bool RW = RW_;
     static constexpr bool ORN = ORN_;
     static constexpr int KM0 = KM0_;
     static constexpr int THREADS = 64 * WAVES;
@@ -570,9 +566,9 @@ __device__ inline void load_a(typename Ty<C::DT>::op_t (&a)[C::MT][C::KS(0)],
 }
 
 // One GEMM stage on MFMA: acc[mt][t] = sum_ks W_s(t, ks) (x) op[mt][ks].
-// Weight fragments come either from LDS -- read a window of FW fragments ahead
-// of the MFMAs that use them, so LDS latency overlaps the matrix pipe -- or
-// from registers (RW).  Each fragment feeds MT MFMAs (one per 16-row sub-tile).
+// Weight fragments come from LDS, read a window of FW fragments ahead of the
+// MFMAs that use them, so LDS latency overlaps the matrix pipe.  Each fragment
+// feeds MT MFMAs (one per 16-row sub-tile).
 // Output tiles are finished in order and handed, a group at a time, to
 // sink(first_tile, group): a group is one K-step of the next stage (two
 // 16-column tiles for 16-bit types, one for fp64) or the last, partial group.
@@ -582,19 +578,15 @@ template <class C> struct Grp { static constexpr int G = C::DT == DT_F64 ? 1 : 2
 
 template <class C, int S, bool ORN_STAGE, class Sink>
 __device__ inline void gemm_stage(const unsigned char* lds,
-                                  const typename Ty<C::DT>::op_t (&wreg)[C::NF(S)],
                                   const typename Ty<C::DT>::op_t (&op)[C::MT][C::KS(S)], int lane,
                                   Sink&& sink) {
     using T = Ty<C::DT>;
     using op_t = typename T::op_t;
     using acc_t = typename T::acc_t;
-    constexpr int KS = C::KS(S), NT = C::NT(S), NF = NT * KS, FW = C::RW ? 1 : C::FW;
+    constexpr int KS = C::KS(S), NT = C::NT(S), NF = NT * KS, FW = C::FW;
     constexpr int G = Grp<C>::G;
     const unsigned char* w = lds + C::woff(S) + lane * C::FB;
-    auto frag = [&](int i) {
-        if constexpr (C::RW) return wreg[i];
-        else return *(const op_t*)(w + i * 64 * C::FB);
-    };
+    auto frag = [&](int i) { return *(const op_t*)(w + i * 64 * C::FB); };
     acc_t acc[C::MT][G];
     op_t fr[FW];
 #pragma unroll
@@ -952,26 +944,6 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
         return make_rsrc(base, (uint32_t)(rows * args.lda * C::ELT));
     };
 
-    // weight fragments held in registers (RW); unused otherwise
-    op_t wr0[C::NF(0)], wr1[C::NF(1)], wr2[C::NF(2)];
-    auto weights_to_regs = [&]() {
-        if constexpr (C::RW) {
-#pragma unroll
-            for (int i = 0; i < C::NF(0); ++i)
-                wr0[i] = *(const op_t*)(lds + C::woff(0) + (i * 64 + lane) * C::FB);
-            if constexpr (C::NST > 1) {
-#pragma unroll
-                for (int i = 0; i < C::NF(1); ++i)
-                    wr1[i] = *(const op_t*)(lds + C::woff(1) + (i * 64 + lane) * C::FB);
-            }
-            if constexpr (C::NST > 2) {
-#pragma unroll
-                for (int i = 0; i < C::NF(2); ++i)
-                    wr2[i] = *(const op_t*)(lds + C::woff(2) + (i * 64 + lane) * C::FB);
-            }
-        }
-    };
-
     auto process = [&](int t, const op_t (&a)[C::MT][C::KS(0)]) {
         const int b = t / TB;
         const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
@@ -985,20 +957,20 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
             group_to_dstage<C, C::NST - 1>(tg, g, scratch, lane);
         };
         if constexpr (C::NST == 1) {
-            gemm_stage<C, 0, C::ORN>(lds, wr0, a, lane, to_d);
+            gemm_stage<C, 0, C::ORN>(lds, a, lane, to_d);
         } else {
             op_t op1[C::MT][C::KS(1)];
-            gemm_stage<C, 0, C::ORN>(lds, wr0, a, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
+            gemm_stage<C, 0, C::ORN>(lds, a, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
                 group_to_operands<C, C::ORN>(tg, g, op1, code, scratch, lane);
             });
             if constexpr (C::NST == 2) {
-                gemm_stage<C, 1, false>(lds, wr1, op1, lane, to_d);
+                gemm_stage<C, 1, false>(lds, op1, lane, to_d);
             } else {
                 op_t op2[C::MT][C::KS(2)];
-                gemm_stage<C, 1, false>(lds, wr1, op1, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
+                gemm_stage<C, 1, false>(lds, op1, lane, [&](int tg, const acc_t (&g)[C::MT][Grp<C>::G]) {
                     group_to_operands<C, false>(tg, g, op2, code2, scratch, lane);
                 });
-                gemm_stage<C, 2, false>(lds, wr2, op2, lane, to_d);
+                gemm_stage<C, 2, false>(lds, op2, lane, to_d);
             }
         }
         flush_d<C>(d_rs, args.ldd, lane, scratch);
@@ -1011,7 +983,7 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
     // unrolled by the ring size so every set keeps its registers (no copies,
     // which would wait on loads still in flight) and PF tiles are always being
     // fetched.  Weights are loaded before the segment, so inside it they are
-    // loop-invariant (in registers for RW, in LDS otherwise).
+    // loop-invariant in LDS.
     constexpr int RING = C::PF + 1;
     op_t ring[RING][C::MT][C::KS(0)];
     int t = t0;
@@ -1047,7 +1019,6 @@ __device__ __forceinline__ void fused_body(const KArgs& args) {
             prologue();
         }
         __syncthreads();
-        weights_to_regs();
         // Every phase either runs or leaves the loop, so no path reaches a
         // later phase (or the next round) with fewer loads in flight than the
         // steady state.
@@ -1071,13 +1042,6 @@ __global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
     fused_body<C>(args);
 }
 
-// Register-resident weights need the whole register file of a SIMD: one wave
-// per SIMD, up to 512 registers (256 VGPRs + 256 AGPRs).
-template <class C>
-__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fused_kernel_rw(KArgs args) {
-    fused_body<C>(args);
-}
 
 // ---------------------------------------------------------------------------
 // Probe: one remap unit on index payloads, through the same executors.

@@ -36,19 +36,11 @@ KernelDesc describe() {
     d.threads = C::THREADS;
     d.rows_wg = C::ROWS_WG;
     d.lds_bytes = C::LDS_BYTES;
-    if constexpr (C::RW) {
-        d.fn = (const void*)&b2bk::fused_kernel_rw<C>;
-        d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
-            hipLaunchKernelGGL(b2bk::fused_kernel_rw<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
-            return hipGetLastError();
-        };
-    } else {
-        d.fn = (const void*)&b2bk::fused_kernel<C>;
-        d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
-            hipLaunchKernelGGL(b2bk::fused_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
-            return hipGetLastError();
-        };
-    }
+    d.fn = (const void*)&b2bk::fused_kernel<C>;
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        hipLaunchKernelGGL(b2bk::fused_kernel<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+        return hipGetLastError();
+    };
     return d;
 }
 
