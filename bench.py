@@ -49,6 +49,9 @@ def main():
                          "timed steps run at settled clocks (default 0.3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables)")
+    ap.add_argument("--latency", type=int, default=0, metavar="N",
+                    help="instead of throughput: N single launches, each timed alone with HIP "
+                         "events and a synchronisation in between; prints latency percentiles")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run device-to-device copies of BYTES (scale for HBM counters)")
     args = ap.parse_args()
@@ -99,6 +102,26 @@ def main():
     def step(i):
         Ad, Bd, D = sets[i % R]
         plan.run(Ad, *Bd, D=D, stream=stream)
+
+    if args.latency:
+        # one launch at a time: event pair around it, wait for it, next launch
+        for i in range(max(args.warmup, 20)):
+            step(i)
+        torch.cuda.synchronize()
+        lat = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(args.latency):
+            e0.record(stream)
+            step(i)
+            e1.record(stream)
+            e1.synchronize()
+            lat.append(e0.elapsed_time(e1) * 1e3)
+        lat = np.array(lat)
+        print(json.dumps({"metric": "single-launch latency", "unit": "us", "launches": args.latency,
+                          "median": float(np.median(lat)), "p10": float(np.percentile(lat, 10)),
+                          "p90": float(np.percentile(lat, 90)), "min": float(lat.min()),
+                          "config": {"workload": c["name"], "plan": plan.info()}}))
+        return
 
     for i in range(args.warmup):
         step(i)
