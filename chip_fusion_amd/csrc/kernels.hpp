@@ -713,6 +713,8 @@ __device__ inline void flush_d(__amdgpu_buffer_rsrc_t rs, int64_t ldd, int lane,
 // transposing reads (ds_read_b64_tr_b16: every 16-lane group gets a 4 x 16
 // block back one column per lane) and one contiguous 16-byte write per lane.
 // Loads, reads and writes are all conflict-free; nothing is scattered.
+constexpr bool kWeightRotation = true;
+
 template <class C>
 struct Tr16 {
     // swizzle of row r's 16-byte chunks (CPR per row) such that the 16 rows
@@ -743,14 +745,20 @@ struct Tr16Geom {
                   "16-bit weight staging");
 };
 
-// rows [r0, r0 + rows) of B_S -> scratch area at byte offset off (row-major, swizzled)
+// rows [r0, r0 + rows) of B_S -> scratch area at byte offset off (row-major,
+// swizzled), in 1 KB pieces.  Workgroups of one XCD that share these weights
+// ask one L2 for them at the same moment; each starts at a different piece
+// (rotation by blockIdx / 8), which lets the L2 serve them several times
+// faster than when every workgroup asks for the same lines in the same order.
 template <class C, int S>
 __device__ inline void tr16_copy(unsigned char* scr, int off, const KArgs& args, int b, int r0, int rows,
                                  int wave, int lane) {
     using G = Tr16Geom<C, S>;
     const auto rs = make_rsrc((const char*)args.B[S] + (int64_t)b * args.sB[S] * C::ELT,
                               (uint32_t)(G::KD * args.ldb[S] * C::ELT));
-    for (int p = wave; p < rows / G::RPP; p += C::WAVES) {
+    const int np = rows / G::RPP, rot = kWeightRotation ? (int)(blockIdx.x / 8) % np : 0;
+    for (int i = wave; i < np; i += C::WAVES) {
+        const int p = i + rot < np ? i + rot : i + rot - np;
         const int r = p * G::RPP + lane / G::CPR, pos = lane % G::CPR;
         lds_dma16<false>(rs, scr + off + p * 1024,
                          (int)((r0 + r) * args.ldb[S] * C::ELT) +
