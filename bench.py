@@ -43,6 +43,11 @@ def main():
     ap.add_argument("--remap", default="auto")
     ap.add_argument("--orient-n", action="store_true")
     ap.add_argument("--unfused", action="store_true")
+    ap.add_argument("--mfma32", action="store_true",
+                    help="kernels on the 32x32x16 instruction with run-time widths")
+    ap.add_argument("--dims", default=None,
+                    help="comma-separated widths K,N1,N2[,N3] replacing the workload's (same batch, M, "
+                         "distribution and seed)")
     ap.add_argument("--rotate-bytes", type=float, default=1 << 30)
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="keep warming up (untimed) until this much GPU time has passed, so the "
@@ -77,11 +82,15 @@ def main():
     import chip_fusion_amd as cf
     import synth
 
-    c = synth.CONFIGS[args.config]
+    c = dict(synth.CONFIGS[args.config])
+    if args.dims:
+        c["dims"] = [int(x) for x in args.dims.split(",")]
+        c["name"] = (f"{c['dtype']} b{c['batch']} {c['M']}x{c['dims'][0]} . "
+                     + " . ".join(f"{c['dims'][s]}x{c['dims'][s + 1]}" for s in range(len(c["dims"]) - 1)))
     dt = c["dtype"]
     flop, algo_bytes = workload_numbers(c)
     print(f"[bench] config {args.config}: {c['name']}; generating inputs", file=sys.stderr, flush=True)
-    A, Bs = synth.make_inputs(args.config)
+    A, Bs = synth.make_inputs(c)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[dt]
@@ -96,7 +105,7 @@ def main():
         sets.append((Ad, Bd, D))
     dims = c["dims"]
     plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
-                   remap=args.remap, orient_n=args.orient_n, unfused=args.unfused)
+                   remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32)
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -179,7 +188,7 @@ def main():
         tr = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
         ent = tr["configs"].get(str(args.config))
         if (ent and tr["source_digest"] == _b.source_digest() and not args.unfused
-                and args.remap == "auto" and not args.orient_n):
+                and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims):
             roof["traffic"] = ent["hbm_bytes"]
             roof["traffic_unit"] = "bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f)" % (
                 tr["fetch_scale"], tr["write_scale"])

@@ -17,7 +17,7 @@ F16, BF16, F64 = 0, 1, 2
 DTYPES = {"f16": F16, "bf16": BF16, "f64": F64}
 TORCH_DTYPES = {F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64}
 REMAP = {"auto": 0, "bpermute": 1, "permlane": 2, "lds": 3, "relabel": 4}
-FLAG_UNFUSED, FLAG_ORIENT_N = 1, 2
+FLAG_UNFUSED, FLAG_ORIENT_N, FLAG_MFMA_32X32 = 1, 2, 4
 SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x16": 3,
           "f16_16x16x16": 4, "f64_16x16x4": 5}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
@@ -80,10 +80,11 @@ class Plan:
     """A planned cascade D = rnd(rnd(A.B0).B1)[.B2] (b2b_gemm_create)."""
 
     def __init__(self, dtype, batch, M, K, N1, N2, N3=0, ld=None, batch_stride=None,
-                 remap="auto", orient_n=False, unfused=False):
+                 remap="auto", orient_n=False, unfused=False, mfma32=False):
         self.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
         self.batch, self.M, self.dims = batch, M, [K, N1, N2] + ([N3] if N3 else [])
-        flags = (REMAP[remap] << 4) | (FLAG_ORIENT_N if orient_n else 0) | (FLAG_UNFUSED if unfused else 0)
+        flags = ((REMAP[remap] << 4) | (FLAG_ORIENT_N if orient_n else 0) | (FLAG_UNFUSED if unfused else 0)
+                 | (FLAG_MFMA_32X32 if mfma32 else 0))
         arr = ctypes.c_int64 * 5
         h = ctypes.c_void_p()
         st = lib().b2b_gemm_create(ctypes.byref(h), self.dtype, batch, M, K, N1, N2, N3,
@@ -155,10 +156,11 @@ def remap_probe(shape, mode, inp, orient_n=False, stream=None):
 
 def mfma_probe(shape, a, b, stream=None):
     """One matrix instruction on raw operands a, b ([64, elems] device tensors);
-    returns the [64, 4] accumulator registers (b2b_mfma_probe)."""
+    returns the accumulator registers, [64, 4] ([64, 16] for 32x32x16) (b2b_mfma_probe)."""
     sh = SHAPES[shape] if isinstance(shape, str) else shape
     acc_dtype = torch.float64 if a.dtype == torch.float64 else torch.float32
-    c = torch.empty((64, 4), dtype=acc_dtype, device=a.device)
+    nacc = 16 if sh in (SHAPES["f16_32x32x16"], SHAPES["bf16_32x32x16"]) else 4
+    c = torch.empty((64, nacc), dtype=acc_dtype, device=a.device)
     _check(lib().b2b_mfma_probe(sh, _ptr(a), _ptr(b), _ptr(c), _stream_ptr(stream)), "b2b_mfma_probe")
     return c
 

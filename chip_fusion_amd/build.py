@@ -4,6 +4,7 @@ import argparse
 import concurrent.futures
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -35,15 +36,32 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
+def _scratch_kernels(log):
+    """(kernel, bytes per lane) for every kernel of a resource-usage report that
+    spills to scratch memory."""
+    out, name = [], None
+    for line in log.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) and name and "kernel" in name:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src, remarks):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-x", "hip", "-c", src, "-o", obj]
-    if remarks:
-        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-x", "hip", "-c", src, "-o", obj,
+                             "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
-    return obj, r.stderr
+    # every kernel keeps its working set in registers and LDS
+    spills = _scratch_kernels(r.stderr)
+    if spills:
+        raise RuntimeError(f"{os.path.basename(src)}: kernels using scratch memory: {spills}")
+    return obj, r.stderr if remarks else ""
 
 
 def build(jobs=None, remarks=False, verbose=False):

@@ -64,7 +64,7 @@ b2b::Shape shape_of(int dt) {
 
 const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, int orn, int km0) {
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.dtype != dt || d.nst != nst || d.orn != orn) continue;
+        if (d.shape32 || d.dtype != dt || d.nst != nst || d.orn != orn) continue;
         if (nst > 1 && d.mode != mode) continue;
         if (km0 >= 0 && d.km0 != km0) continue;
         bool ok = true;
@@ -72,6 +72,28 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
         if (ok) return &d;
     }
     return nullptr;
+}
+
+// Run-time-width kernel (32x32x16) for widths dims[0..nst]: the smallest
+// width bound that holds them all, or null when a granule, a bound or LDS
+// rules the cascade out.
+const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode) {
+    if (dt == B2B_DTYPE_F64) return nullptr;
+    if (dims[0] % 32) return nullptr;
+    int64_t need = dims[0], lds = 0;
+    for (int i = 1; i <= nst; ++i) {
+        if (dims[i] % 32) return nullptr;
+        need = dims[i] > need ? dims[i] : need;
+    }
+    for (int i = 0; i < nst; ++i) lds += dims[i] * dims[i + 1] * 2;
+    if (lds > 160 * 1024) return nullptr;
+    const KernelDesc* best = nullptr;
+    for (const KernelDesc& d : b2b::registry()) {
+        if (!d.shape32 || d.dtype != dt || d.nst != nst || (nst > 1 && d.mode != mode)) continue;
+        if (d.maxd < need) continue;
+        if (!best || d.maxd < best->maxd) best = &d;
+    }
+    return best;
 }
 
 // Coordination rounds in the packed per-lane form the kernels read.
@@ -111,7 +133,14 @@ b2b_status_t grid_for(b2b_gemm_plan* p, int idx, const KernelDesc* k, int* grid)
         int cus = 0, per = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return B2B_ERROR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k->fn, k->threads, 0) != hipSuccess)
+        size_t shm = 0;
+        if (k->dyn_lds) {
+            const int64_t* w = idx == 0 && !p->unfused ? p->dims : p->dims + idx;
+            const int32_t d32[4] = {(int32_t)w[0], (int32_t)w[1], k->nst > 1 ? (int32_t)w[2] : 0,
+                                    k->nst > 2 ? (int32_t)w[3] : 0};
+            shm = (size_t)k->dyn_lds(d32);
+        }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k->fn, k->threads, shm) != hipSuccess)
             return B2B_ERROR_HIP;
         if (per < 1) per = 1;
         p->grid[idx] = cus * per;
@@ -125,6 +154,9 @@ b2b_status_t launch_one(b2b_gemm_plan* p, int idx, const KernelDesc* k, const vo
                         void* D, int64_t ldd, int64_t sD, hipStream_t stream) {
     b2bk::KArgs a;
     std::memset(&a, 0, sizeof a);
+    // widths of this launch's GEMMs: the whole cascade, or stage idx alone
+    const int64_t* w = idx == 0 && !p->unfused ? p->dims : p->dims + idx;
+    for (int i = 0; i <= k->nst; ++i) a.dims[i] = (int32_t)w[i];
     a.A = A;
     a.D = D;
     a.M = p->M;
@@ -173,12 +205,16 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
     if (batch < 1 || M < 1 || K < 1 || N1 < 1 || N2 < 1 || N3 < 0) return B2B_ERROR_INVALID_VALUE;
     if (batch > (int64_t)1 << 30 || M > (int64_t)1 << 31) return B2B_ERROR_INVALID_VALUE;
-    const uint32_t known = B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_REMAP_MASK;
+    const uint32_t known = B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_FLAG_MFMA_32X32 | B2B_REMAP_MASK;
     if (flags & ~known) return B2B_ERROR_INVALID_VALUE;
     const int mode = pick_mode(dt, flags);
     if (mode > b2bk::MODE_RELABEL) return B2B_ERROR_INVALID_VALUE;
     const int orn = (flags & B2B_FLAG_ORIENT_N) ? 1 : 0;
     if (orn && mode != b2bk::MODE_BPERM && mode != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
+    const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0;
+    if (s32 && (orn || dt == B2B_DTYPE_F64)) return B2B_ERROR_NOT_SUPPORTED;
+    // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
+    const int mode32 = (flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO ? b2bk::MODE_RELABEL : mode;
 
     const int nst = N3 > 0 ? 3 : 2;
     const int64_t dims[4] = {K, N1, N2, N3};
@@ -214,7 +250,10 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     std::memset(p->sched, 0, sizeof p->sched);
 
     if (!p->unfused) {
-        if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
+        if (s32) {
+            p->fused = find_gen(dt, nst, dims, mode32);
+            p->mode = mode32;
+        } else if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
             // the cheapest rearrangement compiled for this shape
             static const int order[] = {b2bk::MODE_RELABEL, b2bk::MODE_PERMLANE, b2bk::MODE_LDS,
                                         b2bk::MODE_BPERM};
@@ -224,6 +263,11 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
             }
         } else {
             p->fused = find_kernel(dt, nst, dims, mode, orn, -1);
+        }
+        // widths no fixed-width kernel covers: the run-time-width kernels
+        if (!p->fused && !s32 && !orn) {
+            p->fused = find_gen(dt, nst, dims, mode32);
+            p->mode = mode32;
         }
         if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         const int mode = p->mode;
@@ -238,7 +282,8 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
         for (int s = 0; s < nst; ++s) {
             const int64_t d2[4] = {dims[s], dims[s + 1], 0, 0};
             const int km0 = (s == 0 && dt == B2B_DTYPE_F64) ? b2bk::KM_PAIR64 : b2bk::KM_NAT;
-            p->stage_k[s] = find_kernel(dt, 1, d2, 0, 0, km0);
+            p->stage_k[s] = s32 ? nullptr : find_kernel(dt, 1, d2, 0, 0, km0);
+            if (!p->stage_k[s]) p->stage_k[s] = find_gen(dt, 1, d2, 0);
             if (!p->stage_k[s]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         }
         for (int s = 0; s + 1 < nst; ++s) {
@@ -306,15 +351,21 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     static const char* dts[] = {"f16", "bf16", "f64"};
     static const char* modes[] = {"none", "bpermute", "permlane", "lds", "relabel"};
     const KernelDesc* k = p->unfused ? p->stage_k[0] : p->fused;
+    const char* mfma = p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : k->shape32 ? "32x32x16" : "16x16x32";
+    int lds_bytes = k->lds_bytes;
+    if (k->dyn_lds) {
+        const int32_t d32[4] = {(int32_t)p->dims[0], (int32_t)p->dims[1], (int32_t)p->dims[2], (int32_t)p->dims[3]};
+        lds_bytes = (int)k->dyn_lds(d32);
+    }
     std::string dims = std::to_string(p->dims[0]) + "x" + std::to_string(p->dims[1]) + "x" +
                        std::to_string(p->dims[2]) + (p->nst == 3 ? "x" + std::to_string(p->dims[3]) : "");
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
                   "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d",
                   p->unfused ? "unfused" : "fused", dts[p->dtype], (long long)p->batch,
-                  (long long)p->M, dims.c_str(), p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : "16x16x32",
+                  (long long)p->M, dims.c_str(), mfma,
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
-                  k->rows_wg, k->lds_bytes, p->grid[0],
+                  k->rows_wg, lds_bytes, p->grid[0],
                   (long long)(p->work_bytes[0] + p->work_bytes[1]), p->unfused ? p->nst : 1);
     return B2B_SUCCESS;
 }
@@ -382,14 +433,16 @@ b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, con
 }
 
 b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream) {
-    int dt;
+    int dt, s32 = 0;
     if (shape == B2B_SHAPE_F16_16X16X32) dt = B2B_DTYPE_F16;
     else if (shape == B2B_SHAPE_BF16_16X16X32) dt = B2B_DTYPE_BF16;
+    else if (shape == B2B_SHAPE_F16_32X32X16) dt = B2B_DTYPE_F16, s32 = 1;
+    else if (shape == B2B_SHAPE_BF16_32X32X16) dt = B2B_DTYPE_BF16, s32 = 1;
     else if (shape == B2B_SHAPE_F64_16X16X4) dt = B2B_DTYPE_F64;
     else return B2B_ERROR_NOT_SUPPORTED;
     if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
     for (const b2b::MfmaProbeDesc& d : b2b::mfma_probe_registry())
-        if (d.dtype == dt)
+        if (d.dtype == dt && d.shape32 == s32)
             return d.launch(a, b, c, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
     return B2B_ERROR_NOT_SUPPORTED;
 }

@@ -24,3 +24,5 @@ B2B_PROBE(DT_F64, MODE_LDS, true);
 static ::b2b::MfmaProbeRegistrar mfma_probe_f16(::b2b::describe_mfma_probe<DT_F16>());
 static ::b2b::MfmaProbeRegistrar mfma_probe_bf16(::b2b::describe_mfma_probe<DT_BF16>());
 static ::b2b::MfmaProbeRegistrar mfma_probe_f64(::b2b::describe_mfma_probe<DT_F64>());
+static ::b2b::MfmaProbeRegistrar mfma32_probe_f16(::b2b::describe_mfma32_probe<DT_F16>());
+static ::b2b::MfmaProbeRegistrar mfma32_probe_bf16(::b2b::describe_mfma32_probe<DT_BF16>());

@@ -59,6 +59,7 @@ struct KArgs {
     int64_t sA, sB[3], sD;          // batch strides, elements
     int32_t tiles_per_batch;
     int32_t total_tiles;
+    int32_t dims[4];                // widths K, N1, N2, N3 (kernels with run-time widths)
     // coordination rounds per lane, p | give<<6 | r<<9: table 0 for the first
     // rearrangement (after GEMM0), table 1 for the later ones
     uint16_t sched[2][kMaxRounds][64];

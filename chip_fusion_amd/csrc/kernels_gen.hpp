@@ -1,0 +1,415 @@
+// Fused cascade on the 32x32x16 matrix instruction, with the widths given at
+// run time (any multiple of 32 up to the instance's bound).
+//
+// Page 1 ("数据处理方法、装置、设备及介质", detailed description) derives the
+// rearrangement from the register layout of one matrix instruction's result
+// and of the next one's operand, per hardware and data type; the same method
+// applies to every instruction shape.  On gfx950's v_mfma_f32_32x32x16_{f16,bf16}
+// (operand: lane l holds row l%32 and the 8 k values 8*(l/32)+u; result: lane
+// l holds column l%32 and rows 8*(v/4) + 4*(l/32) + v%4, v < 16) the first GEMM
+// is computed transposed, C0^T = B0^T . A^T, so lane l holds 16 values of row
+// l%32 of C0.  The next GEMM's operand (k = 16 per step) needs 8 of them per
+// lane:
+//   RELABEL   the next GEMM's K order follows the result layout: K-step 2t+s
+//             of 32-column tile t takes, in slot u, intermediate column
+//             32t + 16s + 8*(u/4) + 4*(l/32) + u%4, which is result register
+//             8s+u of the same lane -- nothing moves;
+//   PERMLANE  natural K order: the two 32-lane halves trade one 8-byte half of
+//             each operand (v_permlane32_swap), two swaps per K-step.
+// Nothing leaves the chip between the GEMMs.
+//
+// Weights live in LDS in blocks of 32 columns (each block all rows x 64
+// bytes, so the 4 rows a transposing read touches are 256 contiguous bytes,
+// every bank once) and every weight fragment is read with two transposing
+// reads (ds_read_b64_tr_b16: a 16-lane group gets a 4 x 16 block back one
+// column per lane).  Each wave owns 32 rows of a 256-row tile;
+// D is regrouped with the same lane-half swap into 8 consecutive columns per
+// lane and stored as 16-byte pieces of rows.
+#pragma once
+#include "kernels.hpp"
+
+namespace b2bk {
+
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+
+template <int DT> struct Ty32;
+template <> struct Ty32<DT_F16> {
+    __device__ static inline f16x_t mma(u4_t a, u4_t b, f16x_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, a),
+                                                      __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct Ty32<DT_BF16> {
+    __device__ static inline f16x_t mma(u4_t a, u4_t b, f16x_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8_t, a),
+                                                       __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
+    }
+};
+
+// NST_: GEMMs in the cascade (1 is a single GEMM, for the unfused path);
+// MAXD_: bound on every width; MODE_: MODE_RELABEL or MODE_PERMLANE;
+// PF_: A tiles fetched ahead (0 or 1, registers permitting).
+template <int DT_, int NST_, int MAXD_, int MODE_, int PF_>
+struct GenCfg {
+    static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_;
+    static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
+    static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
+    static constexpr int LDS_MAX = 160 * 1024;
+    static_assert(DT != DT_F64, "the 32x32x16 instruction exists for 16-bit types");
+    static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= 3 && (PF == 0 || PF == 1), "config");
+    static_assert(MODE == MODE_RELABEL || MODE == MODE_PERMLANE, "rearrangement");
+};
+
+// One weight matrix in LDS: `rows` x `n` 16-bit values in blocks of 32
+// columns, each block `rows` x 64 bytes (row r of block t at t*rows*64 + r*64).
+// The 4 consecutive rows a transposing read touches are 256 contiguous bytes,
+// all banks once, and a fragment's address steps by constants in the K-step.
+struct GenMat {
+    int off, rows, n, tstride;
+    __device__ inline void init(int off_, int rows_, int n_) {
+        off = off_;
+        rows = rows_;
+        n = n_;
+        tstride = rows_ * 64;
+    }
+    // byte offset of (row r, 16-bit column c)
+    __device__ inline int pos(int r, int c) const { return off + (c >> 5) * tstride + r * 64 + ((c & 31) << 1); }
+};
+
+// LDS bytes of the weights of a cascade with widths d[0..nst]; with them
+// 4 KB per wave (8 waves) of D staging when that still fits the 160 KB
+__host__ __device__ inline int64_t gen_weight_bytes(const int32_t* d, int nst) {
+    int64_t b = 0;
+    for (int s = 0; s < nst; ++s) b += (int64_t)d[s] * d[s + 1] * 2;
+    return b;
+}
+__host__ __device__ inline bool gen_stage_d(const int32_t* d, int nst) {
+    return gen_weight_bytes(d, nst) + 8 * 4096 <= 160 * 1024;
+}
+__host__ __device__ inline int64_t gen_lds_bytes(const int32_t* d, int nst) {
+    return gen_weight_bytes(d, nst) + (gen_stage_d(d, nst) ? 8 * 4096 : 0);
+}
+
+// Per-lane constants of the weight fragments of one matrix: fragment
+// (32-column tile t, K-step j) is read at base[h] + t tstride + 1024 j for
+// h = 0, 1 (two transposing reads of 4 rows each).  The K order `rel` is
+// false: k = 16j + 8*(l/32) + u, or true: k = 16j + 8*(u/4) + 4*(l/32) + u%4.
+struct GenFrag {
+    int base[2], tstride;
+    __device__ inline void init(const GenMat& m, bool rel, int lane) {
+        const int g = lane >> 4, i = lane & 15, jj = i >> 2, q = i & 3;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r0 = (rel ? 8 * h + 4 * (g >> 1) : 8 * (g >> 1) + 4 * h) + jj;
+            base[h] = m.off + r0 * 64 + 32 * (g & 1) + 8 * q;
+        }
+        tstride = m.tstride;
+    }
+};
+
+__device__ __forceinline__ u4_t gen_wfrag(const unsigned char* lds, const GenFrag& fr, int t, int j) {
+    u4_t out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        auto* a = (__attribute__((address_space(3))) unsigned char*)(lds_ptr_t)lds + fr.base[h] + t * fr.tstride +
+                  1024 * j;
+        const tr4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tr4_t*)a);
+        out[2 * h] = ((unsigned)(unsigned short)v[0]) | ((unsigned)(unsigned short)v[1] << 16);
+        out[2 * h + 1] = ((unsigned)(unsigned short)v[2]) | ((unsigned)(unsigned short)v[3] << 16);
+    }
+    return out;
+}
+
+// weights of batch b -> LDS (16-byte loads, eight in flight per thread).
+// Every thread issues the same loads (past the end: an offset beyond the
+// resource, which reads zero), so the compiler's counts of loads in flight
+// hold on every path and each LDS write waits for its own load only.
+template <class C>
+__device__ inline void gen_stage_weights(unsigned char* lds, const GenMat (&mat)[3], const KArgs& args, int b) {
+#pragma unroll
+    for (int s = 0; s < C::NST; ++s) {
+        const GenMat& m = mat[s];
+        const auto rs = make_rsrc((const char*)args.B[s] + (int64_t)b * args.sB[s] * 2,
+                                  (uint32_t)(m.rows * args.ldb[s] * 2));
+        const int cpr = m.n / 8, total = m.rows * cpr;
+        for (int i0 = 0; i0 < total; i0 += 8 * C::THREADS) {
+            u4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 8;
+                v[k] = ld128(rs, i < total ? (uint32_t)((r * args.ldb[s] + c) * 2) : 0xFFFFFFF0u);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 8;
+                if (i < total) *(u4_t*)(lds + m.pos(r, c)) = v[k];
+            }
+        }
+    }
+}
+
+// A fragments of one wave's 32 rows: K-step j holds row l%32, k = 16j + 8*(l/32) + 0..7.
+// Two K-steps (64 bytes of a row) come from two loads of 16 rows x 64 bytes
+// each -- X: rows 0-15, Y: rows 16-31, lane group g holding 16-byte chunk g
+// of the pair -- which two lane swaps turn into the operand layout:
+//   X = [X0 X1 X2 X3], Y = [Y0 Y1 Y2 Y3]  (16-lane groups)
+//   swap16 -> X = [X0 Y0 X2 Y2], Y = [X1 Y1 X3 Y3]
+//   swap32 -> X = [X0 Y0 X1 Y1] (K-step 2p), Y = [X2 Y2 X3 Y3] (K-step 2p+1).
+// All loads are issued, those past K through an empty resource (zeros, no
+// memory access): the same count on every path keeps the compiler's waits for
+// a tile from covering the next tile's loads.
+template <class C>
+__device__ __forceinline__ void gen_load_a(u4_t (&a)[C::MKS], __amdgpu_buffer_rsrc_t rs,
+                                           __amdgpu_buffer_rsrc_t none, int64_t lda, int ks, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < C::MKS / 2; ++p) {
+        const auto src = 2 * p < ks ? rs : none;
+        a[2 * p] = ld128(src, (uint32_t)((r * lda + 32 * p + 8 * g) * 2));
+        a[2 * p + 1] = ld128(src, (uint32_t)(((16 + r) * lda + 32 * p + 8 * g) * 2));
+    }
+}
+
+// the lane swaps of gen_load_a, once the loads have arrived
+template <class C>
+__device__ __forceinline__ void gen_arrange_a(u4_t (&a)[C::MKS]) {
+#pragma unroll
+    for (int p = 0; p < C::MKS / 2; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unsigned x = a[2 * p][i], y = a[2 * p + 1][i];
+            swap16(x, y);
+            swap32(x, y);
+            a[2 * p][i] = x;
+            a[2 * p + 1][i] = y;
+        }
+}
+
+// Result tile -> two K-steps of the next GEMM's operand (rounded to the type).
+template <class C>
+__device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t& o1) {
+    using T = Ty<C::DT>;
+    unsigned p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
+    // K-step s: result registers 8s..8s+7 (packed p[4s..4s+3])
+    if constexpr (C::MODE == MODE_PERMLANE) {
+        // natural K order: half 0 keeps registers 8s..8s+3 and takes the
+        // other half's; half 1 keeps 8s+4..8s+7 and takes the other half's
+        swap32(p[0], p[2]);
+        swap32(p[1], p[3]);
+        swap32(p[4], p[6]);
+        swap32(p[5], p[7]);
+    }
+    o0 = u4_t{p[0], p[1], p[2], p[3]};
+    o1 = u4_t{p[4], p[5], p[6], p[7]};
+}
+
+// Result tiles -> D.  Lane half h of a 32 x 32 result tile holds columns
+// 8a + 4h + 0..3; one lane-half swap per pair of blocks leaves 8 consecutive
+// columns per lane: n0 + 8h.. and n0 + 16 + 8h.. of row l%32.
+template <class C>
+__device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t& hi) {
+    using T = Ty<C::DT>;
+    unsigned p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
+    swap32(p[0], p[2]);
+    swap32(p[1], p[3]);
+    swap32(p[4], p[6]);
+    swap32(p[5], p[7]);
+    lo = u4_t{p[0], p[1], p[2], p[3]};
+    hi = u4_t{p[4], p[5], p[6], p[7]};
+}
+
+// A pair of result tiles (64 columns at n0; `two` false: only the first) ->
+// D through the wave's 4 KB staging region (32 rows x 128 bytes, 16-byte
+// chunks XOR-swizzled by row), read back so that each store writes 8 rows x
+// 128 contiguous bytes.  Without a staging region (stg < 0) the 16-byte
+// pieces go straight to memory.
+template <class C>
+__device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, const f16x_t& acc0, const f16x_t& acc1,
+                                               bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    u4_t c[4];
+    gen_regroup_d<C>(acc0, c[0], c[1]);
+    gen_regroup_d<C>(acc1, c[2], c[3]);
+    if (stg < 0) {
+        // chunk q of this lane sits at column n0 + 16 q + 8 h
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < 2 || two) st128(rs, (uint32_t)((m * ldd + n0 + 16 * q + 8 * h) * 2), c[q]);
+        return;
+    }
+    unsigned char* st = lds + stg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int chunk = 2 * q + h;                   // 16-byte chunk of the 128-byte row segment
+        *(u4_t*)(st + m * 128 + ((chunk ^ (m & 7)) << 4)) = c[q];
+    }
+    // LDS accesses of one wave complete in order; only the compiler must not
+    // move the reads above the writes
+    asm volatile("" ::: "memory");
+    const int ch = lane & 7, nch = two ? 8 : 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const u4_t v = *(const u4_t*)(st + r * 128 + ((ch ^ (r & 7)) << 4));
+        if (ch < nch) st128(rs, (uint32_t)((r * ldd + n0 + 8 * ch) * 2), v);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// One GEMM of the cascade on one wave's 32 rows: x holds the operand K-steps
+// (ks of them), the result has nt tiles of 32 columns, each handed to sink(t, acc).
+// Tiles go in pairs: two independent accumulation chains keep the matrix
+// core busy while either waits for its previous product.  With an odd tile
+// count the last pair computes its tile twice and drops the copy (a branch
+// per pair, not per product).  sink(t, acc_t, acc_t+1, two) takes each pair.
+template <class C, class Sink>
+__device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag& fr, const u4_t (&x)[C::MKS],
+                                         int ks, int nt, Sink&& sink) {
+#pragma unroll
+    for (int t = 0; t < C::MNT; t += 2) {
+        if (t < nt) {
+            const bool two = t + 1 < nt;
+            const int t1 = two ? t + 1 : t;
+            f16x_t acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int j = 0; j < C::MKS; ++j)
+                if (j < ks) {
+                    acc0 = Ty32<C::DT>::mma(gen_wfrag(lds, fr, t, j), x[j], acc0);
+                    acc1 = Ty32<C::DT>::mma(gen_wfrag(lds, fr, t1, j), x[j], acc1);
+                }
+            sink(t, acc0, acc1, two);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void gen_body(const KArgs& args) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = args.dims[i];
+    GenMat mat[3];
+    int off = 0;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        mat[s].init(off, s < C::NST ? d[s] : 0, s < C::NST ? d[s + 1] : 32);
+        off += s < C::NST ? d[s] * d[s + 1] * 2 : 0;
+    }
+    const int ks0 = d[0] / 16, dn = d[C::NST];
+    // the wave's D staging region follows the weights, where LDS allows
+    const int stg = gen_stage_d(d, C::NST) ? off + wave * 4096 : -1;
+    constexpr bool REL = C::MODE == MODE_RELABEL;
+    GenFrag fr[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) fr[s].init(mat[s], REL && s > 0, lane);
+
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+    const int per = args.total_tiles / G, extra = args.total_tiles % G;
+    const int t0 = lid * per + (lid < extra ? lid : extra);
+    const int t1 = t0 + per + (lid < extra ? 1 : 0);
+    if (t0 >= t1) return;
+    const int TB = args.tiles_per_batch;
+
+    int t_end = t1;
+    auto rows_of = [&](int t) {
+        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        const int64_t r = args.M - row0;
+        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
+    };
+    // tiles past the segment get an empty resource (their loads return zeros)
+    auto a_rsrc = [&](int t) {
+        const bool live = t < t_end;
+        const int tc = live ? t : t0;
+        const int64_t rows = live ? rows_of(tc) : 0;
+        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        return make_rsrc((const char*)args.A + ((int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda) * 2,
+                         (uint32_t)(rows * args.lda * 2));
+    };
+
+    auto process = [&](int t, const u4_t (&a_in)[C::MKS]) __attribute__((always_inline)) {
+        u4_t a[C::MKS];
+#pragma unroll
+        for (int j = 0; j < C::MKS; ++j) a[j] = a_in[j];
+        gen_arrange_a<C>(a);
+        const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 2,
+                                    (uint32_t)(rows * args.ldd * 2));
+        auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
+            gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
+        };
+        if constexpr (C::NST == 1) {
+            gen_gemm<C>(lds, fr[0], a, ks0, dn / 32, to_d);
+        } else {
+            u4_t o1[C::MKS];
+            gen_gemm<C>(lds, fr[0], a, ks0, d[1] / 32,
+                        [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
+                            gen_to_operand<C>(a0, o1[2 * tt], o1[2 * tt + 1]);
+                            if (two) gen_to_operand<C>(a1, o1[2 * tt + 2], o1[2 * tt + 3]);
+                        });
+            if constexpr (C::NST == 2) {
+                gen_gemm<C>(lds, fr[1], o1, d[1] / 16, dn / 32, to_d);
+            } else {
+                u4_t o2[C::MKS];
+                gen_gemm<C>(lds, fr[1], o1, d[1] / 16, d[2] / 32,
+                            [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
+                                gen_to_operand<C>(a0, o2[2 * tt], o2[2 * tt + 1]);
+                                if (two) gen_to_operand<C>(a1, o2[2 * tt + 2], o2[2 * tt + 3]);
+                            });
+                gen_gemm<C>(lds, fr[2], o2, d[2] / 16, dn / 32, to_d);
+            }
+        }
+    };
+
+    const auto no_rsrc = make_rsrc(args.A, 0u);
+    u4_t ring[C::PF + 1][C::MKS];
+    int t = t0;
+    while (t < t1) {
+        const int b = t / TB;
+        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+        __syncthreads();   // the previous segment's weight reads are over
+        gen_stage_weights<C>(lds, mat, args, b);
+        __syncthreads();
+        if constexpr (C::PF == 0) {
+            for (; t < t_end; ++t) {
+                gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+                process(t, ring[0]);
+            }
+        } else {
+            // two register sets: the next tile's A is in flight while this one is computed
+            gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+            for (;;) {
+                gen_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                process(t, ring[0]);
+                if (++t >= t_end) break;
+                gen_load_a<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                process(t, ring[1]);
+                if (++t >= t_end) break;
+            }
+        }
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gen_kernel(KArgs args) {
+    gen_body<C>(args);
+}
+
+// One 32x32x16 instruction on raw operands (64 lanes x 8 16-bit values each),
+// all 16 result registers of every lane written out: a probe of the layouts.
+template <int DT>
+__global__ __launch_bounds__(64) void mfma32_probe_kernel(const void* a, const void* b, void* c) {
+    const int lane = threadIdx.x;
+    const u4_t av = ((const u4_t*)a)[lane], bv = ((const u4_t*)b)[lane];
+    ((f16x_t*)c)[lane] = Ty32<DT>::mma(av, bv, f16x_t{});
+}
+
+}  // namespace b2bk

@@ -6,13 +6,18 @@
 
 #include "kernels.hpp"
 #include "kernels_cs.hpp"
+#include "kernels_gen.hpp"
 
 namespace b2b {
 
 struct KernelDesc {
     int dtype, nst, dims[4], mode, orn, km0;
     int mt, waves, threads, rows_wg, lds_bytes;
+    int shape32 = 0;  // 1: 32x32x16 instruction, widths at run time up to maxd (dims are 0)
+    int maxd = 0;
     const void* fn;   // the __global__ function, for occupancy queries
+    // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
+    int64_t (*dyn_lds)(const int32_t* d) = nullptr;
     hipError_t (*launch)(const b2bk::KArgs&, int grid, hipStream_t);
 };
 
@@ -71,6 +76,37 @@ KernelDesc describe_cs() {
     return d;
 }
 
+// Instances with run-time widths on the 32x32x16 instruction.
+template <class C>
+KernelDesc describe_gen() {
+    KernelDesc d;
+    d.dtype = C::DT;
+    d.nst = C::NST;
+    for (int& x : d.dims) x = 0;   // never matched by width
+    d.mode = C::NST > 1 ? C::MODE : 0;
+    d.orn = 0;
+    d.km0 = b2bk::KM_NAT;
+    d.mt = C::ROWS_WAVE / 16;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::ROWS_WG;
+    d.lds_bytes = 0;
+    d.shape32 = 1;
+    d.maxd = C::MAXD;
+    d.fn = (const void*)&b2bk::gen_kernel<C>;
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST); };
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        // dynamic LDS up to the whole 160 KB of a CU
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void*)&b2bk::gen_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
+        if (attr != hipSuccess) return attr;
+        const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST);
+        hipLaunchKernelGGL(b2bk::gen_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
 // Probe instances of the rearrangement executors.
 struct ProbeDesc {
     int dtype, mode, orn;
@@ -81,7 +117,7 @@ struct ProbeRegistrar {
     explicit ProbeRegistrar(const ProbeDesc& d) { probe_registry().push_back(d); }
 };
 struct MfmaProbeDesc {
-    int dtype;
+    int dtype, shape32;
     hipError_t (*launch)(const void*, const void*, void*, hipStream_t);
 };
 std::vector<MfmaProbeDesc>& mfma_probe_registry();
@@ -92,8 +128,20 @@ template <int DT>
 MfmaProbeDesc describe_mfma_probe() {
     MfmaProbeDesc d;
     d.dtype = DT;
+    d.shape32 = 0;
     d.launch = [](const void* a, const void* b, void* c, hipStream_t s) -> hipError_t {
         hipLaunchKernelGGL(b2bk::mfma_probe_kernel<DT>, dim3(1), dim3(64), 0, s, a, b, c);
+        return hipGetLastError();
+    };
+    return d;
+}
+template <int DT>
+MfmaProbeDesc describe_mfma32_probe() {
+    MfmaProbeDesc d;
+    d.dtype = DT;
+    d.shape32 = 1;
+    d.launch = [](const void* a, const void* b, void* c, hipStream_t s) -> hipError_t {
+        hipLaunchKernelGGL(b2bk::mfma32_probe_kernel<DT>, dim3(1), dim3(64), 0, s, a, b, c);
         return hipGetLastError();
     };
     return d;
@@ -120,6 +168,10 @@ ProbeDesc describe_probe() {
 #define B2B_CS_INSTANCE(...)                                                           \
     static ::b2b::Registrar B2B_CAT(b2b_cs_reg_, __LINE__)(                            \
         ::b2b::describe_cs<::b2bk::CsCfg<__VA_ARGS__>>())
+// B2B_GEN_INSTANCE(dtype, stages, max width, mode, A tiles ahead)
+#define B2B_GEN_INSTANCE(...)                                                          \
+    static ::b2b::Registrar B2B_CAT(b2b_gen_reg_, __LINE__)(                           \
+        ::b2b::describe_gen<::b2bk::GenCfg<__VA_ARGS__>>())
 #define B2B_INSTANCE(...)                                                              \
     static ::b2b::Registrar B2B_CAT(b2b_reg_, __LINE__)(                               \
         ::b2b::describe<::b2bk::Cfg<__VA_ARGS__>>())

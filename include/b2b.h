@@ -65,6 +65,13 @@ enum {
     B2B_FLAG_ORIENT_N = 1u << 1,   /* first GEMM computed as A.B0 (accumulator lanes hold
                                       columns); default computes it transposed so that lanes
                                       hold rows.  Only with REMAP_BPERMUTE or REMAP_LDS. */
+    B2B_FLAG_MFMA_32X32 = 1u << 2, /* fp16/bf16 only: kernels on v_mfma_f32_32x32x16 with the
+                                      widths taken at run time (K, N1..N3 multiples of
+                                      32, each at most 256, the fused path's weights at most
+                                      160 KB; the unfused path's per GEMM).  Rearrangement
+                                      REMAP_RELABEL (the default) or REMAP_PERMLANE (a swap of
+                                      32-lane halves).  Without this flag these kernels serve
+                                      fp16/bf16 cascades that no fixed-width kernel covers. */
     B2B_REMAP_AUTO = 0u << 4,      /* the library picks the rearrangement */
     B2B_REMAP_BPERMUTE = 1u << 4,  /* coordination-matrix rounds: one ds_bpermute per round */
     B2B_REMAP_PERMLANE = 2u << 4,  /* fixed lane-row swaps (v_permlane16/32_swap) */
@@ -88,9 +95,12 @@ typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
  *   batch_stride  batch strides in elements: {A, B0, B1, B2, D}; NULL means dense;
  *                 0 for a B* broadcasts it
  *   flags         B2B_FLAG_* | B2B_REMAP_*
- * Returns INVALID_VALUE for non-positive sizes, ld below the row width, or ld
- * not a multiple of 16 bytes; NOT_SUPPORTED for shapes the fused kernels do not
- * cover (then the caller may retry with B2B_FLAG_UNFUSED).
+ * Returns INVALID_VALUE for non-positive sizes, ld below the row width, ld
+ * not a multiple of 16 bytes, or unknown flags; NOT_SUPPORTED for cascades no
+ * kernel covers: fp64 widths other than the compiled ones (64), fp16/bf16 widths
+ * that break the granules or bounds of B2B_FLAG_MFMA_32X32 (and have no
+ * fixed-width kernel), or weights beyond LDS (then the caller may retry with
+ * B2B_FLAG_UNFUSED, whose per-GEMM kernels need only one matrix in LDS).
  */
 b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
                              int64_t K, int64_t N1, int64_t N2, int64_t N3,
@@ -175,8 +185,9 @@ b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, con
  * Runs one matrix instruction of `shape` on raw operand registers and writes
  * every lane's accumulator registers (a probe of the layout catalogue).
  *   a, b  device, 64 lanes x operand elements (8 x 16-bit, or 1 x fp64) each
- *   c     device, 64 lanes x accumulator elements (4 x float32, or 4 x fp64)
- * Accumulators start at zero.  Shapes: 16x16x32 f16/bf16, 16x16x4 f64.
+ *   c     device, 64 lanes x accumulator elements (4 x float32, 16 x float32 for
+ *         32x32x16, or 4 x fp64)
+ * Accumulators start at zero.  Shapes: 16x16x32 and 32x32x16 f16/bf16, 16x16x4 f64.
  */
 b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream);
 

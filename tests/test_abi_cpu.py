@@ -48,7 +48,14 @@ def _create(**kw):
     (dict(flags=1 << 12), 1),                 # unknown flag
     (dict(flags=(7 << 4)), 1),                # unknown remap mode
     (dict(flags=2 | (2 << 4)), 1),            # orientation N with permlane
-    (dict(K=96, N1=96, N2=96), 2),            # no kernel for this shape
+    (dict(K=96, N1=80, N2=96), 2),            # N1 off the 32-column granule
+    (dict(K=80, N1=64, N2=64), 2),            # K off the 32-column granule
+    (dict(K=96, N1=96, N2=288), 2),           # a width above 256
+    (dict(dtype=2, K=96, N1=96, N2=96), 2),   # fp64: fixed widths only
+    (dict(K=256, N1=256, N2=256, flags=4), 2),         # 32x32 path: 256 KB of weights
+    (dict(dtype=2, flags=4), 2),                       # 32x32 path: 16-bit types only
+    (dict(flags=4 | (1 << 4)), 2),                     # 32x32 path: no coordination rounds
+    (dict(flags=4 | 2 | (3 << 4)), 2),                 # 32x32 path: orientation T only
     (dict(batch=2, bs=[0, 4096, 4096, 0, 8192]), 1),   # A broadcast over batches
 ])
 def test_create_rejects(kw, status):
@@ -65,6 +72,33 @@ def test_create_accepts_and_destroy():
     assert b"path=fused" in buf.value and b"remap=relabel" in buf.value
     assert cf.lib().b2b_gemm_destroy(h) == 0
     assert cf.lib().b2b_gemm_destroy(None) == 0
+
+
+def _info(**kw):
+    st, h = _create(**kw)
+    assert st == 0 and h.value, st
+    buf = ctypes.create_string_buffer(512)
+    assert cf.lib().b2b_gemm_get_info(h, buf, 512) == 0
+    assert cf.lib().b2b_gemm_destroy(h) == 0
+    return dict(kv.split("=", 1) for kv in buf.value.decode().split())
+
+
+@pytest.mark.parametrize("kw,expect", [
+    # widths no fixed-width kernel covers go to the run-time-width kernels
+    (dict(K=96, N1=160, N2=64), dict(path="fused", mfma="32x32x16", remap="relabel", lds_bytes=str(51200 + 32768))),
+    (dict(dtype=1, K=32, N1=32, N2=256, N3=32), dict(mfma="32x32x16", dims="32x32x256x32")),
+    (dict(K=96, N1=160, N2=64, flags=2 << 4), dict(mfma="32x32x16", remap="permlane")),
+    # the configurations' widths keep their fixed-width kernels unless asked
+    (dict(), dict(mfma="16x16x32", remap="relabel")),
+    (dict(flags=4), dict(mfma="32x32x16", remap="relabel", lds_bytes=str(16384 + 32768))),
+    (dict(K=128, N1=128, N2=128, N3=64, flags=4 | (2 << 4)), dict(mfma="32x32x16", remap="permlane")),
+    # the 256-wide cascade (256 KB of weights) keeps its column-split kernel
+    (dict(dtype=1, K=256, N1=256, N2=256), dict(mfma="16x16x32", remap="lds")),
+])
+def test_plan_selection(kw, expect):
+    info = _info(**kw)
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
 
 
 def test_run_rejects_bad_pointers():
@@ -114,3 +148,12 @@ def test_schedules_valid_and_match_oracle(shape, orient, packed):
     ok, why = R.validate(H, rel)
     assert ok, why
     assert H == R.coordination_matrix(rel)
+
+
+def test_build_rejects_scratch_spills():
+    from chip_fusion_amd import build
+    log = ("x.hpp:1:1: remark: Function Name: _ZN4b2bk12fused_kernelI1AEEvv [-Rpass-analysis]\n"
+           "x.hpp:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis]\n"
+           "x.hpp:1:1: remark: Function Name: _ZN4b2bk10gen_kernelI1BEEvv [-Rpass-analysis]\n"
+           "x.hpp:1:1: remark:     ScratchSize [bytes/lane]: 80 [-Rpass-analysis]\n")
+    assert build._scratch_kernels(log) == [("_ZN4b2bk10gen_kernelI1BEEvv", 80)]

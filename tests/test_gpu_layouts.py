@@ -11,7 +11,8 @@ from oracle import remap as R
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape", ["f16_16x16x32", "bf16_16x16x32", "f64_16x16x4"])
+@pytest.mark.parametrize("shape", ["f16_16x16x32", "bf16_16x16x32", "f16_32x32x16", "bf16_32x32x16",
+                                   "f64_16x16x4"])
 def test_mfma_layout(shape):
     sh = R.SHAPES[shape]
     rng = np.random.default_rng(1)
