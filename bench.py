@@ -104,8 +104,12 @@ def main():
         D = torch.empty((c["batch"], c["M"], c["dims"][-1]), dtype=A0.dtype, device=dev)
         sets.append((Ad, Bd, D))
     dims = c["dims"]
-    plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
-                   remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32)
+    if len(dims) <= 4:
+        plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
+                       remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32)
+    else:   # longer cascades: the chain entry points
+        plan = cf.Chain(dt, c["batch"], c["M"], dims, remap=args.remap, unfused=args.unfused,
+                        mfma32=args.mfma32)
     stream = torch.cuda.current_stream()
 
     def step(i):

@@ -38,19 +38,23 @@ std::vector<MfmaProbeDesc>& mfma_probe_registry() {
 
 using b2b::KernelDesc;
 
+constexpr int kMaxSt = b2bk::kMaxStages;
+
 struct b2b_gemm_plan {
     int dtype = 0, nst = 0, mode = 0, orn = 0;
-    int64_t batch = 0, M = 0, dims[4] = {0, 0, 0, 0};
-    int64_t ld[5] = {0, 0, 0, 0, 0}, bs[5] = {0, 0, 0, 0, 0};
+    int64_t batch = 0, M = 0, dims[kMaxSt + 1] = {};
+    // leading dimensions and batch strides (elements): [0] A, [1 + s] B_s, [nst + 1] D
+    int64_t ld[kMaxSt + 2] = {}, bs[kMaxSt + 2] = {};
     uint32_t flags = 0;
     bool unfused = false;
-    const KernelDesc* fused = nullptr;          // fused path
-    const KernelDesc* stage_k[3] = {nullptr, nullptr, nullptr};   // unfused path
-    void* work[2] = {nullptr, nullptr};          // unfused intermediates
-    int64_t work_bytes[2] = {0, 0};
+    bool chain = false;                          // made by b2b_chain_create
+    const KernelDesc* fused = nullptr;           // fused path
+    const KernelDesc* stage_k[kMaxSt] = {};      // unfused path
+    void* work[kMaxSt - 1] = {};                 // unfused intermediates
+    int64_t work_bytes[kMaxSt - 1] = {};
     uint16_t sched[2][b2bk::kMaxRounds][64];
     std::mutex grid_mu;
-    int grid_dev = -1, grid[3] = {0, 0, 0};
+    int grid_dev = -1, grid[kMaxSt] = {};
 };
 
 namespace {
@@ -136,8 +140,8 @@ b2b_status_t grid_for(b2b_gemm_plan* p, int idx, const KernelDesc* k, int* grid)
         size_t shm = 0;
         if (k->dyn_lds) {
             const int64_t* w = idx == 0 && !p->unfused ? p->dims : p->dims + idx;
-            const int32_t d32[4] = {(int32_t)w[0], (int32_t)w[1], k->nst > 1 ? (int32_t)w[2] : 0,
-                                    k->nst > 2 ? (int32_t)w[3] : 0};
+            int32_t d32[kMaxSt + 1] = {};
+            for (int i = 0; i <= k->nst; ++i) d32[i] = (int32_t)w[i];
             shm = (size_t)k->dyn_lds(d32);
         }
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k->fn, k->threads, shm) != hipSuccess)
@@ -196,14 +200,22 @@ const char* b2b_status_string(b2b_status_t s) {
     return "unknown status";
 }
 
-b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
-                             int64_t K, int64_t N1, int64_t N2, int64_t N3, const int64_t* ld,
-                             const int64_t* batch_stride, uint32_t flags) {
+}  // extern "C"
+
+namespace {
+
+// Validates and plans a cascade of nst GEMMs with widths d[0..nst]; L and S hold
+// nst + 2 leading dimensions and batch strides ([0] A, [1 + s] B_s, [nst + 1] D)
+// or are null (dense).
+b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
+                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain) {
     if (!plan) return B2B_ERROR_INVALID_VALUE;
     *plan = nullptr;
-    const int dt = (int)dtype;
     if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
-    if (batch < 1 || M < 1 || K < 1 || N1 < 1 || N2 < 1 || N3 < 0) return B2B_ERROR_INVALID_VALUE;
+    if (nst < 1 || nst > kMaxSt || !d) return B2B_ERROR_INVALID_VALUE;
+    if (batch < 1 || M < 1) return B2B_ERROR_INVALID_VALUE;
+    for (int i = 0; i <= nst; ++i)
+        if (d[i] < 1 || d[i] > (int64_t)1 << 24) return B2B_ERROR_INVALID_VALUE;
     if (batch > (int64_t)1 << 30 || M > (int64_t)1 << 31) return B2B_ERROR_INVALID_VALUE;
     const uint32_t known = B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_FLAG_MFMA_32X32 | B2B_REMAP_MASK;
     if (flags & ~known) return B2B_ERROR_INVALID_VALUE;
@@ -216,24 +228,22 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
     const int mode32 = (flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO ? b2bk::MODE_RELABEL : mode;
 
-    const int nst = N3 > 0 ? 3 : 2;
-    const int64_t dims[4] = {K, N1, N2, N3};
-    const int64_t nlast = dims[nst];
-    const int64_t dense_ld[5] = {K, N1, N2, N3 > 0 ? N3 : 0, nlast};
-    int64_t L[5], S[5];
-    for (int i = 0; i < 5; ++i) L[i] = ld ? ld[i] : dense_ld[i];
-    if (nst == 2) L[3] = 0;
-    const int64_t rows_of[5] = {M, K, N1, N2, M};
-    const int64_t width_of[5] = {K, N1, N2, N3, nlast};
+    int64_t dims[kMaxSt + 1] = {};
+    for (int i = 0; i <= nst; ++i) dims[i] = d[i];
+    const int n = nst + 2;
+    int64_t L[kMaxSt + 2], S[kMaxSt + 2];
     const int es = elt_size(dt);
-    for (int i = 0; i < 5; ++i) {
-        if (i == 3 && nst == 2) { S[i] = 0; continue; }
-        if (L[i] < width_of[i]) return B2B_ERROR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i) {
+        // operand i: A (rows M, width K), B_s (rows d[s], width d[s+1]), D (rows M, width d[nst])
+        const int64_t rows = (i == 0 || i == n - 1) ? M : dims[i - 1];
+        const int64_t width = i == 0 ? dims[0] : (i == n - 1 ? dims[nst] : dims[i]);
+        L[i] = Lin ? Lin[i] : width;
+        if (L[i] < width) return B2B_ERROR_INVALID_VALUE;
         if ((L[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
-        S[i] = batch_stride ? batch_stride[i] : rows_of[i] * L[i];
+        S[i] = Sin ? Sin[i] : rows * L[i];
         if (S[i] < 0 || (S[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
     }
-    if (batch > 1 && (S[0] == 0 || S[4] < M * L[4])) return B2B_ERROR_INVALID_VALUE;
+    if (batch > 1 && (S[0] == 0 || S[n - 1] < M * L[n - 1])) return B2B_ERROR_INVALID_VALUE;
 
     b2b_gemm_plan* p = new (std::nothrow) b2b_gemm_plan();
     if (!p) return B2B_ERROR_OUT_OF_MEMORY;
@@ -243,14 +253,17 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     p->orn = orn;
     p->batch = batch;
     p->M = M;
-    for (int i = 0; i < 4; ++i) p->dims[i] = dims[i];
-    for (int i = 0; i < 5; ++i) { p->ld[i] = L[i]; p->bs[i] = S[i]; }
+    p->chain = chain;
+    for (int i = 0; i <= nst; ++i) p->dims[i] = dims[i];
+    for (int i = 0; i < n; ++i) { p->ld[i] = L[i]; p->bs[i] = S[i]; }
     p->flags = flags;
     p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
     std::memset(p->sched, 0, sizeof p->sched);
 
     if (!p->unfused) {
-        if (s32) {
+        if (s32 || nst > 3) {
+            // the fixed-width kernels cover up to three GEMMs
+            if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
             p->fused = find_gen(dt, nst, dims, mode32);
             p->mode = mode32;
         } else if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
@@ -270,8 +283,7 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
             p->mode = mode32;
         }
         if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
-        const int mode = p->mode;
-        if (mode == b2bk::MODE_BPERM) {
+        if (p->mode == b2bk::MODE_BPERM) {
             if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1])) {
                 delete p;
                 return B2B_ERROR_NOT_SUPPORTED;
@@ -300,32 +312,26 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
     return B2B_SUCCESS;
 }
 
-b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const void* B1,
-                          const void* B2, void* D, void* stream) {
-    if (!p || !A || !B0 || !B1 || !D) return B2B_ERROR_INVALID_VALUE;
-    if ((p->nst == 3) != (B2 != nullptr)) return B2B_ERROR_INVALID_VALUE;
-    const void* ins[4] = {A, B0, B1, B2};
-    for (const void* q : ins)
-        if (q && ((uintptr_t)q % 16 || q == (const void*)D)) return B2B_ERROR_INVALID_VALUE;
-    if ((uintptr_t)D % 16) return B2B_ERROR_INVALID_VALUE;
-    hipStream_t s = (hipStream_t)stream;
-    const void* Bs[3] = {B0, B1, B2};
-    if (!p->unfused) {
-        const int64_t ldb[3] = {p->ld[1], p->ld[2], p->ld[3]};
-        const int64_t sB[3] = {p->bs[1], p->bs[2], p->bs[3]};
-        return launch_one(p, 0, p->fused, A, p->ld[0], p->bs[0], Bs, ldb, sB, D, p->ld[4], p->bs[4], s);
-    }
+// Enqueues the cascade; B holds the plan's nst weight pointers.
+b2b_status_t run_impl(b2b_gemm_t p, const void* A, const void* const* B, void* D, void* stream) {
+    if (!A || !D || (uintptr_t)A % 16 || (uintptr_t)D % 16 || A == (const void*)D) return B2B_ERROR_INVALID_VALUE;
+    for (int s = 0; s < p->nst; ++s)
+        if (!B[s] || (uintptr_t)B[s] % 16 || B[s] == (const void*)D) return B2B_ERROR_INVALID_VALUE;
+    hipStream_t st = (hipStream_t)stream;
+    const int nd = p->nst + 1;    // index of D's leading dimension and stride
+    if (!p->unfused)
+        return launch_one(p, 0, p->fused, A, p->ld[0], p->bs[0], B, p->ld + 1, p->bs + 1, D, p->ld[nd],
+                          p->bs[nd], st);
     const void* x = A;
     int64_t ldx = p->ld[0], sx = p->bs[0];
-    for (int st = 0; st < p->nst; ++st) {
-        const bool last = st + 1 == p->nst;
-        void* y = last ? D : p->work[st];
-        const int64_t ldy = last ? p->ld[4] : p->dims[st + 1];
-        const int64_t sy = last ? p->bs[4] : p->M * p->dims[st + 1];
-        const void* Bst[1] = {Bs[st]};
-        const int64_t ldb[1] = {p->ld[st + 1]};
-        const int64_t sB[1] = {p->bs[st + 1]};
-        b2b_status_t r = launch_one(p, st, p->stage_k[st], x, ldx, sx, Bst, ldb, sB, y, ldy, sy, s);
+    for (int s = 0; s < p->nst; ++s) {
+        const bool last = s + 1 == p->nst;
+        void* y = last ? D : p->work[s];
+        const int64_t ldy = last ? p->ld[nd] : p->dims[s + 1];
+        const int64_t sy = last ? p->bs[nd] : p->M * p->dims[s + 1];
+        const void* Bst[1] = {B[s]};
+        b2b_status_t r = launch_one(p, s, p->stage_k[s], x, ldx, sx, Bst, p->ld + 1 + s, p->bs + 1 + s, y, ldy,
+                                    sy, st);
         if (r != B2B_SUCCESS) return r;
         x = y;
         ldx = ldy;
@@ -334,10 +340,69 @@ b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const voi
     return B2B_SUCCESS;
 }
 
+}  // namespace
+
+extern "C" {
+
+b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
+                             int64_t K, int64_t N1, int64_t N2, int64_t N3, const int64_t* ld,
+                             const int64_t* batch_stride, uint32_t flags) {
+    if (plan) *plan = nullptr;
+    if (N3 < 0) return B2B_ERROR_INVALID_VALUE;
+    const int nst = N3 > 0 ? 3 : 2;
+    const int64_t d[4] = {K, N1, N2, N3};
+    // {lda, ldb0, ldb1, ldb2, ldd} -> one entry per operand (ldb2 only with three GEMMs)
+    int64_t L[5], S[5];
+    if (ld || batch_stride) {
+        for (int i = 0, j = 0; i < 5; ++i) {
+            if (i == 3 && nst == 2) continue;
+            L[j] = ld ? ld[i] : 0;
+            S[j] = batch_stride ? batch_stride[i] : 0;
+            ++j;
+        }
+    }
+    // missing arrays stay dense: fill the dense values create_impl would use
+    if (ld || batch_stride) {
+        const int64_t rows[5] = {M, K, N1, N2, M};
+        const int64_t width[5] = {K, N1, N2, N3, nst == 3 ? N3 : N2};
+        for (int i = 0, j = 0; i < 5; ++i) {
+            if (i == 3 && nst == 2) continue;
+            if (!ld) L[j] = width[i];
+            if (!batch_stride) S[j] = rows[i] * L[j];
+            ++j;
+        }
+    }
+    return create_impl(plan, (int)dtype, batch, M, nst, d, (ld || batch_stride) ? L : nullptr,
+                       (ld || batch_stride) ? S : nullptr, flags, false);
+}
+
+b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M, int32_t nst,
+                              const int64_t* widths, const int64_t* ld, const int64_t* batch_stride,
+                              uint32_t flags) {
+    if (plan) *plan = nullptr;
+    if (!widths) return B2B_ERROR_INVALID_VALUE;
+    return create_impl(plan, (int)dtype, batch, M, nst, widths, ld, batch_stride, flags, true);
+}
+
+b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const void* B1,
+                          const void* B2, void* D, void* stream) {
+    if (!p || p->nst < 2 || p->nst > 3) return B2B_ERROR_INVALID_VALUE;
+    if ((p->nst == 3) != (B2 != nullptr)) return B2B_ERROR_INVALID_VALUE;
+    const void* Bs[3] = {B0, B1, B2};
+    return run_impl(p, A, Bs, D, stream);
+}
+
+b2b_status_t b2b_chain_run(b2b_gemm_t p, const void* A, const void* const* B, void* D, void* stream) {
+    if (!p || !B) return B2B_ERROR_INVALID_VALUE;
+    return run_impl(p, A, B, D, stream);
+}
+
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {
     if (!p) return B2B_SUCCESS;
     b2b_status_t st = B2B_SUCCESS;
-    if (p->work[0] || p->work[1]) {
+    bool any = false;
+    for (void* w : p->work) any = any || w;
+    if (any) {
         if (hipDeviceSynchronize() != hipSuccess) st = B2B_ERROR_HIP;
         for (void* w : p->work)
             if (w && hipFree(w) != hipSuccess) st = B2B_ERROR_HIP;
@@ -351,14 +416,17 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     static const char* dts[] = {"f16", "bf16", "f64"};
     static const char* modes[] = {"none", "bpermute", "permlane", "lds", "relabel"};
     const KernelDesc* k = p->unfused ? p->stage_k[0] : p->fused;
+    int64_t work = 0;
+    for (int64_t w : p->work_bytes) work += w;
     const char* mfma = p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : k->shape32 ? "32x32x16" : "16x16x32";
     int lds_bytes = k->lds_bytes;
     if (k->dyn_lds) {
-        const int32_t d32[4] = {(int32_t)p->dims[0], (int32_t)p->dims[1], (int32_t)p->dims[2], (int32_t)p->dims[3]};
+        int32_t d32[kMaxSt + 1] = {};
+        for (int i = 0; i <= k->nst; ++i) d32[i] = (int32_t)p->dims[i];
         lds_bytes = (int)k->dyn_lds(d32);
     }
-    std::string dims = std::to_string(p->dims[0]) + "x" + std::to_string(p->dims[1]) + "x" +
-                       std::to_string(p->dims[2]) + (p->nst == 3 ? "x" + std::to_string(p->dims[3]) : "");
+    std::string dims = std::to_string(p->dims[0]);
+    for (int i = 1; i <= p->nst; ++i) dims += "x" + std::to_string(p->dims[i]);
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
                   "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d",
@@ -366,7 +434,7 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
                   (long long)p->M, dims.c_str(), mfma,
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, lds_bytes, p->grid[0],
-                  (long long)(p->work_bytes[0] + p->work_bytes[1]), p->unfused ? p->nst : 1);
+                  (long long)work, p->unfused ? p->nst : 1);
     return B2B_SUCCESS;
 }
 

@@ -49,17 +49,18 @@ enum {
 };
 
 constexpr int kMaxRounds = 8;
+constexpr int kMaxStages = 8;       // GEMMs in one cascade
 
 struct KArgs {
     const void* A;
-    const void* B[3];
+    const void* B[kMaxStages];
     void* D;
     int64_t M;
-    int64_t lda, ldb[3], ldd;
-    int64_t sA, sB[3], sD;          // batch strides, elements
+    int64_t lda, ldb[kMaxStages], ldd;
+    int64_t sA, sB[kMaxStages], sD; // batch strides, elements
     int32_t tiles_per_batch;
     int32_t total_tiles;
-    int32_t dims[4];                // widths K, N1, N2, N3 (kernels with run-time widths)
+    int32_t dims[kMaxStages + 1];   // widths K, N1, N2, ... (kernels with run-time widths)
     // coordination rounds per lane, p | give<<6 | r<<9: table 0 for the first
     // rearrangement (after GEMM0), table 1 for the later ones
     uint16_t sched[2][kMaxRounds][64];

@@ -46,7 +46,8 @@ template <> struct Ty32<DT_BF16> {
     }
 };
 
-// NST_: GEMMs in the cascade (1 is a single GEMM, for the unfused path);
+// NST_: GEMMs in the cascade (1 is a single GEMM, for the unfused path; up
+// to kMaxStages, the weights of all of them in LDS);
 // MAXD_: bound on every width; MODE_: MODE_RELABEL or MODE_PERMLANE;
 // PF_: A tiles fetched ahead (0 or 1, registers permitting).
 template <int DT_, int NST_, int MAXD_, int MODE_, int PF_>
@@ -56,7 +57,7 @@ struct GenCfg {
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
     static constexpr int LDS_MAX = 160 * 1024;
     static_assert(DT != DT_F64, "the 32x32x16 instruction exists for 16-bit types");
-    static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= 3 && (PF == 0 || PF == 1), "config");
+    static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= kMaxStages && (PF == 0 || PF == 1), "config");
     static_assert(MODE == MODE_RELABEL || MODE == MODE_PERMLANE, "rearrangement");
 };
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ u4_t gen_wfrag(const unsigned char* lds, const GenFra
 // resource, which reads zero), so the compiler's counts of loads in flight
 // hold on every path and each LDS write waits for its own load only.
 template <class C>
-__device__ inline void gen_stage_weights(unsigned char* lds, const GenMat (&mat)[3], const KArgs& args, int b) {
+__device__ inline void gen_stage_weights(unsigned char* lds, const GenMat (&mat)[C::NST], const KArgs& args, int b) {
 #pragma unroll
     for (int s = 0; s < C::NST; ++s) {
         const GenMat& m = mat[s];
@@ -288,28 +289,37 @@ __device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag
     }
 }
 
+// f(integral_constant<int, S>) for S = B .. E-1
+template <int B, int E, class F>
+__device__ __forceinline__ void gen_static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        gen_static_for<B + 1, E>(f);
+    }
+}
+
 template <class C>
 __device__ __forceinline__ void gen_body(const KArgs& args) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int d[4];
+    int d[C::NST + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = args.dims[i];
-    GenMat mat[3];
+    for (int i = 0; i <= C::NST; ++i) d[i] = args.dims[i];
+    GenMat mat[C::NST];
     int off = 0;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        mat[s].init(off, s < C::NST ? d[s] : 0, s < C::NST ? d[s + 1] : 32);
-        off += s < C::NST ? d[s] * d[s + 1] * 2 : 0;
+    for (int s = 0; s < C::NST; ++s) {
+        mat[s].init(off, d[s], d[s + 1]);
+        off += d[s] * d[s + 1] * 2;
     }
     const int ks0 = d[0] / 16, dn = d[C::NST];
     // the wave's D staging region follows the weights, where LDS allows
     const int stg = gen_stage_d(d, C::NST) ? off + wave * 4096 : -1;
     constexpr bool REL = C::MODE == MODE_RELABEL;
-    GenFrag fr[3];
+    GenFrag fr[C::NST];
 #pragma unroll
-    for (int s = 0; s < 3; ++s) fr[s].init(mat[s], REL && s > 0, lane);
+    for (int s = 0; s < C::NST; ++s) fr[s].init(mat[s], REL && s > 0, lane);
 
     const int G = gridDim.x, bid = blockIdx.x;
     const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
@@ -349,23 +359,23 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         if constexpr (C::NST == 1) {
             gen_gemm<C>(lds, fr[0], a, ks0, dn / 32, to_d);
         } else {
-            u4_t o1[C::MKS];
-            gen_gemm<C>(lds, fr[0], a, ks0, d[1] / 32,
-                        [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
-                            gen_to_operand<C>(a0, o1[2 * tt], o1[2 * tt + 1]);
-                            if (two) gen_to_operand<C>(a1, o1[2 * tt + 2], o1[2 * tt + 3]);
-                        });
-            if constexpr (C::NST == 2) {
-                gen_gemm<C>(lds, fr[1], o1, d[1] / 16, dn / 32, to_d);
-            } else {
-                u4_t o2[C::MKS];
-                gen_gemm<C>(lds, fr[1], o1, d[1] / 16, d[2] / 32,
-                            [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
-                                gen_to_operand<C>(a0, o2[2 * tt], o2[2 * tt + 1]);
-                                if (two) gen_to_operand<C>(a1, o2[2 * tt + 2], o2[2 * tt + 3]);
-                            });
-                gen_gemm<C>(lds, fr[2], o2, d[2] / 16, dn / 32, to_d);
-            }
+            // the operands of stage s come from oA (s odd) or oB (s even, s > 0)
+            u4_t oA[C::MKS], oB[C::MKS];
+            auto to_ops = [&](u4_t (&o)[C::MKS]) __attribute__((always_inline)) {
+                return [&o](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
+                    gen_to_operand<C>(a0, o[2 * tt], o[2 * tt + 1]);
+                    if (two) gen_to_operand<C>(a1, o[2 * tt + 2], o[2 * tt + 3]);
+                };
+            };
+            gen_gemm<C>(lds, fr[0], a, ks0, d[1] / 32, to_ops(oA));
+            gen_static_for<1, C::NST - 1>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int S = decltype(sc)::value;
+                if constexpr (S % 2 == 1) gen_gemm<C>(lds, fr[S], oA, d[S] / 16, d[S + 1] / 32, to_ops(oB));
+                else gen_gemm<C>(lds, fr[S], oB, d[S] / 16, d[S + 1] / 32, to_ops(oA));
+            });
+            constexpr int L = C::NST - 1;
+            if constexpr (L % 2 == 1) gen_gemm<C>(lds, fr[L], oA, d[L] / 16, dn / 32, to_d);
+            else gen_gemm<C>(lds, fr[L], oB, d[L] / 16, dn / 32, to_d);
         }
     };
 

@@ -110,9 +110,38 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
  * Enqueues the cascade on `stream` (a hipStream_t; NULL is the null stream).
  * A, B0, B1, B2, D are device pointers, 16-byte aligned; B2 must be NULL iff
  * N3 == 0; D must not alias any input.  Only enqueues; does not synchronise.
+ * Plans of one GEMM or of more than three (b2b_chain_create) take
+ * b2b_chain_run; here they return INVALID_VALUE.
  */
 b2b_status_t b2b_gemm_run(b2b_gemm_t plan, const void* A, const void* B0, const void* B1,
                           const void* B2, void* D, void* stream);
+
+/*
+ * A cascade of any number of GEMMs (page 1 allows as many fused operators as
+ * the flow holds): D = rnd(...rnd(rnd(A.B_0).B_1)...B_{nst-1}).
+ *   nst           GEMMs, 1..8
+ *   widths        nst + 1 values: K, then the column count of every B_s (the
+ *                 last is D's)
+ *   ld            nst + 2 leading dimensions in elements: A, B_0..B_{nst-1},
+ *                 D; NULL means dense
+ *   batch_stride  nst + 2 batch strides in elements, same order; NULL means
+ *                 dense; 0 for a B_s broadcasts it
+ *   flags         as for b2b_gemm_create
+ * Up to three GEMMs this plans exactly what b2b_gemm_create plans.  Longer
+ * fused cascades run on the 32x32x16 run-time-width kernels (fp16/bf16; K and
+ * the widths multiples of 32, each at most 256, all weights together at most
+ * 160 KB); the unfused path takes any such cascade whose single GEMMs are
+ * covered.  Errors as for b2b_gemm_create; INVALID_VALUE also for nst outside
+ * 1..8 or a NULL widths.
+ */
+b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M, int32_t nst,
+                              const int64_t* widths, const int64_t* ld, const int64_t* batch_stride,
+                              uint32_t flags);
+
+/* Enqueues a cascade planned by either create call; B holds its nst weight
+ * pointers (device, 16-byte aligned, none equal to D).  Same asynchrony and
+ * errors as b2b_gemm_run. */
+b2b_status_t b2b_chain_run(b2b_gemm_t plan, const void* A, const void* const* B, void* D, void* stream);
 
 /* Releases a plan (and its workspace, after the device is idle). NULL is a no-op. */
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);

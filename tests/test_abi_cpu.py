@@ -157,3 +157,65 @@ def test_build_rejects_scratch_spills():
            "x.hpp:1:1: remark: Function Name: _ZN4b2bk10gen_kernelI1BEEvv [-Rpass-analysis]\n"
            "x.hpp:1:1: remark:     ScratchSize [bytes/lane]: 80 [-Rpass-analysis]\n")
     assert build._scratch_kernels(log) == [("_ZN4b2bk10gen_kernelI1BEEvv", 80)]
+
+
+def _chain(dtype=0, batch=1, M=128, widths=(128, 128, 128, 128, 64), ld=None, bs=None, flags=0, nst=None):
+    h = ctypes.c_void_p(123)
+    n = len(widths) - 1 if nst is None else nst
+    w = (ctypes.c_int64 * len(widths))(*widths) if widths is not None else None
+    arr = ctypes.c_int64 * (len(widths) + 1 if widths else 1)
+    st = cf.lib().b2b_chain_create(ctypes.byref(h), dtype, batch, M, n, w,
+                                   arr(*ld) if ld else None, arr(*bs) if bs else None, flags)
+    return st, h
+
+
+def _chain_info(**kw):
+    st, h = _chain(**kw)
+    assert st == 0 and h.value, st
+    buf = ctypes.create_string_buffer(512)
+    assert cf.lib().b2b_gemm_get_info(h, buf, 512) == 0
+    assert cf.lib().b2b_gemm_destroy(h) == 0
+    return dict(kv.split("=", 1) for kv in buf.value.decode().split())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nst=0, widths=(128,)), 1),
+    (dict(nst=9, widths=(64,) * 10), 1),
+    (dict(widths=None, nst=2), 1),
+    (dict(widths=(128, 0, 128)), 1),
+    (dict(dtype=2, widths=(64, 64, 64, 64, 64)), 2),                 # fp64: up to three GEMMs
+    (dict(widths=(128,) * 7), 2),                                     # 192 KB of weights
+    (dict(widths=(128, 128, 128, 128, 64), flags=2 | (3 << 4)), 2),   # orientation N beyond three
+    (dict(widths=(128, 96, 80, 64, 32)), 2),                          # a width off the granule
+])
+def test_chain_create_rejects(kw, status):
+    st, h = _chain(**kw)
+    assert st == status
+    assert h.value is None
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), dict(mfma="32x32x16", dims="128x128x128x128x64", remap="relabel")),
+    (dict(dtype=1, widths=(64, 96, 128, 32, 128, 64, 128), flags=2 << 4),
+     dict(mfma="32x32x16", dims="64x96x128x32x128x64x128", remap="permlane")),
+    (dict(dtype=1, widths=(64, 96, 160, 32, 224, 64, 128)),
+     dict(mfma="32x32x16", dims="64x96x160x32x224x64x128", remap="relabel")),
+    # up to three GEMMs the chain call plans what b2b_gemm_create plans
+    (dict(widths=(128, 128, 128)), dict(mfma="16x16x32", remap="relabel", mt="1")),
+    (dict(widths=(128, 128, 128, 64)), dict(mfma="16x16x32", remap="relabel")),
+    (dict(widths=(128, 128)), dict(mfma="16x16x32", dims="128x128")),   # one GEMM
+])
+def test_chain_plan_selection(kw, expect):
+    info = _chain_info(**kw)
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
+
+
+def test_gemm_run_rejects_chain_plans():
+    st, h = _chain()
+    assert st == 0
+    a = ctypes.c_void_p(0x1000)
+    assert cf.lib().b2b_gemm_run(h, a, a, a, a, ctypes.c_void_p(0x2000), None) == 1
+    ptrs = (ctypes.c_void_p * 4)(0x1000, 0x1000, None, 0x1000)
+    assert cf.lib().b2b_chain_run(h, a, ptrs, ctypes.c_void_p(0x2000), None) == 1   # a NULL weight
+    cf.lib().b2b_gemm_destroy(h)
