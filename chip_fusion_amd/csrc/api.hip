@@ -68,7 +68,7 @@ b2b::Shape shape_of(int dt) {
 
 const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, int orn, int km0) {
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.shape32 || d.dtype != dt || d.nst != nst || d.orn != orn) continue;
+        if (d.rtw || d.dtype != dt || d.nst != nst || d.orn != orn) continue;
         if (nst > 1 && d.mode != mode) continue;
         if (km0 >= 0 && d.km0 != km0) continue;
         bool ok = true;
@@ -78,22 +78,22 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
     return nullptr;
 }
 
-// Run-time-width kernel (32x32x16) for widths dims[0..nst]: the smallest
-// width bound that holds them all, or null when a granule, a bound or LDS
-// rules the cascade out.
+// Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
+// 16x16x4 for fp64): the smallest width bound that holds them all, or null
+// when a granule, a bound or LDS rules the cascade out.
 const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode) {
-    if (dt == B2B_DTYPE_F64) return nullptr;
-    if (dims[0] % 32) return nullptr;
+    const bool f64 = dt == B2B_DTYPE_F64;
+    if (dims[0] % (f64 ? 8 : 32)) return nullptr;
     int64_t need = dims[0], lds = 0;
     for (int i = 1; i <= nst; ++i) {
-        if (dims[i] % 32) return nullptr;
+        if (dims[i] % (f64 ? 16 : 32)) return nullptr;
         need = dims[i] > need ? dims[i] : need;
     }
-    for (int i = 0; i < nst; ++i) lds += dims[i] * dims[i + 1] * 2;
+    for (int i = 0; i < nst; ++i) lds += dims[i] * dims[i + 1] * elt_size(dt);
     if (lds > 160 * 1024) return nullptr;
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!d.shape32 || d.dtype != dt || d.nst != nst || (nst > 1 && d.mode != mode)) continue;
+        if (!d.rtw || d.dtype != dt || d.nst != nst || (nst > 1 && d.mode != mode)) continue;
         if (d.maxd < need) continue;
         if (!best || d.maxd < best->maxd) best = &d;
     }

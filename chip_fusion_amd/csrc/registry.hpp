@@ -7,13 +7,15 @@
 #include "kernels.hpp"
 #include "kernels_cs.hpp"
 #include "kernels_gen.hpp"
+#include "kernels_gen64.hpp"
 
 namespace b2b {
 
 struct KernelDesc {
     int dtype, nst, dims[4], mode, orn, km0;
     int mt, waves, threads, rows_wg, lds_bytes;
-    int shape32 = 0;  // 1: 32x32x16 instruction, widths at run time up to maxd (dims are 0)
+    int shape32 = 0;  // 1: 32x32x16 instruction
+    int rtw = 0;      // 1: widths read at run time, up to maxd (dims are 0)
     int maxd = 0;
     const void* fn;   // the __global__ function, for occupancy queries
     // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
@@ -92,6 +94,7 @@ KernelDesc describe_gen() {
     d.rows_wg = C::ROWS_WG;
     d.lds_bytes = 0;
     d.shape32 = 1;
+    d.rtw = 1;
     d.maxd = C::MAXD;
     d.fn = (const void*)&b2bk::gen_kernel<C>;
     d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST); };
@@ -102,6 +105,36 @@ KernelDesc describe_gen() {
         if (attr != hipSuccess) return attr;
         const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST);
         hipLaunchKernelGGL(b2bk::gen_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+// fp64 instances with run-time widths.
+template <class C>
+KernelDesc describe_gen64() {
+    KernelDesc d;
+    d.dtype = C::DT;
+    d.nst = C::NST;
+    for (int& x : d.dims) x = 0;   // never matched by width
+    d.mode = C::NST > 1 ? C::MODE : 0;
+    d.orn = 0;
+    d.km0 = b2bk::KM_PAIR64;
+    d.mt = 1;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::ROWS_WG;
+    d.lds_bytes = 0;
+    d.rtw = 1;
+    d.maxd = C::MAXD;
+    d.fn = (const void*)&b2bk::gen64_kernel<C>;
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen64_lds_bytes(w, C::NST); };
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void*)&b2bk::gen64_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
+        if (attr != hipSuccess) return attr;
+        const size_t shm = (size_t)b2bk::gen64_lds_bytes(a.dims, C::NST);
+        hipLaunchKernelGGL(b2bk::gen64_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };
     return d;
@@ -172,6 +205,10 @@ ProbeDesc describe_probe() {
 #define B2B_GEN_INSTANCE(...)                                                          \
     static ::b2b::Registrar B2B_CAT(b2b_gen_reg_, __LINE__)(                           \
         ::b2b::describe_gen<::b2bk::GenCfg<__VA_ARGS__>>())
+// B2B_GEN64_INSTANCE(stages, max width, A tiles ahead, tiles per group)
+#define B2B_GEN64_INSTANCE(...)                                                        \
+    static ::b2b::Registrar B2B_CAT(b2b_gen64_reg_, __LINE__)(                         \
+        ::b2b::describe_gen64<::b2bk::Gen64Cfg<__VA_ARGS__>>())
 #define B2B_INSTANCE(...)                                                              \
     static ::b2b::Registrar B2B_CAT(b2b_reg_, __LINE__)(                               \
         ::b2b::describe<::b2bk::Cfg<__VA_ARGS__>>())

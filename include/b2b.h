@@ -71,7 +71,11 @@ enum {
                                       160 KB; the unfused path's per GEMM).  Rearrangement
                                       REMAP_RELABEL (the default) or REMAP_PERMLANE (a swap of
                                       32-lane halves).  Without this flag these kernels serve
-                                      fp16/bf16 cascades that no fixed-width kernel covers. */
+                                      fp16/bf16 cascades that no fixed-width kernel covers; fp64
+                                      cascades no fixed-width kernel covers go to fp64 kernels
+                                      with run-time widths (v_mfma_f64_16x16x4; K a multiple of
+                                      8, N1..N3 of 16, each at most 128, weights at most 160 KB;
+                                      the layouts coincide, nothing moves). */
     B2B_REMAP_AUTO = 0u << 4,      /* the library picks the rearrangement */
     B2B_REMAP_BPERMUTE = 1u << 4,  /* coordination-matrix rounds: one ds_bpermute per round */
     B2B_REMAP_PERMLANE = 2u << 4,  /* fixed lane-row swaps (v_permlane16/32_swap) */
@@ -97,10 +101,10 @@ typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
  *   flags         B2B_FLAG_* | B2B_REMAP_*
  * Returns INVALID_VALUE for non-positive sizes, ld below the row width, ld
  * not a multiple of 16 bytes, or unknown flags; NOT_SUPPORTED for cascades no
- * kernel covers: fp64 widths other than the compiled ones (64), fp16/bf16 widths
- * that break the granules or bounds of B2B_FLAG_MFMA_32X32 (and have no
- * fixed-width kernel), or weights beyond LDS (then the caller may retry with
- * B2B_FLAG_UNFUSED, whose per-GEMM kernels need only one matrix in LDS).
+ * kernel covers: widths that break the granules or bounds of the run-time-width
+ * kernels (see B2B_FLAG_MFMA_32X32) and have no fixed-width kernel, or weights
+ * beyond LDS (then the caller may retry with B2B_FLAG_UNFUSED, whose per-GEMM
+ * kernels need only one matrix in LDS).
  */
 b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
                              int64_t K, int64_t N1, int64_t N2, int64_t N3,
@@ -128,10 +132,10 @@ b2b_status_t b2b_gemm_run(b2b_gemm_t plan, const void* A, const void* B0, const 
  *                 dense; 0 for a B_s broadcasts it
  *   flags         as for b2b_gemm_create
  * Up to three GEMMs this plans exactly what b2b_gemm_create plans.  Longer
- * fused cascades run on the 32x32x16 run-time-width kernels (fp16/bf16; K and
- * the widths multiples of 32, each at most 256, all weights together at most
- * 160 KB); the unfused path takes any such cascade whose single GEMMs are
- * covered.  Errors as for b2b_gemm_create; INVALID_VALUE also for nst outside
+ * fused cascades run on the run-time-width kernels (fp16/bf16 up to six GEMMs,
+ * K and the widths multiples of 32, each at most 256; fp64 up to five, each at
+ * most 64; all weights together at most 160 KB); the unfused path takes any
+ * cascade whose single GEMMs are covered.  Errors as for b2b_gemm_create; INVALID_VALUE also for nst outside
  * 1..8 or a NULL widths.
  */
 b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M, int32_t nst,

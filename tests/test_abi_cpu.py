@@ -51,7 +51,8 @@ def _create(**kw):
     (dict(K=96, N1=80, N2=96), 2),            # N1 off the 32-column granule
     (dict(K=80, N1=64, N2=64), 2),            # K off the 32-column granule
     (dict(K=96, N1=96, N2=288), 2),           # a width above 256
-    (dict(dtype=2, K=96, N1=96, N2=96), 2),   # fp64: fixed widths only
+    (dict(dtype=2, K=96, N1=96, N2=160), 2),  # fp64: widths above 128
+    (dict(dtype=2, K=92, N1=96, N2=96), 2),   # fp64: K off the 8-column granule
     (dict(K=256, N1=256, N2=256, flags=4), 2),         # 32x32 path: 256 KB of weights
     (dict(dtype=2, flags=4), 2),                       # 32x32 path: 16-bit types only
     (dict(flags=4 | (1 << 4)), 2),                     # 32x32 path: no coordination rounds
@@ -88,6 +89,9 @@ def _info(**kw):
     (dict(K=96, N1=160, N2=64), dict(path="fused", mfma="32x32x16", remap="relabel", lds_bytes=str(51200 + 32768))),
     (dict(dtype=1, K=32, N1=32, N2=256, N3=32), dict(mfma="32x32x16", dims="32x32x256x32")),
     (dict(K=96, N1=160, N2=64, flags=2 << 4), dict(mfma="32x32x16", remap="permlane")),
+    # fp64 widths no fixed-width kernel covers: run-time widths on 16x16x4
+    (dict(dtype=2, K=96, N1=48, N2=112), dict(mfma="f64_16x16x4", remap="relabel", rows_per_wg="128")),
+    (dict(dtype=2, K=8, N1=128, N2=16, N3=64), dict(mfma="f64_16x16x4", dims="8x128x16x64")),
     # the configurations' widths keep their fixed-width kernels unless asked
     (dict(), dict(mfma="16x16x32", remap="relabel")),
     (dict(flags=4), dict(mfma="32x32x16", remap="relabel", lds_bytes=str(16384 + 32768))),
@@ -183,7 +187,7 @@ def _chain_info(**kw):
     (dict(nst=9, widths=(64,) * 10), 1),
     (dict(widths=None, nst=2), 1),
     (dict(widths=(128, 0, 128)), 1),
-    (dict(dtype=2, widths=(64, 64, 64, 64, 64)), 2),                 # fp64: up to three GEMMs
+    (dict(dtype=2, widths=(64,) * 7), 2),                             # fp64: up to five GEMMs
     (dict(widths=(128,) * 7), 2),                                     # 192 KB of weights
     (dict(widths=(128, 128, 128, 128, 64), flags=2 | (3 << 4)), 2),   # orientation N beyond three
     (dict(widths=(128, 96, 80, 64, 32)), 2),                          # a width off the granule
@@ -204,6 +208,7 @@ def test_chain_create_rejects(kw, status):
     (dict(widths=(128, 128, 128)), dict(mfma="16x16x32", remap="relabel", mt="1")),
     (dict(widths=(128, 128, 128, 64)), dict(mfma="16x16x32", remap="relabel")),
     (dict(widths=(128, 128)), dict(mfma="16x16x32", dims="128x128")),   # one GEMM
+    (dict(dtype=2, widths=(64, 48, 64, 32, 64)), dict(mfma="f64_16x16x4", dims="64x48x64x32x64")),
 ])
 def test_chain_plan_selection(kw, expect):
     info = _chain_info(**kw)
