@@ -45,6 +45,8 @@ def main():
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--mfma32", action="store_true",
                     help="kernels on the 32x32x16 instruction with run-time widths")
+    ap.add_argument("--tune", action="store_true",
+                    help="let the library time its candidate kernels on the first buffer set and keep the fastest")
     ap.add_argument("--dims", default=None,
                     help="comma-separated widths K,N1,N2[,N3] replacing the workload's (same batch, M, "
                          "distribution and seed)")
@@ -111,6 +113,9 @@ def main():
         plan = cf.Chain(dt, c["batch"], c["M"], dims, remap=args.remap, unfused=args.unfused,
                         mfma32=args.mfma32)
     stream = torch.cuda.current_stream()
+    if args.tune:
+        plan.tune(sets, reps=2 * R, stream=stream)
+        print(f"[bench] tuned: {plan.info()}", file=sys.stderr, flush=True)
 
     def step(i):
         Ad, Bd, D = sets[i % R]
@@ -192,7 +197,7 @@ def main():
         tr = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
         ent = tr["configs"].get(str(args.config))
         if (ent and tr["source_digest"] == _b.source_digest() and not args.unfused
-                and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims):
+                and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims and not args.tune):
             roof["traffic"] = ent["hbm_bytes"]
             roof["traffic_unit"] = "bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f)" % (
                 tr["fetch_scale"], tr["write_scale"])

@@ -22,8 +22,8 @@ SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x
           "f16_16x16x16": 4, "f64_16x16x4": 5}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
           4: "out of memory"}
-EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_run", "b2b_gemm_destroy",
-           "b2b_status_string",
+EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_run", "b2b_gemm_tune",
+           "b2b_gemm_destroy", "b2b_status_string",
            "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_probe",
            "b2b_mfma_probe")
 
@@ -51,6 +51,8 @@ def lib():
         L.b2b_chain_create.argtypes = [ctypes.POINTER(vp), i32, i64, i64, ctypes.c_int32, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
         L.b2b_chain_run.argtypes = [vp, vp, ctypes.POINTER(vp), vp, vp]
+        L.b2b_gemm_tune.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(vp), vp, ctypes.c_int32]
         L.b2b_gemm_destroy.argtypes = [vp]
         L.b2b_status_string.argtypes = [i32]
         L.b2b_status_string.restype = ctypes.c_char_p
@@ -104,6 +106,20 @@ class Plan:
                                 _stream_ptr(stream))
         _check(st, "b2b_gemm_run")
         return D
+
+    def tune(self, sets, reps=10, stream=None):
+        """Keeps the fastest compiled kernel for this cascade (b2b_gemm_tune),
+        timed over `sets`, a list of (A, [B_0, ..], D) representative of the
+        use; every D holds the kept kernel's result afterwards."""
+        nst = len(self.dims) - 1
+        for _, Bs, _ in sets:
+            if len(Bs) != nst:
+                raise ValueError(f"{nst} weight matrices expected, got {len(Bs)}")
+        n = len(sets)
+        As = (ctypes.c_void_p * n)(*[a.data_ptr() for a, _, _ in sets])
+        Bp = (ctypes.c_void_p * (n * nst))(*[b.data_ptr() for _, Bs, _ in sets for b in Bs])
+        Ds = (ctypes.c_void_p * n)(*[d.data_ptr() for _, _, d in sets])
+        _check(lib().b2b_gemm_tune(self._h, n, As, Bp, Ds, _stream_ptr(stream), reps), "b2b_gemm_tune")
 
     def info(self):
         buf = ctypes.create_string_buffer(512)

@@ -8,12 +8,14 @@
 // and run() is the third: it only enqueues the fused kernel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "b2b.h"
 #include "plan.hpp"
@@ -81,20 +83,21 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
 // Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
 // 16x16x4 for fp64): the smallest width bound that holds them all, or null
 // when a granule, a bound or LDS rules the cascade out.
-const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode) {
+bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims) {
+    if (!d.rtw || d.dtype != dt || d.nst != nst) return false;
     const bool f64 = dt == B2B_DTYPE_F64;
-    if (dims[0] % (f64 ? 8 : 32)) return nullptr;
-    int64_t need = dims[0], lds = 0;
-    for (int i = 1; i <= nst; ++i) {
-        if (dims[i] % (f64 ? 16 : 32)) return nullptr;
-        need = dims[i] > need ? dims[i] : need;
-    }
+    if (dims[0] % (f64 ? 8 : 32) || dims[0] > d.maxd) return false;
+    int64_t lds = 0;
+    for (int i = 1; i <= nst; ++i)
+        if (dims[i] % (f64 ? 16 : 32) || dims[i] > d.maxd) return false;
     for (int i = 0; i < nst; ++i) lds += dims[i] * dims[i + 1] * elt_size(dt);
-    if (lds > 160 * 1024) return nullptr;
+    return lds <= 160 * 1024;
+}
+
+const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!d.rtw || d.dtype != dt || d.nst != nst || (nst > 1 && d.mode != mode)) continue;
-        if (d.maxd < need) continue;
+        if (!gen_fits(d, dt, nst, dims) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd) best = &d;
     }
     return best;
@@ -409,6 +412,115 @@ b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {
     }
     delete p;
     return st;
+}
+
+b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, const void* const* B,
+                           void* const* D, void* stream, int32_t reps) {
+    if (!p || nsets < 1 || !A || !B || !D || reps < 1 || reps > 10000) return B2B_ERROR_INVALID_VALUE;
+    if (p->unfused) return B2B_ERROR_NOT_SUPPORTED;
+    const bool any_mode = (p->flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO;
+    const bool s32 = (p->flags & B2B_FLAG_MFMA_32X32) != 0;
+    // every compiled kernel that computes this cascade under the plan's flags
+    std::vector<const KernelDesc*> cands;
+    for (const KernelDesc& d : b2b::registry()) {
+        if (d.dtype != p->dtype || d.nst != p->nst) continue;
+        if (d.rtw) {
+            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims)) continue;
+        } else {
+            if (s32 || d.orn != p->orn) continue;
+            bool ok = true;
+            for (int i = 0; i <= p->nst; ++i) ok = ok && d.dims[i] == p->dims[i];
+            if (!ok) continue;
+        }
+        if (s32 && !d.shape32) continue;
+        const int m = p->nst > 1 ? d.mode : p->mode;
+        if (!any_mode && p->nst > 1 && m != p->mode) continue;
+        cands.push_back(&d);
+    }
+    if (cands.empty()) return B2B_ERROR_NOT_SUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return B2B_ERROR_HIP;
+    }
+    const KernelDesc* keep = p->fused;
+    const int keep_mode = p->mode;
+    auto run_set = [&](int i) { return run_impl(p, A[i], B + (size_t)i * p->nst, D[i], stream); };
+    // candidates run interleaved over three rounds; in each, one untimed run,
+    // then reps runs back to back over the buffer sets in turn (sets larger
+    // than the 256 MB Infinity Cache make them cold, as a stream of distinct
+    // batches is); the score is the median round
+    const int rounds = 3;
+    std::vector<float> times(cands.size() * rounds, 0.f);
+    std::vector<char> usable(cands.size(), 1);
+    b2b_status_t rc = B2B_SUCCESS;
+    for (int r = 0; r < rounds && rc == B2B_SUCCESS; ++r)
+        for (size_t i = 0; i < cands.size() && rc == B2B_SUCCESS; ++i) {
+            if (!usable[i]) continue;
+            const KernelDesc* k = cands[i];
+            const int mode = p->nst > 1 ? k->mode : keep_mode;
+            if (mode == b2bk::MODE_BPERM &&
+                (!make_sched(p->dtype, p->orn != 0, p->sched[0]) || !make_sched(p->dtype, false, p->sched[1]))) {
+                usable[i] = 0;
+                continue;
+            }
+            p->fused = k;
+            p->mode = mode;
+            {
+                std::lock_guard<std::mutex> lock(p->grid_mu);
+                p->grid[0] = 0;   // this kernel's own grid
+            }
+            rc = run_set(nsets - 1);   // untimed; validates the arguments
+            float ms = 0.f;
+            if (rc == B2B_SUCCESS) {
+                if (hipEventRecord(e0, st) != hipSuccess) rc = B2B_ERROR_HIP;
+                for (int q = 0; q < reps && rc == B2B_SUCCESS; ++q) rc = run_set(q % nsets);
+                if (rc == B2B_SUCCESS &&
+                    (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                     hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                    rc = B2B_ERROR_HIP;
+            }
+            times[i * rounds + r] = ms;
+        }
+    const KernelDesc* best = nullptr;
+    int best_mode = 0;
+    float best_ms = 0.f, keep_ms = -1.f;
+    for (size_t i = 0; i < cands.size() && rc == B2B_SUCCESS; ++i) {
+        if (!usable[i]) continue;
+        float* t = &times[i * rounds];
+        std::sort(t, t + rounds);
+        const float ms = t[rounds / 2];
+        const int mode = p->nst > 1 ? cands[i]->mode : keep_mode;
+        if (cands[i] == keep && mode == keep_mode) keep_ms = ms;
+        if (!best || ms < best_ms) {
+            best = cands[i];
+            best_mode = mode;
+            best_ms = ms;
+        }
+    }
+    // the planned kernel stays unless another is clearly (3 %) faster
+    if (best && keep_ms >= 0.f && best_ms > 0.97f * keep_ms) {
+        best = keep;
+        best_mode = keep_mode;
+    }
+    if (!best) rc = B2B_ERROR_NOT_SUPPORTED;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    p->fused = rc == B2B_SUCCESS ? best : keep;
+    p->mode = rc == B2B_SUCCESS ? best_mode : keep_mode;
+    if (p->mode == b2bk::MODE_BPERM &&
+        (!make_sched(p->dtype, p->orn != 0, p->sched[0]) || !make_sched(p->dtype, false, p->sched[1])))
+        return B2B_ERROR_NOT_SUPPORTED;
+    {
+        std::lock_guard<std::mutex> lock(p->grid_mu);
+        p->grid[0] = 0;
+    }
+    if (rc != B2B_SUCCESS) return rc;
+    // leave every D as the kept kernel computes it
+    for (int i = 0; i < nsets && rc == B2B_SUCCESS; ++i) rc = run_set(i);
+    if (rc == B2B_SUCCESS && hipStreamSynchronize(st) != hipSuccess) rc = B2B_ERROR_HIP;
+    return rc;
 }
 
 b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {

@@ -153,6 +153,25 @@ b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);
 /* Static description of a status code. */
 const char* b2b_status_string(b2b_status_t s);
 
+/*
+ * Picks, for this plan, the fastest of the compiled kernels that compute its
+ * cascade (both instruction shapes and every rearrangement when the plan was
+ * made with B2B_REMAP_AUTO; only the requested ones otherwise).  The caller
+ * hands in nsets buffer sets, representative of its use: A[i], the nst
+ * weight pointers B[i * nst .. i * nst + nst - 1] and D[i].  In three
+ * interleaved rounds every candidate runs once untimed and then `reps` times
+ * back to back over the sets in turn (timed with events on `stream`); the
+ * median round scores it.  Sets larger together than the 256 MB Infinity
+ * Cache time cold HBM traffic, as a stream of distinct batches sees it; a
+ * single small set times warm caches.  The planned kernel stays unless
+ * another scores at least 3 % faster.  Every D holds the kept kernel's result
+ * when the call returns (the call synchronises the stream).  Not for unfused
+ * plans (NOT_SUPPORTED).  It changes the plan: no other call may use the plan
+ * meanwhile.  reps: 1..10000.
+ */
+b2b_status_t b2b_gemm_tune(b2b_gemm_t plan, int32_t nsets, const void* const* A, const void* const* B,
+                           void* const* D, void* stream, int32_t reps);
+
 /* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
    remap mode, tile, grid, LDS and workspace bytes, kernel launches per run)
    into buf (NUL-terminated). */

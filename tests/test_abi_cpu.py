@@ -224,3 +224,17 @@ def test_gemm_run_rejects_chain_plans():
     ptrs = (ctypes.c_void_p * 4)(0x1000, 0x1000, None, 0x1000)
     assert cf.lib().b2b_chain_run(h, a, ptrs, ctypes.c_void_p(0x2000), None) == 1   # a NULL weight
     cf.lib().b2b_gemm_destroy(h)
+
+
+def test_tune_rejects_bad_arguments():
+    st, h = _create()
+    assert st == 0
+    L = cf.lib()
+    As = (ctypes.c_void_p * 1)(0x1000)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    Ds = (ctypes.c_void_p * 1)(0x2000)
+    assert L.b2b_gemm_tune(None, 1, As, ptrs, Ds, None, 5) == 1
+    assert L.b2b_gemm_tune(h, 1, As, None, Ds, None, 5) == 1
+    assert L.b2b_gemm_tune(h, 0, As, ptrs, Ds, None, 5) == 1
+    assert L.b2b_gemm_tune(h, 1, As, ptrs, Ds, None, 0) == 1
+    L.b2b_gemm_destroy(h)
