@@ -24,7 +24,8 @@ STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime 
           4: "out of memory"}
 EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_run", "b2b_gemm_tune",
            "b2b_gemm_destroy", "b2b_status_string",
-           "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_probe",
+           "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_compile",
+           "b2b_remap_execute", "b2b_remap_probe",
            "b2b_mfma_probe")
 
 
@@ -60,6 +61,8 @@ def lib():
         L.b2b_remap_relation.argtypes = [i32, i32, vp, i64, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
         L.b2b_remap_schedule.argtypes = [i32, i32, i32, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int32)]
         L.b2b_remap_probe.argtypes = [i32, i32, u32, vp, vp, vp]
+        L.b2b_remap_compile.argtypes = [i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]
+        L.b2b_remap_execute.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
         L.b2b_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
         for n in EXPORTS:
             if n not in ("b2b_status_string",):
@@ -192,6 +195,32 @@ def remap_schedule(shape, orient_n=False, packed=False):
     _check(lib().b2b_remap_schedule(sh, int(orient_n), int(packed), p.ctypes.data, q.ctypes.data,
                                     r.ctypes.data, n, ctypes.byref(rounds)), "b2b_remap_schedule")
     return p.reshape(-1, 64), q.reshape(-1, 64), r.reshape(-1, 64)
+
+
+def remap_compile(src, dst):
+    """Relation and coordination rounds between two layouts given as labels
+    [64 * E] (b2b_remap_compile); returns rel, p, q, r ([E, 64] each for p, q, r)."""
+    src = np.ascontiguousarray(src, np.int32)
+    dst = np.ascontiguousarray(dst, np.int32)
+    if src.size != dst.size or src.size % 64:
+        raise ValueError("layouts must hold 64 * E labels each")
+    E = src.size // 64
+    rel = np.empty(src.size, np.int32)
+    p, q, r = (np.empty(src.size, np.int32) for _ in range(3))
+    rounds = ctypes.c_int32()
+    _check(lib().b2b_remap_compile(E, src.ctypes.data, dst.ctypes.data, rel.ctypes.data, p.ctypes.data,
+                                   q.ctypes.data, r.ctypes.data, ctypes.byref(rounds)), "b2b_remap_compile")
+    return rel, p.reshape(E, 64), q.reshape(E, 64), r.reshape(E, 64)
+
+
+def remap_execute(p, q, r, payload, stream=None):
+    """Runs compiled rounds on a device int32/uint32 tensor [64 * E] (b2b_remap_execute)."""
+    p, q, r = (np.ascontiguousarray(x, np.int32).reshape(-1) for x in (p, q, r))
+    E = p.size // 64
+    out = torch.empty_like(payload)
+    _check(lib().b2b_remap_execute(E, E, p.ctypes.data, q.ctypes.data, r.ctypes.data, _ptr(payload), _ptr(out),
+                                   _stream_ptr(stream)), "b2b_remap_execute")
+    return out
 
 
 def remap_probe(shape, mode, inp, orient_n=False, stream=None):

@@ -590,6 +590,56 @@ b2b_status_t b2b_remap_schedule(b2b_shape_t shape, int orient_n, int packed, int
     return B2B_SUCCESS;
 }
 
+b2b_status_t b2b_remap_compile(int32_t elems, const int32_t* src, const int32_t* dst, int32_t* rel, int32_t* p,
+                               int32_t* q, int32_t* r, int32_t* rounds) {
+    if (elems < 1 || elems > b2bk::kExecMax || !src || !dst) return B2B_ERROR_INVALID_VALUE;
+    b2b::Relation relation;
+    if (!b2b::build_relation_from_labels(elems, src, dst, &relation)) return B2B_ERROR_INVALID_VALUE;
+    b2b::Schedule s;
+    if (!b2b::build_schedule(relation, &s) || !b2b::check_schedule(relation, s)) return B2B_ERROR_NOT_SUPPORTED;
+    if (rounds) *rounds = s.rounds;
+    const int n = 64 * elems;
+    for (int i = 0; i < n; ++i) {
+        if (rel) rel[i] = relation.src_of[i];
+        if (p) p[i] = s.p[i];
+        if (q) q[i] = s.q[i];
+        if (r) r[i] = s.r[i];
+    }
+    return B2B_SUCCESS;
+}
+
+b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, const int32_t* q, const int32_t* r,
+                               const uint32_t* in, uint32_t* out, void* stream) {
+    if (elems < 1 || elems > b2bk::kExecMax || rounds != elems || !p || !q || !r || !in || !out)
+        return B2B_ERROR_INVALID_VALUE;
+    b2bk::ExecArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.elems = elems;
+    a.rounds = rounds;
+    // receiver tables -> one code per (round, lane); the sender's element comes
+    // from the receiver that asks it.  Each round must ask every lane once and
+    // each receiver must fill every slot once.
+    std::vector<int> filled(64 * elems, 0);
+    for (int j = 0; j < rounds; ++j) {
+        int give[64];
+        bool asked[64] = {};
+        for (int i = 0; i < 64; ++i) {
+            const int k = j * 64 + i, pi = p[k], qi = q[k], ri = r[k];
+            if (pi < 0 || pi > 63 || qi < 0 || qi >= elems || ri < 0 || ri >= elems || asked[pi])
+                return B2B_ERROR_INVALID_VALUE;
+            asked[pi] = true;
+            give[pi] = qi;
+            if (filled[i * elems + ri]++) return B2B_ERROR_INVALID_VALUE;
+        }
+        for (int i = 0; i < 64; ++i) {
+            const int k = j * 64 + i;
+            a.code[j][i] = (uint16_t)(p[k] | (give[i] << 6) | (r[k] << 10));
+        }
+    }
+    hipLaunchKernelGGL(b2bk::remap_exec_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, in, out, a);
+    return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+}
+
 b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, const void* in, void* out,
                              void* stream) {
     int dt;

@@ -1054,6 +1054,42 @@ __global__ __launch_bounds__(C::THREADS) void fused_kernel(KArgs args) {
 
 
 // ---------------------------------------------------------------------------
+// Executor of compiled coordination rounds (any relation of 64 x E 32-bit
+// elements, E <= 16): in round j every lane offers one of its elements and
+// takes one from the lane its code names, into the slot its code names --
+// one ds_bpermute per round.  code[j][lane] = p | give << 6 | r << 10.
+// ---------------------------------------------------------------------------
+constexpr int kExecMax = 16;
+struct ExecArgs {
+    int32_t elems, rounds;
+    uint16_t code[kExecMax][64];
+};
+
+template <int MAXE = kExecMax>
+__global__ __launch_bounds__(64) void remap_exec_kernel(const uint32_t* in, uint32_t* out, ExecArgs args) {
+    const int lane = threadIdx.x, E = args.elems;
+    unsigned x[MAXE], y[MAXE];
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        x[e] = e < E ? in[lane * E + e] : 0u;
+        y[e] = 0u;
+    }
+    for (int j = 0; j < args.rounds; ++j) {
+        const unsigned c = args.code[j][lane];
+        const int src = c & 63, give = (c >> 6) & 15, slot = (c >> 10) & 15;
+        unsigned v = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) v = e == give ? x[e] : v;   // selects, no indexing
+        const unsigned got = (unsigned)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) y[e] = e == slot ? got : y[e];
+    }
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e)
+        if (e < E) out[lane * E + e] = y[e];
+}
+
+// ---------------------------------------------------------------------------
 // Probe: one remap unit on index payloads, through the same executors.
 // in/out: 64 lanes x E elements (uint16 for 16-bit types, uint64 for fp64).
 // ---------------------------------------------------------------------------

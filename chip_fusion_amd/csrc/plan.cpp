@@ -94,6 +94,26 @@ bool build_relation(Shape s, bool orient_n, Relation* out) {
     return true;
 }
 
+bool build_relation_from_labels(int elems, const int32_t* src, const int32_t* dst, Relation* out) {
+    if (elems < 1 || !src || !dst) return false;
+    const int n = kLanes * elems;
+    std::map<int32_t, int> where;
+    for (int i = 0; i < n; ++i)
+        if (!where.emplace(src[i], i).second) return false;   // a label twice in the source
+    out->elems = elems;
+    out->tiles = 0;
+    out->ksteps = 0;
+    out->src_of.assign(n, -1);
+    std::vector<char> used(n, 0);
+    for (int d = 0; d < n; ++d) {
+        auto it = where.find(dst[d]);
+        if (it == where.end() || used[it->second]) return false;   // missing or taken twice
+        used[it->second] = 1;
+        out->src_of[d] = it->second;
+    }
+    return true;
+}
+
 bool pack_relation(const Relation& r, Relation* packed) {
     if (r.elems % 2) return false;
     const int E = r.elems, P = E / 2;

@@ -54,6 +54,12 @@ struct Relation {
 // orient_n = false: first GEMM computed transposed (lanes hold rows of C0).
 bool build_relation(Shape s, bool orient_n, Relation* out);
 
+// The relation between any two layouts of the same 64*elems elements, each
+// given as a label per (lane, element) (index lane*elems + e): src_of[d] = the
+// source index holding the label of destination index d.  False unless both
+// hold the same labels, each once.
+bool build_relation_from_labels(int elems, const int32_t* src, const int32_t* dst, Relation* out);
+
 // Pairs of 16-bit elements moved as one 32-bit value; false when the relation
 // splits a pair.
 bool pack_relation(const Relation& r, Relation* packed);

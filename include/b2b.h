@@ -220,6 +220,33 @@ b2b_status_t b2b_remap_schedule(b2b_shape_t shape, int orient_n, int packed, int
                                 int32_t* q, int32_t* r, int64_t cap, int32_t* rounds);
 
 /*
+ * Remap compiler (page 1's general method, for any pair of layouts): the
+ * relation and the coordination rounds between two layouts of the same
+ * 64*E elements, each layout given as one label per (lane, element), index
+ * l*E + e (any int32 labels, e.g. row*width + column of the element).
+ *   elems      E, 1..16
+ *   src, dst   64*E labels each
+ *   rel        out or NULL: 64*E entries, rel[d] = source index feeding d
+ *   p, q, r    out or NULL: 64*E entries each, round-major as in
+ *              b2b_remap_schedule (sender lane, sender element, own slot)
+ *   rounds     out or NULL: E
+ * INVALID_VALUE unless both layouts hold the same 64*E distinct labels.
+ * Host-only, no GPU needed.
+ */
+b2b_status_t b2b_remap_compile(int32_t elems, const int32_t* src, const int32_t* dst, int32_t* rel, int32_t* p,
+                               int32_t* q, int32_t* r, int32_t* rounds);
+
+/*
+ * Executes coordination rounds (host tables p, q, r as b2b_remap_compile
+ * writes them) on one wave: 64*E 32-bit elements `in` (device, index l*E + e)
+ * are rearranged into `out` (device), one ds_bpermute per round.
+ * INVALID_VALUE unless rounds == elems (1..16), every round asks each lane
+ * once and every lane fills each of its slots once.
+ */
+b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, const int32_t* q, const int32_t* r,
+                               const uint32_t* in, uint32_t* out, void* stream);
+
+/*
  * Runs one device rearrangement executor on index payloads and writes what
  * it produced (a probe of the exchange kernels, used by the parity tests).
  *   in   device, 64*E source elements (uint16 for 16-bit shapes, uint64 for
