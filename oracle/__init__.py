@@ -41,6 +41,8 @@ def _load():
         lib.oracle_cascade.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, i64, vp, vp, vp, i64,
                                        vp, ctypes.c_int]
         lib.oracle_cascade.restype = ctypes.c_int
+        lib.oracle_cascade_typed.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, vp, vp, i64, vp, ctypes.c_int]
+        lib.oracle_cascade_typed.restype = ctypes.c_int
         for n in ("oracle_encode_f16_array", "oracle_encode_bf16_array",
                   "oracle_decode_f16_array", "oracle_decode_bf16_array"):
             getattr(lib, n).argtypes = [vp, vp, i64]
@@ -134,8 +136,18 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
     16-bit inputs/outputs are uint16 encodings, fp64 is float64.
     rows: optional flat row ids (b*M + m); then the result is [len(rows), N_last]
     in that order, else [batch, M, N_last] (or [M, N_last] for 2-D A).
+    dtype may also be a list of len(Bs) + 1 16-bit types, one per stage: A and
+    B_s in types[s], the result of GEMM s rounded into types[s + 1], D in the last.
     """
-    dt = dtype_code(dtype)
+    if isinstance(dtype, (list, tuple)):
+        types = [dtype_code(t) for t in dtype]
+        if len(types) != len(Bs) + 1 or any(t == F64 for t in types):
+            raise ValueError("one 16-bit type per GEMM and one for D")
+        if len(set(types)) == 1:
+            return cascade(types[0], A, Bs, rows, nthreads)
+    else:
+        types = None
+    dt = dtype_code(dtype) if types is None else types[0]
     A = _as_input(dt, A)
     squeeze = A.ndim == 2
     if squeeze:
@@ -156,9 +168,15 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
     out = np.empty((nrows, dims[-1]), np.float64 if dt == F64 else np.uint16)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
-    rc = _load().oracle_cascade(dt, len(Bs), _ptr(dims_a), batch, M, _ptr(A), bptrs,
-                                _ptr(rows) if rows is not None else None, nrows, _ptr(out),
-                                int(nthreads))
+    if types is None:
+        rc = _load().oracle_cascade(dt, len(Bs), _ptr(dims_a), batch, M, _ptr(A), bptrs,
+                                    _ptr(rows) if rows is not None else None, nrows, _ptr(out),
+                                    int(nthreads))
+    else:
+        ta = np.array(types, np.int32)
+        rc = _load().oracle_cascade_typed(_ptr(ta), len(Bs), _ptr(dims_a), batch, M, _ptr(A), bptrs,
+                                          _ptr(rows) if rows is not None else None, nrows, _ptr(out),
+                                          int(nthreads))
     if rc:
         raise ValueError(f"oracle_cascade failed ({rc})")
     if rows is not None:

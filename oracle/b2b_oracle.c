@@ -10,7 +10,10 @@
  * description, the cascaded-GEMM definition and the three-operator cascade):
  * a cascade of S = 2 or 3 GEMMs with nothing between them,
  *     X_0 = A,   X_{s+1} = rnd(X_s . B_s),   D = X_S,
- * evaluated independently for every batch and every row.  The pages fuse the
+ * evaluated independently for every batch and every row.  With a type per
+ * stage (oracle_cascade_typed; the pages let each fused operator have its own
+ * data type and layout), GEMM s takes X_s and B_s in type t_s and its result is
+ * rounded into t_{s+1}, the next GEMM's operand type (t_S is D's type).  The pages fuse the
  * cascade so that the intermediate never leaves the chip; the value of the
  * cascade itself is the plain matrix product written out here.
  *
@@ -176,6 +179,7 @@ int oracle_gemm_acc(int dtype, int64_t M, int64_t K, int64_t N,
 
 typedef struct {
     int dtype, nst;
+    int st[OR_MAX_STAGES + 1];          /* 16-bit type of X_s and B_s; st[nst]: D */
     int64_t batch, M, dims[OR_MAX_STAGES + 1];
     const void* A;
     const float* Bf[OR_MAX_STAGES];     /* decoded weights (16-bit inputs) */
@@ -219,7 +223,7 @@ static void* cascade_worker(void* arg)
         } else {
             const uint16_t* a = (const uint16_t*)j->A + (b * j->M + m) * K0;
             float* x = (float*)xin;
-            for (int64_t k = 0; k < K0; ++k) x[k] = dec16(j->dtype, a[k]);
+            for (int64_t k = 0; k < K0; ++k) x[k] = dec16(j->st[0], a[k]);
             uint16_t* drow = (uint16_t*)j->D + i * j->dims[j->nst];
             for (int s = 0; s < j->nst; ++s) {
                 int64_t K = j->dims[s], N = j->dims[s + 1];
@@ -230,12 +234,13 @@ static void* cascade_worker(void* arg)
                     float av = x[k];
                     for (int64_t n = 0; n < N; ++n) y[n] = y[n] + av * w[k * N + n];
                 }
-                /* round the stage result to the input type: this is exactly
-                   what the next stage consumes, and what D holds at the end */
+                /* round the stage result to the next stage's type: this is
+                   exactly what the next stage consumes, and what D holds at
+                   the end */
                 for (int64_t n = 0; n < N; ++n) {
-                    uint16_t h = enc16(j->dtype, y[n]);
+                    uint16_t h = enc16(j->st[s + 1], y[n]);
                     if (s + 1 == j->nst) drow[n] = h;
-                    else y[n] = dec16(j->dtype, h);
+                    else y[n] = dec16(j->st[s + 1], h);
                 }
                 void* t = xin; xin = xout; xout = t; x = (float*)xin;
             }
@@ -245,12 +250,14 @@ static void* cascade_worker(void* arg)
     return NULL;
 }
 
-int oracle_cascade(int dtype, int nstages, const int64_t* dims, int64_t batch, int64_t M,
-                   const void* A, const void* const* B, const int64_t* rows, int64_t nrows,
-                   void* D_out, int nthreads)
+static int cascade_run(int dtype, const int* types, int nstages, const int64_t* dims, int64_t batch,
+                       int64_t M, const void* A, const void* const* B, const int64_t* rows,
+                       int64_t nrows, void* D_out, int nthreads)
 {
     if (nstages < 1 || nstages > OR_MAX_STAGES || batch < 0 || M < 0 || nrows < 0) return 1;
     if (dtype != OR_F16 && dtype != OR_BF16 && dtype != OR_F64) return 2;
+    for (int s = 0; s <= nstages; ++s)
+        if (types && types[s] != OR_F16 && types[s] != OR_BF16) return 2;
     for (int s = 0; s <= nstages; ++s) if (dims[s] <= 0) return 1;
     if (!rows) nrows = batch * M;
     if (nrows == 0) return 0;
@@ -263,6 +270,7 @@ int oracle_cascade(int dtype, int nstages, const int64_t* dims, int64_t batch, i
     memset(&base, 0, sizeof base);
     base.dtype = dtype; base.nst = nstages; base.batch = batch; base.M = M;
     for (int s = 0; s <= nstages; ++s) base.dims[s] = dims[s];
+    for (int s = 0; s <= nstages; ++s) base.st[s] = types ? types[s] : dtype;
     base.A = A; base.rows = rows; base.D = D_out;
     float* dec[OR_MAX_STAGES] = {0};
     int rc = 0;
@@ -271,7 +279,7 @@ int oracle_cascade(int dtype, int nstages, const int64_t* dims, int64_t batch, i
         int64_t n = batch * dims[s] * dims[s + 1];
         dec[s] = (float*)malloc((size_t)n * sizeof(float));
         if (!dec[s]) { rc = 3; goto done; }
-        for (int64_t i = 0; i < n; ++i) dec[s][i] = dec16(dtype, ((const uint16_t*)B[s])[i]);
+        for (int64_t i = 0; i < n; ++i) dec[s][i] = dec16(base.st[s], ((const uint16_t*)B[s])[i]);
         base.Bf[s] = dec[s];
     }
     {
@@ -297,4 +305,21 @@ int oracle_cascade(int dtype, int nstages, const int64_t* dims, int64_t batch, i
 done:
     for (int s = 0; s < nstages; ++s) free(dec[s]);
     return rc;
+}
+
+int oracle_cascade(int dtype, int nstages, const int64_t* dims, int64_t batch, int64_t M,
+                   const void* A, const void* const* B, const int64_t* rows, int64_t nrows,
+                   void* D_out, int nthreads)
+{
+    return cascade_run(dtype, NULL, nstages, dims, batch, M, A, B, rows, nrows, D_out, nthreads);
+}
+
+/* types[0..nstages]: OR_F16 or OR_BF16 each; A in types[0], B_s in types[s],
+   the result of GEMM s rounded into types[s + 1]; D in types[nstages] */
+int oracle_cascade_typed(const int* types, int nstages, const int64_t* dims, int64_t batch, int64_t M,
+                         const void* A, const void* const* B, const int64_t* rows, int64_t nrows,
+                         void* D_out, int nthreads)
+{
+    if (!types) return 2;
+    return cascade_run(types[0], types, nstages, dims, batch, M, A, B, rows, nrows, D_out, nthreads);
 }

@@ -252,6 +252,51 @@ def test_intermediate_rounding_exact(dtype, lims, dims):
     assert np.array_equal(oracle.decode(dtype, D).astype(np.float64), want)
 
 
+@pytest.mark.parametrize("types,lims,dims", [(("f16", "bf16", "f16"), [6, 6, 6], [32, 32, 32]),
+                                             (("bf16", "f16", "bf16"), [12, 12, 1], [64, 16, 16]),
+                                             (("f16", "bf16", "f16", "bf16"), [3, 3, 3, 2], [32, 32, 16, 16]),
+                                             (("bf16", "bf16", "f16", "f16"), [3, 3, 2, 1], [32, 32, 16, 4])])
+def test_typed_intermediate_rounding_exact(types, lims, dims):
+    """A type per stage: integer inputs whose intermediates exceed the exact
+    integer range of the type they are rounded into (256 for bf16, 2048 for
+    fp16).  The oracle must equal the exact int64 stage rounded by the library
+    cast of that stage's type (numpy for binary16, torch for bfloat16), and
+    must differ from the same inputs read as one uniform type."""
+    rng = np.random.default_rng(17)
+    A = synth.to_dtype(rng.integers(0, lims[0] + 1, (40, dims[0])), types[0])
+    Bs = [synth.to_dtype(rng.integers(0, lims[s + 1] + 1, (dims[s], dims[s + 1])), types[s])
+          for s in range(len(dims) - 1)]
+    D = oracle.cascade(list(types), A, Bs)
+    x = oracle.decode(types[0], A).astype(np.int64)
+    rounded = False
+    for s, B in enumerate(Bs):
+        y = x @ oracle.decode(types[s], B).astype(np.int64)
+        assert np.abs(y).max() < 2 ** 24
+        limit = 2048 if types[s + 1] == "f16" else 256
+        rounded |= bool(s + 1 < len(Bs) and np.abs(y).max() > limit)
+        x = _np_round(types[s + 1], y).astype(np.int64)
+    assert rounded
+    got = oracle.decode(types[-1], D).astype(np.float64)
+    assert np.array_equal(got, x.astype(np.float64))
+
+
+def test_typed_rounding_points():
+    """fp16 values through identity weights into a bf16 intermediate and back
+    to fp16: 1 + 2^-8 is a tie between bf16 neighbours 1 and 1 + 2^-7 (-> 1,
+    even), 1 + 3*2^-9 goes up to 1 + 2^-7, 1.5 and 2^-14 are exact in both;
+    the bf16 results are exact in fp16 again.  With the intermediate in fp16
+    instead, every value comes through unchanged."""
+    vals = np.array([[1 + 2 ** -8, 1 + 3 * 2 ** -9, 1.5, 2.0 ** -14]], np.float32)
+    A = oracle.encode("f16", vals)
+    I16 = oracle.encode("f16", np.eye(4, dtype=np.float32))
+    Ib = oracle.encode("bf16", np.eye(4, dtype=np.float32))
+    D = oracle.cascade(["f16", "bf16", "f16"], A, [I16, Ib])
+    assert oracle.decode("f16", D).tolist() == [[1.0, 1 + 2 ** -7, 1.5, 2.0 ** -14]]
+    D2 = oracle.cascade(["f16", "f16", "bf16"], A, [I16, I16])
+    assert oracle.decode("bf16", D2).tolist() == [[1.0, 1 + 2 ** -7, 1.5, 2.0 ** -14]]
+    assert np.array_equal(oracle.cascade(["f16", "f16", "f16"], A, [I16, I16]), A)
+
+
 # ----------------------------------------------------------------------------
 # Closed forms and invariants
 # ----------------------------------------------------------------------------
