@@ -50,6 +50,9 @@ def main():
     ap.add_argument("--dims", default=None,
                     help="comma-separated widths K,N1,N2[,N3] replacing the workload's (same batch, M, "
                          "distribution and seed)")
+    ap.add_argument("--types", default=None,
+                    help="comma-separated 16-bit type per GEMM and one for D (e.g. f16,bf16,f16): "
+                         "a cascade with a type per stage on the workload's shape")
     ap.add_argument("--rotate-bytes", type=float, default=1 << 30)
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="keep warming up (untimed) until this much GPU time has passed, so the "
@@ -90,23 +93,33 @@ def main():
         c["name"] = (f"{c['dtype']} b{c['batch']} {c['M']}x{c['dims'][0]} . "
                      + " . ".join(f"{c['dims'][s]}x{c['dims'][s + 1]}" for s in range(len(c["dims"]) - 1)))
     dt = c["dtype"]
+    types = args.types.split(",") if args.types else None
+    if types:
+        if len(types) != len(c["dims"]) or any(t not in ("f16", "bf16") for t in types) or dt == "f64":
+            print("--types takes one of f16/bf16 per GEMM and one for D on a 16-bit workload", file=sys.stderr)
+            sys.exit(2)
+        c["name"] += " types " + "/".join(types)
     flop, algo_bytes = workload_numbers(c)
     print(f"[bench] config {args.config}: {c['name']}; generating inputs", file=sys.stderr, flush=True)
-    A, Bs = synth.make_inputs(c)
+    A, Bs = synth.make_inputs(c, types=types)
+    st_types = types or [dt] * len(c["dims"])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[dt]
     R = max(1, min(64, int(np.ceil(args.rotate_bytes / set_bytes))))
-    A0 = cf.to_device(A, dt)
-    B0 = [cf.to_device(b, dt) for b in Bs]
+    A0 = cf.to_device(A, st_types[0])
+    B0 = [cf.to_device(b, st_types[s]) for s, b in enumerate(Bs)]
     sets = []
     for r in range(R):
         Ad = A0 if r == 0 else A0.clone()
         Bd = B0 if r == 0 else [b.clone() for b in B0]
-        D = torch.empty((c["batch"], c["M"], c["dims"][-1]), dtype=A0.dtype, device=dev)
+        D = torch.empty((c["batch"], c["M"], c["dims"][-1]), dtype=cf.TORCH_DTYPES[cf.DTYPES[st_types[-1]]],
+                        device=dev)
         sets.append((Ad, Bd, D))
     dims = c["dims"]
-    if len(dims) <= 4:
+    if types:
+        plan = cf.Chain(types, c["batch"], c["M"], dims, remap=args.remap, unfused=args.unfused)
+    elif len(dims) <= 4:
         plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
                        remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32)
     else:   # longer cascades: the chain entry points
@@ -197,7 +210,8 @@ def main():
         tr = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
         ent = tr["configs"].get(str(args.config))
         if (ent and tr["source_digest"] == _b.source_digest() and not args.unfused
-                and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims and not args.tune):
+                and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims
+                and not args.tune and not types):
             roof["traffic"] = ent["hbm_bytes"]
             roof["traffic_unit"] = "bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f)" % (
                 tr["fetch_scale"], tr["write_scale"])
@@ -212,8 +226,10 @@ def main():
     import oracle
     rows = np.linspace(0, c["batch"] * c["M"] - 1, 64).astype(np.int64)
     got = cf.to_host(sets[(args.steps - 1) % R][2]).reshape(-1, dims[-1])[rows]
-    ref = oracle.cascade(dt, A, Bs, rows=rows)
-    g, rf = oracle.decode(dt, got).astype(np.float64), oracle.decode(dt, ref).astype(np.float64)
+    otype = types if types else dt
+    ref = oracle.cascade(otype, A, Bs, rows=rows)
+    g, rf = (oracle.decode(st_types[-1], got).astype(np.float64),
+             oracle.decode(st_types[-1], ref).astype(np.float64))
     sample_err = float(np.linalg.norm(g - rf) / np.linalg.norm(rf))
 
     cpu = None
@@ -222,12 +238,12 @@ def main():
         per_row = flop / (c["batch"] * c["M"])
         n = 2048
         t0 = time.perf_counter()
-        oracle.cascade(dt, A, Bs, rows=np.arange(n, dtype=np.int64), nthreads=nthreads)
+        oracle.cascade(otype, A, Bs, rows=np.arange(n, dtype=np.int64), nthreads=nthreads)
         dt1 = time.perf_counter() - t0
         n2 = int(min(c["batch"] * c["M"], max(n, n * args.cpu_seconds / max(dt1, 1e-6))))
         idx = np.linspace(0, c["batch"] * c["M"] - 1, n2).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.cascade(dt, A, Bs, rows=idx, nthreads=nthreads)
+        oracle.cascade(otype, A, Bs, rows=idx, nthreads=nthreads)
         el = time.perf_counter() - t0
         cpu = {"value": n2 * per_row / el / 1e12, "unit": "TFLOP/s", "cores": nthreads,
                "kind": "oracle", "seconds": el,
@@ -245,7 +261,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": "/".join(types) if types else dt,
         "data": "synthetic",
         "pct_of_mfma_peak": 100.0 * value * 1e12 / PEAK[dt],
         "config": {"workload": c["name"], "batch": c["batch"], "M": c["M"], "dims": dims,

@@ -22,7 +22,7 @@ SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x
           "f16_16x16x16": 4, "f64_16x16x4": 5}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
           4: "out of memory"}
-EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_run", "b2b_gemm_tune",
+EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_create_typed", "b2b_chain_run", "b2b_gemm_tune",
            "b2b_gemm_destroy", "b2b_status_string",
            "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_compile",
            "b2b_remap_execute", "b2b_remap_probe",
@@ -52,6 +52,9 @@ def lib():
         L.b2b_chain_create.argtypes = [ctypes.POINTER(vp), i32, i64, i64, ctypes.c_int32, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
         L.b2b_chain_run.argtypes = [vp, vp, ctypes.POINTER(vp), vp, vp]
+        L.b2b_chain_create_typed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), i64, i64, ctypes.c_int32,
+                                             ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
+        L.b2b_chain_create_typed.restype = i32
         L.b2b_gemm_tune.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     ctypes.POINTER(vp), vp, ctypes.c_int32]
         L.b2b_gemm_destroy.argtypes = [vp]
@@ -143,28 +146,41 @@ class Plan:
 
 class Chain(Plan):
     """A planned cascade of any number of GEMMs (b2b_chain_create):
-    D = rnd(...rnd(A.B_0)...B_{n-1}) with widths [K, N_1, ..., N_n]."""
+    D = rnd(...rnd(A.B_0)...B_{n-1}) with widths [K, N_1, ..., N_n].
+    dtype may be a list of len(widths) types, one per GEMM and the last for D
+    (b2b_chain_create_typed)."""
 
     def __init__(self, dtype, batch, M, widths, ld=None, batch_stride=None, remap="auto",
                  unfused=False, mfma32=False):
-        self.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        code = lambda t: DTYPES[t] if isinstance(t, str) else int(t)
+        typed = isinstance(dtype, (list, tuple))
+        self.dtypes = [code(t) for t in dtype] if typed else None
+        self.dtype = self.dtypes[0] if typed else code(dtype)
         self.batch, self.M, self.dims = batch, M, list(widths)
         nst = len(self.dims) - 1
         flags = ((REMAP[remap] << 4) | (FLAG_UNFUSED if unfused else 0) | (FLAG_MFMA_32X32 if mfma32 else 0))
         w = (ctypes.c_int64 * (nst + 1))(*self.dims)
         arr = ctypes.c_int64 * (nst + 2)
         h = ctypes.c_void_p()
-        st = lib().b2b_chain_create(ctypes.byref(h), self.dtype, batch, M, nst, w,
-                                    arr(*ld) if ld is not None else None,
-                                    arr(*batch_stride) if batch_stride is not None else None, flags)
-        _check(st, "b2b_chain_create")
+        lds = arr(*ld) if ld is not None else None
+        bss = arr(*batch_stride) if batch_stride is not None else None
+        if typed:
+            if len(self.dtypes) != nst + 1:
+                raise ValueError(f"{nst + 1} types expected (one per GEMM and D), got {len(self.dtypes)}")
+            ts = (ctypes.c_int32 * (nst + 1))(*self.dtypes)
+            st = lib().b2b_chain_create_typed(ctypes.byref(h), ts, batch, M, nst, w, lds, bss, flags)
+            _check(st, "b2b_chain_create_typed")
+        else:
+            st = lib().b2b_chain_create(ctypes.byref(h), self.dtype, batch, M, nst, w, lds, bss, flags)
+            _check(st, "b2b_chain_create")
         self._h = h
 
     def run(self, A, *Bs, D=None, stream=None):
         if len(Bs) != len(self.dims) - 1:
             raise ValueError(f"{len(self.dims) - 1} weight matrices expected, got {len(Bs)}")
         if D is None:
-            D = torch.empty((self.batch, self.M, self.dims[-1]), dtype=A.dtype, device=A.device)
+            dt = TORCH_DTYPES[self.dtypes[-1]] if self.dtypes else A.dtype
+            D = torch.empty((self.batch, self.M, self.dims[-1]), dtype=dt, device=A.device)
         ptrs = (ctypes.c_void_p * len(Bs))(*[b.data_ptr() for b in Bs])
         st = lib().b2b_chain_run(self._h, _ptr(A), ptrs, _ptr(D), _stream_ptr(stream))
         _check(st, "b2b_chain_run")

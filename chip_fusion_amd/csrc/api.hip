@@ -44,6 +44,7 @@ constexpr int kMaxSt = b2bk::kMaxStages;
 
 struct b2b_gemm_plan {
     int dtype = 0, nst = 0, mode = 0, orn = 0;
+    int tm = -1;                                 // type per stage (bit s: bf16), or -1: dtype throughout
     int64_t batch = 0, M = 0, dims[kMaxSt + 1] = {};
     // leading dimensions and batch strides (elements): [0] A, [1 + s] B_s, [nst + 1] D
     int64_t ld[kMaxSt + 2] = {}, bs[kMaxSt + 2] = {};
@@ -83,8 +84,8 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
 // Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
 // 16x16x4 for fp64): the smallest width bound that holds them all, or null
 // when a granule, a bound or LDS rules the cascade out.
-bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims) {
-    if (!d.rtw || d.dtype != dt || d.nst != nst) return false;
+bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1) {
+    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm) return false;
     const bool f64 = dt == B2B_DTYPE_F64;
     if (dims[0] % (f64 ? 8 : 32) || dims[0] > d.maxd) return false;
     int64_t lds = 0;
@@ -94,10 +95,10 @@ bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims) {
     return lds <= 160 * 1024;
 }
 
-const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode) {
+const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!gen_fits(d, dt, nst, dims) || (nst > 1 && d.mode != mode)) continue;
+        if (!gen_fits(d, dt, nst, dims, tm) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd) best = &d;
     }
     return best;
@@ -210,8 +211,10 @@ namespace {
 // Validates and plans a cascade of nst GEMMs with widths d[0..nst]; L and S hold
 // nst + 2 leading dimensions and batch strides ([0] A, [1 + s] B_s, [nst + 1] D)
 // or are null (dense).
+// tm >= 0: a 16-bit type per stage (bit s set: GEMM s in bf16; bit nst: D), dt
+// the type of bit 0; the cascade then runs on the 32x32x16 kernels.
 b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
-                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain) {
+                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1) {
     if (!plan) return B2B_ERROR_INVALID_VALUE;
     *plan = nullptr;
     if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
@@ -226,7 +229,10 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     if (mode > b2bk::MODE_RELABEL) return B2B_ERROR_INVALID_VALUE;
     const int orn = (flags & B2B_FLAG_ORIENT_N) ? 1 : 0;
     if (orn && mode != b2bk::MODE_BPERM && mode != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
-    const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0;
+    const bool typed = tm >= 0;
+    if (typed && (orn || (mode != b2bk::MODE_RELABEL && (flags & B2B_REMAP_MASK) != B2B_REMAP_AUTO)))
+        return B2B_ERROR_NOT_SUPPORTED;   // typed cascades are relabelled on the 32x32x16 kernels
+    const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0 || typed;
     if (s32 && (orn || dt == B2B_DTYPE_F64)) return B2B_ERROR_NOT_SUPPORTED;
     // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
     const int mode32 = (flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO ? b2bk::MODE_RELABEL : mode;
@@ -251,6 +257,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     b2b_gemm_plan* p = new (std::nothrow) b2b_gemm_plan();
     if (!p) return B2B_ERROR_OUT_OF_MEMORY;
     p->dtype = dt;
+    p->tm = tm;
     p->nst = nst;
     p->mode = mode;
     p->orn = orn;
@@ -267,7 +274,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         if (s32 || nst > 3) {
             // the fixed-width kernels cover up to three GEMMs
             if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
-            p->fused = find_gen(dt, nst, dims, mode32);
+            p->fused = find_gen(dt, nst, dims, mode32, tm);
             p->mode = mode32;
         } else if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
             // the cheapest rearrangement compiled for this shape
@@ -297,8 +304,12 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         for (int s = 0; s < nst; ++s) {
             const int64_t d2[4] = {dims[s], dims[s + 1], 0, 0};
             const int km0 = (s == 0 && dt == B2B_DTYPE_F64) ? b2bk::KM_PAIR64 : b2bk::KM_NAT;
-            p->stage_k[s] = s32 ? nullptr : find_kernel(dt, 1, d2, 0, 0, km0);
-            if (!p->stage_k[s]) p->stage_k[s] = find_gen(dt, 1, d2, 0);
+            // stage s alone: its own type in, the next stage's type out
+            const int sub = typed ? (tm >> s) & 3 : 0;
+            const int sdt = typed ? ((sub & 1) ? B2B_DTYPE_BF16 : B2B_DTYPE_F16) : dt;
+            const int stm = (sub == 1 || sub == 2) ? sub : -1;
+            p->stage_k[s] = (s32 || stm >= 0) ? nullptr : find_kernel(sdt, 1, d2, 0, 0, km0);
+            if (!p->stage_k[s]) p->stage_k[s] = find_gen(sdt, 1, d2, 0, stm);
             if (!p->stage_k[s]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         }
         for (int s = 0; s + 1 < nst; ++s) {
@@ -387,6 +398,26 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
     return create_impl(plan, (int)dtype, batch, M, nst, widths, ld, batch_stride, flags, true);
 }
 
+b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes, int64_t batch, int64_t M,
+                                    int32_t nst, const int64_t* widths, const int64_t* ld,
+                                    const int64_t* batch_stride, uint32_t flags) {
+    if (plan) *plan = nullptr;
+    if (!widths || !dtypes || nst < 1 || nst > kMaxSt) return B2B_ERROR_INVALID_VALUE;
+    bool same = true;
+    int tm = 0;
+    for (int s = 0; s <= nst; ++s) {
+        if (dtypes[s] != B2B_DTYPE_F16 && dtypes[s] != B2B_DTYPE_BF16 && dtypes[s] != B2B_DTYPE_F64)
+            return B2B_ERROR_NOT_SUPPORTED;
+        same = same && dtypes[s] == dtypes[0];
+        if (dtypes[s] == B2B_DTYPE_BF16) tm |= 1 << s;
+    }
+    // one type throughout: exactly the plan of b2b_chain_create
+    if (same) return create_impl(plan, (int)dtypes[0], batch, M, nst, widths, ld, batch_stride, flags, true);
+    for (int s = 0; s <= nst; ++s)
+        if (dtypes[s] == B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
+    return create_impl(plan, (int)dtypes[0], batch, M, nst, widths, ld, batch_stride, flags, true, tm);
+}
+
 b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const void* B1,
                           const void* B2, void* D, void* stream) {
     if (!p || p->nst < 2 || p->nst > 3) return B2B_ERROR_INVALID_VALUE;
@@ -423,9 +454,9 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
     // every compiled kernel that computes this cascade under the plan's flags
     std::vector<const KernelDesc*> cands;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.dtype != p->dtype || d.nst != p->nst) continue;
+        if (d.dtype != p->dtype || d.nst != p->nst || d.tm != p->tm) continue;
         if (d.rtw) {
-            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims)) continue;
+            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims, p->tm)) continue;
         } else {
             if (s32 || d.orn != p->orn) continue;
             bool ok = true;
@@ -537,12 +568,18 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
         for (int i = 0; i <= k->nst; ++i) d32[i] = (int32_t)p->dims[i];
         lds_bytes = (int)k->dyn_lds(d32);
     }
+    std::string dts_s = dts[p->dtype];
+    if (p->tm >= 0) {
+        // a type per stage: GEMM 0's, GEMM 1's, ..., then D's
+        dts_s.clear();
+        for (int s = 0; s <= p->nst; ++s) dts_s += std::string(s ? "/" : "") + dts[(p->tm >> s) & 1];
+    }
     std::string dims = std::to_string(p->dims[0]);
     for (int i = 1; i <= p->nst; ++i) dims += "x" + std::to_string(p->dims[i]);
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
                   "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d",
-                  p->unfused ? "unfused" : "fused", dts[p->dtype], (long long)p->batch,
+                  p->unfused ? "unfused" : "fused", dts_s.c_str(), (long long)p->batch,
                   (long long)p->M, dims.c_str(), mfma,
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, lds_bytes, p->grid[0],

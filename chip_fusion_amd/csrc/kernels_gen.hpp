@@ -25,6 +25,11 @@
 // column per lane).  Each wave owns 32 rows of a 256-row tile;
 // D is regrouped with the same lane-half swap into 8 consecutive columns per
 // lane and stored as 16-byte pieces of rows.
+//
+// A cascade may give each GEMM its own 16-bit type (GenCfg's type mask):
+// the fp16 and bf16 instructions share every register layout, so a stage
+// changes only the instruction it issues and the type its result is rounded
+// into.
 #pragma once
 #include "kernels.hpp"
 
@@ -49,16 +54,22 @@ template <> struct Ty32<DT_BF16> {
 // NST_: GEMMs in the cascade (1 is a single GEMM, for the unfused path; up
 // to kMaxStages, the weights of all of them in LDS);
 // MAXD_: bound on every width; MODE_: MODE_RELABEL or MODE_PERMLANE;
-// PF_: A tiles fetched ahead (0 or 1, registers permitting).
-template <int DT_, int NST_, int MAXD_, int MODE_, int PF_>
+// PF_: A tiles fetched ahead (0 or 1, registers permitting);
+// TM_: -1, every operand, intermediate and D in DT_; else a type per stage
+// (page 1 lets each fused operator have its own data type): bit s set means
+// bf16, clear fp16, for the operands of GEMM s (A, B_s and the intermediate
+// rounded for it) and, at bit NST, for D.  DT_ is then the type of bit 0.
+template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1>
 struct GenCfg {
-    static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_;
+    static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_, TM = TM_;
+    static constexpr int stype(int s) { return TM < 0 ? DT : (((TM >> s) & 1) ? DT_BF16 : DT_F16); }
     static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
     static constexpr int LDS_MAX = 160 * 1024;
     static_assert(DT != DT_F64, "the 32x32x16 instruction exists for 16-bit types");
     static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= kMaxStages && (PF == 0 || PF == 1), "config");
     static_assert(MODE == MODE_RELABEL || MODE == MODE_PERMLANE, "rearrangement");
+    static_assert(TM < 0 || (TM < (2 << NST) && stype(0) == DT), "type mask");
 };
 
 // One weight matrix in LDS: `rows` x `n` 16-bit values in blocks of 32
@@ -188,10 +199,10 @@ __device__ __forceinline__ void gen_arrange_a(u4_t (&a)[C::MKS]) {
         }
 }
 
-// Result tile -> two K-steps of the next GEMM's operand (rounded to the type).
-template <class C>
+// Result tile -> two K-steps of the next GEMM's operand (rounded to its type NDT).
+template <class C, int NDT>
 __device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t& o1) {
-    using T = Ty<C::DT>;
+    using T = Ty<NDT>;
     unsigned p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
@@ -213,7 +224,7 @@ __device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t
 // columns per lane: n0 + 8h.. and n0 + 16 + 8h.. of row l%32.
 template <class C>
 __device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t& hi) {
-    using T = Ty<C::DT>;
+    using T = Ty<C::stype(C::NST)>;
     unsigned p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
@@ -269,7 +280,8 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
 // core busy while either waits for its previous product.  With an odd tile
 // count the last pair computes its tile twice and drops the copy (a branch
 // per pair, not per product).  sink(t, acc_t, acc_t+1, two) takes each pair.
-template <class C, class Sink>
+// SDT: the GEMM's operand type.
+template <class C, int SDT, class Sink>
 __device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag& fr, const u4_t (&x)[C::MKS],
                                          int ks, int nt, Sink&& sink) {
 #pragma unroll
@@ -281,8 +293,8 @@ __device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag
 #pragma unroll
             for (int j = 0; j < C::MKS; ++j)
                 if (j < ks) {
-                    acc0 = Ty32<C::DT>::mma(gen_wfrag(lds, fr, t, j), x[j], acc0);
-                    acc1 = Ty32<C::DT>::mma(gen_wfrag(lds, fr, t1, j), x[j], acc1);
+                    acc0 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t, j), x[j], acc0);
+                    acc1 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t1, j), x[j], acc1);
                 }
             sink(t, acc0, acc1, two);
         }
@@ -357,25 +369,31 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
             gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
         };
         if constexpr (C::NST == 1) {
-            gen_gemm<C>(lds, fr[0], a, ks0, dn / 32, to_d);
+            gen_gemm<C, C::stype(0)>(lds, fr[0], a, ks0, dn / 32, to_d);
         } else {
-            // the operands of stage s come from oA (s odd) or oB (s even, s > 0)
+            // the operands of stage s come from oA (s odd) or oB (s even, s > 0),
+            // rounded into stage s's type
             u4_t oA[C::MKS], oB[C::MKS];
-            auto to_ops = [&](u4_t (&o)[C::MKS]) __attribute__((always_inline)) {
+            auto to_ops = [&](u4_t (&o)[C::MKS], auto nt) __attribute__((always_inline)) {
+                constexpr int NDT = decltype(nt)::value;
                 return [&o](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
-                    gen_to_operand<C>(a0, o[2 * tt], o[2 * tt + 1]);
-                    if (two) gen_to_operand<C>(a1, o[2 * tt + 2], o[2 * tt + 3]);
+                    gen_to_operand<C, NDT>(a0, o[2 * tt], o[2 * tt + 1]);
+                    if (two) gen_to_operand<C, NDT>(a1, o[2 * tt + 2], o[2 * tt + 3]);
                 };
             };
-            gen_gemm<C>(lds, fr[0], a, ks0, d[1] / 32, to_ops(oA));
+            using T1 = std::integral_constant<int, C::stype(1)>;
+            gen_gemm<C, C::stype(0)>(lds, fr[0], a, ks0, d[1] / 32, to_ops(oA, T1{}));
             gen_static_for<1, C::NST - 1>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int S = decltype(sc)::value;
-                if constexpr (S % 2 == 1) gen_gemm<C>(lds, fr[S], oA, d[S] / 16, d[S + 1] / 32, to_ops(oB));
-                else gen_gemm<C>(lds, fr[S], oB, d[S] / 16, d[S + 1] / 32, to_ops(oA));
+                using TN = std::integral_constant<int, C::stype(S + 1)>;
+                if constexpr (S % 2 == 1)
+                    gen_gemm<C, C::stype(S)>(lds, fr[S], oA, d[S] / 16, d[S + 1] / 32, to_ops(oB, TN{}));
+                else
+                    gen_gemm<C, C::stype(S)>(lds, fr[S], oB, d[S] / 16, d[S + 1] / 32, to_ops(oA, TN{}));
             });
             constexpr int L = C::NST - 1;
-            if constexpr (L % 2 == 1) gen_gemm<C>(lds, fr[L], oA, d[L] / 16, dn / 32, to_d);
-            else gen_gemm<C>(lds, fr[L], oB, d[L] / 16, dn / 32, to_d);
+            if constexpr (L % 2 == 1) gen_gemm<C, C::stype(L)>(lds, fr[L], oA, d[L] / 16, dn / 32, to_d);
+            else gen_gemm<C, C::stype(L)>(lds, fr[L], oB, d[L] / 16, dn / 32, to_d);
         }
     };
 

@@ -17,6 +17,7 @@ struct KernelDesc {
     int shape32 = 0;  // 1: 32x32x16 instruction
     int rtw = 0;      // 1: widths read at run time, up to maxd (dims are 0)
     int maxd = 0;
+    int tm = -1;      // type per stage (bit s: bf16 operands of GEMM s, bit nst: D), or -1: all dtype
     const void* fn;   // the __global__ function, for occupancy queries
     // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
     int64_t (*dyn_lds)(const int32_t* d) = nullptr;
@@ -96,6 +97,7 @@ KernelDesc describe_gen() {
     d.shape32 = 1;
     d.rtw = 1;
     d.maxd = C::MAXD;
+    d.tm = C::TM;
     d.fn = (const void*)&b2bk::gen_kernel<C>;
     d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST); };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
@@ -205,6 +207,9 @@ ProbeDesc describe_probe() {
 #define B2B_GEN_INSTANCE(...)                                                          \
     static ::b2b::Registrar B2B_CAT(b2b_gen_reg_, __LINE__)(                           \
         ::b2b::describe_gen<::b2bk::GenCfg<__VA_ARGS__>>())
+// B2B_GEN_TYPED(stages, max width, A tiles ahead, type mask): relabelled, a type per stage
+#define B2B_GEN_TYPED(NST, MAXD, PF, TM)                                                \
+    B2B_GEN_INSTANCE(((TM) & 1) ? ::b2bk::DT_BF16 : ::b2bk::DT_F16, NST, MAXD, ::b2bk::MODE_RELABEL, PF, TM)
 // B2B_GEN64_INSTANCE(stages, max width, A tiles ahead, tiles per group)
 #define B2B_GEN64_INSTANCE(...)                                                        \
     static ::b2b::Registrar B2B_CAT(b2b_gen64_reg_, __LINE__)(                         \

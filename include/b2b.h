@@ -142,6 +142,29 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
                               const int64_t* widths, const int64_t* ld, const int64_t* batch_stride,
                               uint32_t flags);
 
+/*
+ * A cascade with a 16-bit type per stage (page 1: each fused operator may
+ * have its own data type, and the rearrangement relation follows the type):
+ * GEMM s multiplies X_s by B_s in dtypes[s] with fp32 accumulation, and its
+ * result is rounded to nearest-even into dtypes[s + 1], the next GEMM's
+ * operand type; D is in dtypes[nst].
+ *   dtypes        nst + 1 types: A and B_0 in dtypes[0], B_s in dtypes[s],
+ *                 D in dtypes[nst]; B2B_DTYPE_F16 or B2B_DTYPE_BF16 (the
+ *                 same type throughout, fp64 included, plans exactly what
+ *                 b2b_chain_create plans)
+ *   other arguments as for b2b_chain_create
+ * Mixed types run relabelled on the 32x32x16 run-time-width kernels: fused
+ * for two GEMMs (widths up to 256) and three (up to 128), and unfused for any
+ * length (each GEMM then changes type on its way out).  NOT_SUPPORTED for fp64
+ * mixed with a 16-bit type, B2B_FLAG_ORIENT_N, a rearrangement other than
+ * RELABEL or AUTO, or widths those kernels do not cover; otherwise errors as
+ * for b2b_chain_create.  Runs with b2b_chain_run (or b2b_gemm_run for two or
+ * three GEMMs).
+ */
+b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes, int64_t batch, int64_t M,
+                                    int32_t nst, const int64_t* widths, const int64_t* ld,
+                                    const int64_t* batch_stride, uint32_t flags);
+
 /* Enqueues a cascade planned by either create call; B holds its nst weight
  * pointers (device, 16-byte aligned, none equal to D).  Same asynchrony and
  * errors as b2b_gemm_run. */

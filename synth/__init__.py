@@ -157,12 +157,13 @@ def tensor(seed, tensor_id, shape, dtype, dist, scale=1.0):
     return to_dtype(v, dtype).reshape(shape)
 
 
-def make_inputs(cfg, M=None, batch=None, dist=None, seed=None):
+def make_inputs(cfg, M=None, batch=None, dist=None, seed=None, types=None):
     """Inputs of a workload: returns (A, [B0, B1, (B2)]).
 
     cfg: a CONFIGS key or dict.  M / batch / dist / seed override the
     workload's values (smaller sizes for the parity tests, 'ternary' for the
-    exactness variants).
+    exactness variants).  types: one 16-bit type per GEMM (A and B_0 in
+    types[0], B_s in types[s]) instead of the workload's single type.
     """
     c = dict(CONFIGS[cfg]) if isinstance(cfg, int) else dict(cfg)
     M = c["M"] if M is None else M
@@ -171,7 +172,8 @@ def make_inputs(cfg, M=None, batch=None, dist=None, seed=None):
     seed = c["seed"] if seed is None else seed
     scale = c["scale"] if dist != "ternary" else 1.0
     dims = c["dims"]
-    A = tensor(seed, 0, (batch, M, dims[0]), c["dtype"], dist, scale)
-    Bs = [tensor(seed, 1 + s, (batch, dims[s], dims[s + 1]), c["dtype"], dist, scale)
+    ty = types if types is not None else [c["dtype"]] * len(dims)
+    A = tensor(seed, 0, (batch, M, dims[0]), ty[0], dist, scale)
+    Bs = [tensor(seed, 1 + s, (batch, dims[s], dims[s + 1]), ty[s], dist, scale)
           for s in range(len(dims) - 1)]
     return A, Bs

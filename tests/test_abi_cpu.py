@@ -216,6 +216,53 @@ def test_chain_plan_selection(kw, expect):
         assert info[k] == v, (k, info)
 
 
+def _typed(dtypes, widths, flags=0, batch=1, M=128):
+    h = ctypes.c_void_p(123)
+    n = len(widths) - 1
+    ts = (ctypes.c_int32 * len(dtypes))(*dtypes) if dtypes is not None else None
+    w = (ctypes.c_int64 * len(widths))(*widths)
+    st = cf.lib().b2b_chain_create_typed(ctypes.byref(h), ts, batch, M, n, w, None, None, flags)
+    info = None
+    if st == 0:
+        buf = ctypes.create_string_buffer(512)
+        assert cf.lib().b2b_gemm_get_info(h, buf, 512) == 0
+        info = dict(kv.split("=", 1) for kv in buf.value.decode().split())
+        assert cf.lib().b2b_gemm_destroy(h) == 0
+    else:
+        assert h.value is None
+    return st, info
+
+
+@pytest.mark.parametrize("dtypes,widths,expect", [
+    ((0, 1, 0), (128, 128, 128), dict(dtype="f16/bf16/f16", mfma="32x32x16", remap="relabel")),
+    ((1, 0, 1), (256, 256, 64), dict(dtype="bf16/f16/bf16", mfma="32x32x16", lds_bytes="163840")),
+    ((0, 1, 0, 1), (128, 96, 128, 64), dict(dtype="f16/bf16/f16/bf16", mfma="32x32x16", launches="1")),
+    ((0, 0, 0, 1), (128, 128, 128, 64), dict(dtype="f16/f16/f16/bf16", path="fused")),
+    # one type throughout: the plan of b2b_chain_create
+    ((1, 1, 1), (128, 128, 128), dict(dtype="bf16", mfma="16x16x32")),
+    ((2, 2, 2), (64, 64, 64), dict(dtype="f64", mfma="f64_16x16x4")),
+])
+def test_typed_plan_selection(dtypes, widths, expect):
+    st, info = _typed(dtypes, widths)
+    assert st == 0
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
+
+
+@pytest.mark.parametrize("dtypes,widths,flags,status", [
+    (None, (128, 128, 128), 0, 1),
+    ((0, 1, 0), (128, 128, 128), 2 << 4, 2),                      # lane-half swaps: not compiled typed
+    ((0, 1, 0), (128, 128, 128), 2 | (3 << 4), 2),                # orientation N
+    ((0, 2, 0), (64, 64, 64), 0, 2),                              # fp64 mixed with a 16-bit type
+    ((0, 1, 0, 1, 0), (128, 128, 128, 128, 64), 0, 2),            # fused typed: up to three GEMMs
+    ((0, 1, 0, 1), (256, 128, 128, 64), 0, 2),                    # three typed GEMMs: widths up to 128
+    ((0, 5, 0), (128, 128, 128), 0, 2),                           # unknown type
+])
+def test_typed_rejects(dtypes, widths, flags, status):
+    st, _ = _typed(dtypes, widths, flags)
+    assert st == status
+
+
 def test_gemm_run_rejects_chain_plans():
     st, h = _chain()
     assert st == 0
