@@ -21,9 +21,9 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, F64 = 0, 1, 2
+F16, BF16, F64, TF32 = 0, 1, 2, 3
 _NAMES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16,
-          "f64": F64, "fp64": F64, "float64": F64}
+          "f64": F64, "fp64": F64, "float64": F64, "tf32": TF32}
 
 _lib = None
 
@@ -44,7 +44,7 @@ def _load():
         lib.oracle_cascade_typed.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, vp, vp, i64, vp, ctypes.c_int]
         lib.oracle_cascade_typed.restype = ctypes.c_int
         for n in ("oracle_encode_f16_array", "oracle_encode_bf16_array",
-                  "oracle_decode_f16_array", "oracle_decode_bf16_array"):
+                  "oracle_decode_f16_array", "oracle_decode_bf16_array", "oracle_round_tf32_array"):
             getattr(lib, n).argtypes = [vp, vp, i64]
             getattr(lib, n).restype = None
         _lib = lib
@@ -62,9 +62,15 @@ def _ptr(a):
 
 
 def _as_input(dt, x):
-    """16-bit inputs travel as their uint16 encodings, fp64 as float64."""
+    """16-bit inputs travel as their uint16 encodings, fp64 as float64, tf32
+    as the float32 values it rounds."""
     if dt == F64:
         return np.ascontiguousarray(x, dtype=np.float64)
+    if dt == TF32:
+        x = np.ascontiguousarray(x)
+        if x.dtype != np.float32:
+            raise TypeError("tf32 oracle inputs are float32 values")
+        return x
     x = np.ascontiguousarray(x)
     if x.dtype != np.uint16:
         raise TypeError("16-bit oracle inputs are uint16 bit patterns")
@@ -99,10 +105,20 @@ def decode_bf16(h):
     return y
 
 
+def round_tf32(x):
+    """float32 -> float32 rounded to tf32 (10 fraction bits, nearest-even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, np.float32)
+    _load().oracle_round_tf32_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
 def decode(dtype, x):
     dt = dtype_code(dtype)
     if dt == F64:
         return np.asarray(x, dtype=np.float64)
+    if dt == TF32:
+        return np.asarray(x, dtype=np.float32)
     return decode_f16(x) if dt == F16 else decode_bf16(x)
 
 
@@ -110,19 +126,22 @@ def encode(dtype, x):
     dt = dtype_code(dtype)
     if dt == F64:
         return np.asarray(x, dtype=np.float64)
+    if dt == TF32:
+        return np.asarray(x, dtype=np.float32)
     return encode_f16(x) if dt == F16 else encode_bf16(x)
 
 
 def gemm_acc(dtype, X, B):
     """One stage before rounding: sum_k X[m,k]*B[k,n], k ascending from +0,
-    float32 for 16-bit inputs (returned as float32), float64 with fma for fp64."""
+    float32 for 16-bit inputs (returned as float32), float64 with fma for fp64,
+    float32 over operands rounded to tf32 for tf32."""
     dt = dtype_code(dtype)
     X = _as_input(dt, X)
     B = _as_input(dt, B)
     M, K = X.shape
     K2, N = B.shape
     assert K == K2
-    out = np.empty((M, N), np.float64 if dt == F64 else np.float32)
+    out = np.empty((M, N), np.float64 if dt == F64 else np.float32)     # tf32 sums in float32 too
     rc = _load().oracle_gemm_acc(dt, M, K, N, _ptr(X), _ptr(B), _ptr(out))
     if rc:
         raise ValueError(f"oracle_gemm_acc failed ({rc})")
@@ -141,7 +160,7 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
     """
     if isinstance(dtype, (list, tuple)):
         types = [dtype_code(t) for t in dtype]
-        if len(types) != len(Bs) + 1 or any(t == F64 for t in types):
+        if len(types) != len(Bs) + 1 or any(t in (F64, TF32) for t in types):
             raise ValueError("one 16-bit type per GEMM and one for D")
         if len(set(types)) == 1:
             return cascade(types[0], A, Bs, rows, nthreads)
@@ -165,7 +184,7 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
         nrows = rows.size
     else:
         nrows = batch * M
-    out = np.empty((nrows, dims[-1]), np.float64 if dt == F64 else np.uint16)
+    out = np.empty((nrows, dims[-1]), {F64: np.float64, TF32: np.float32}.get(dt, np.uint16))
     if nthreads is None:
         nthreads = os.cpu_count() or 1
     if types is None:

@@ -25,6 +25,14 @@
  *   - fp64 accumulates with a fused multiply-add per term (C99 fma);
  *   - inputs are dense row-major, batches contiguous.
  *
+ * tf32 (the type of the pages' own worked example): inputs and outputs are
+ * binary32 values; each GEMM rounds both operands to tf32 (1 sign, 8 exponent
+ * and 10 fraction bits: binary32 with the low 13 fraction bits rounded off to
+ * nearest-even), multiplies them exactly (two 11-bit significands fit a
+ * binary32 product) and sums the K products in binary32, ascending k from +0.
+ * The stage result stays binary32 and is rounded to tf32 when the next GEMM
+ * takes it as an operand; D is the last stage's binary32 result.
+ *
  * The binary16 / bfloat16 encoders below are written from the IEEE 754
  * definitions (round to nearest, ties to even, gradual underflow, overflow to
  * infinity); no vendor conversion routine is used.
@@ -37,7 +45,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_BF16 = 1, OR_F64 = 2 };
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F64 = 2, OR_TF32 = 3 };
 
 static uint32_t f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
 static float bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
@@ -118,6 +126,28 @@ uint16_t oracle_f32_to_bf16(float x)
 
 float oracle_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
 
+/* ---------------------------------------------------------------------------
+ * tf32: the tf32 quantum is 2^13 units of the binary32 last place in every
+ * binade (normal and subnormal alike, the exponent field being the same), so
+ * rounding to nearest-even acts on the low 13 bits of the encoding; a carry
+ * into the exponent is the next binade, into the all-ones exponent overflow
+ * to infinity.  Infinities stay; a NaN stays a (quiet) NaN.
+ * ------------------------------------------------------------------------- */
+float oracle_round_tf32(float x)
+{
+    uint32_t u = f32_bits(x);
+    if (((u >> 23) & 0xFFu) == 0xFFu) {
+        if (u & 0x7FFFFFu) u |= 0x400000u;
+        return bits_f32(u & ~0x1FFFu);
+    }
+    uint32_t q = u >> 13, rem = u & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (q & 1u))) q++;
+    return bits_f32(q << 13);
+}
+
+void oracle_round_tf32_array(const float* x, float* y, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) y[i] = oracle_round_tf32(x[i]); }
+
 void oracle_encode_f16_array(const float* x, uint16_t* y, int64_t n)
 { for (int64_t i = 0; i < n; ++i) y[i] = oracle_f32_to_f16(x[i]); }
 void oracle_encode_bf16_array(const float* x, uint16_t* y, int64_t n)
@@ -150,6 +180,19 @@ int oracle_gemm_acc(int dtype, int64_t M, int64_t K, int64_t N,
             for (int64_t k = 0; k < K; ++k) {
                 double a = x[m * K + k];
                 for (int64_t n = 0; n < N; ++n) row[n] = fma(a, b[k * N + n], row[n]);
+            }
+        }
+        return 0;
+    }
+    if (dtype == OR_TF32) {
+        const float* x = (const float*)X; const float* b = (const float*)B;
+        float* acc = (float*)acc_out;
+        for (int64_t m = 0; m < M; ++m) {
+            float* row = acc + m * N;
+            for (int64_t n = 0; n < N; ++n) row[n] = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                float a = oracle_round_tf32(x[m * K + k]);
+                for (int64_t n = 0; n < N; ++n) row[n] = row[n] + a * oracle_round_tf32(b[k * N + n]);
             }
         }
         return 0;
@@ -220,6 +263,22 @@ static void* cascade_worker(void* arg)
                 void* t = xin; xin = xout; xout = t; x = (double*)xin;
             }
             memcpy((double*)j->D + i * j->dims[j->nst], xin, (size_t)j->dims[j->nst] * sizeof(double));
+        } else if (j->dtype == OR_TF32) {
+            const float* a = (const float*)j->A + (b * j->M + m) * K0;
+            float* x = (float*)xin;
+            for (int64_t k = 0; k < K0; ++k) x[k] = a[k];
+            for (int s = 0; s < j->nst; ++s) {
+                int64_t K = j->dims[s], N = j->dims[s + 1];
+                const float* w = j->Bf[s] + b * K * N;   /* already rounded to tf32 */
+                float* y = (float*)xout;
+                for (int64_t n = 0; n < N; ++n) y[n] = 0.0f;
+                for (int64_t k = 0; k < K; ++k) {
+                    float av = oracle_round_tf32(x[k]);
+                    for (int64_t n = 0; n < N; ++n) y[n] = y[n] + av * w[k * N + n];
+                }
+                void* t = xin; xin = xout; xout = t; x = (float*)xin;
+            }
+            memcpy((float*)j->D + i * j->dims[j->nst], xin, (size_t)j->dims[j->nst] * sizeof(float));
         } else {
             const uint16_t* a = (const uint16_t*)j->A + (b * j->M + m) * K0;
             float* x = (float*)xin;
@@ -255,7 +314,8 @@ static int cascade_run(int dtype, const int* types, int nstages, const int64_t* 
                        int64_t nrows, void* D_out, int nthreads)
 {
     if (nstages < 1 || nstages > OR_MAX_STAGES || batch < 0 || M < 0 || nrows < 0) return 1;
-    if (dtype != OR_F16 && dtype != OR_BF16 && dtype != OR_F64) return 2;
+    if (dtype != OR_F16 && dtype != OR_BF16 && dtype != OR_F64 && dtype != OR_TF32) return 2;
+    if (types && dtype == OR_TF32) return 2;
     for (int s = 0; s <= nstages; ++s)
         if (types && types[s] != OR_F16 && types[s] != OR_BF16) return 2;
     for (int s = 0; s <= nstages; ++s) if (dims[s] <= 0) return 1;
@@ -279,7 +339,10 @@ static int cascade_run(int dtype, const int* types, int nstages, const int64_t* 
         int64_t n = batch * dims[s] * dims[s + 1];
         dec[s] = (float*)malloc((size_t)n * sizeof(float));
         if (!dec[s]) { rc = 3; goto done; }
-        for (int64_t i = 0; i < n; ++i) dec[s][i] = dec16(base.st[s], ((const uint16_t*)B[s])[i]);
+        if (dtype == OR_TF32)
+            for (int64_t i = 0; i < n; ++i) dec[s][i] = oracle_round_tf32(((const float*)B[s])[i]);
+        else
+            for (int64_t i = 0; i < n; ++i) dec[s][i] = dec16(base.st[s], ((const uint16_t*)B[s])[i]);
         base.Bf[s] = dec[s];
     }
     {

@@ -148,6 +148,9 @@ def to_dtype(x, dtype):
                         np.empty(x.size, np.uint16)).reshape(shape)
     if dtype == "f64":
         return x.reshape(shape)
+    if dtype == "tf32":                 # float32 storage; the cascade rounds operands to tf32 itself
+        return _chunked(x.size, lambda a, b: x[a:b].astype(np.float32),
+                        np.empty(x.size, np.float32)).reshape(shape)
     raise ValueError(dtype)
 
 

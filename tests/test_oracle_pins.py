@@ -141,6 +141,60 @@ def test_rounding_points():
 
 
 # ----------------------------------------------------------------------------
+# tf32 rounding
+# ----------------------------------------------------------------------------
+def _tf32_ref(x):
+    """Nearest-even rounding of float32 values to 11 significant bits in
+    float64 arithmetic (frexp / rint / ldexp), with the fixed 2^-136 quantum
+    below 2^-126 and overflow to infinity past the largest tf32 value;
+    independent of the oracle's integer rounding of the encoding."""
+    x = np.asarray(x, np.float64)
+    out = np.empty_like(x)
+    fin = np.isfinite(x)
+    out[~fin] = x[~fin]
+    xf = x[fin]
+    m, e = np.frexp(xf)                             # xf = m 2^e, 0.5 <= |m| < 1
+    q = np.where(np.abs(xf) >= 2.0 ** -126,
+                 np.ldexp(np.rint(np.ldexp(m, 11)), e - 11),
+                 np.ldexp(np.rint(np.ldexp(xf, 136)), -136))
+    big = np.abs(q) > (2.0 - 2.0 ** -10) * 2.0 ** 127
+    q[big] = np.copysign(np.inf, q[big])
+    out[fin] = q
+    return out
+
+
+def test_tf32_rounding_against_float64_reference():
+    """Every fraction pattern of five binades (normal, the smallest normal,
+    a subnormal one, the largest), 2^22 random encodings, and the specials."""
+    pats = [np.arange(1 << 23, dtype=np.uint32) | np.uint32(e << 23) for e in (1, 2, 127, 254, 0)]
+    rng = np.random.default_rng(5)
+    pats.append(rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32))
+    u = np.concatenate(pats)
+    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    got = oracle.round_tf32(x).astype(np.float64)
+    want = _tf32_ref(x)
+    bad = ~((got == want) | (np.isnan(got) & np.isnan(want)))
+    assert not bad.any(), (x[bad][:5], got[bad][:5], want[bad][:5])
+    sp = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0], np.float32)
+    r = oracle.round_tf32(sp)
+    assert r[0] == np.inf and r[1] == -np.inf and np.isnan(r[2])
+    assert r[3] == 0.0 and not np.signbit(r[3]) and r[4] == 0.0 and np.signbit(r[4])
+
+
+def test_tf32_rounding_points():
+    """1 + 2^-11 is a tie between 1 and 1 + 2^-10 (-> 1, even); 1 + 3*2^-11
+    a tie between 1 + 2^-10 and 1 + 2^-9 (-> 1 + 2^-9, even); the largest
+    float32 rounds past the largest tf32 value (2 - 2^-10) 2^127 to infinity;
+    the smallest subnormal is below half the tf32 quantum 2^-136."""
+    x = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 + 2 ** -11 + 2 ** -20,
+                  np.finfo(np.float32).max, 2.0 ** -149, 3 * 2.0 ** -137], np.float32)
+    got = oracle.round_tf32(x).tolist()
+    assert got == [1.0, 1 + 2 ** -9, 1 + 2 ** -10, np.inf, 0.0, 2.0 ** -135]
+
+
+# ----------------------------------------------------------------------------
 # One stage against exact rational arithmetic (tiny sizes)
 # ----------------------------------------------------------------------------
 def _exact(Xd, Bd):
@@ -150,17 +204,21 @@ def _exact(Xd, Bd):
              for n in range(N)] for m in range(M)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16", "f64"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f64", "tf32"])
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_stage_within_dot_product_bound(dtype, seed):
     """|acc - exact| <= gamma_K * sum_k |x||b| (Higham, Accuracy and Stability of
     Numerical Algorithms, the recursive-summation dot-product bound), with the
-    accumulator's unit roundoff: 2^-24 for float32, 2^-53 for float64."""
+    accumulator's unit roundoff: 2^-24 for float32, 2^-53 for float64.  For
+    tf32 the exact products are those of the operands rounded to tf32."""
     M, K, N = 5, 13, 7
     X = synth.tensor(seed, 0, (M, K), dtype, "uniform")
     B = synth.tensor(seed, 1, (K, N), dtype, "uniform")
     acc = oracle.gemm_acc(dtype, X, B)
     Xd, Bd = oracle.decode(dtype, X).astype(np.float64), oracle.decode(dtype, B).astype(np.float64)
+    if dtype == "tf32":
+        Xd, Bd = _tf32_ref(Xd), _tf32_ref(Bd)
+        assert not np.array_equal(Xd, oracle.decode(dtype, X))   # the rounding did something
     ex = _exact(Xd, Bd)
     u = 2.0 ** -53 if dtype == "f64" else 2.0 ** -24
     gamma = K * u / (1 - K * u)
@@ -295,6 +353,48 @@ def test_typed_rounding_points():
     D2 = oracle.cascade(["f16", "f16", "bf16"], A, [I16, I16])
     assert oracle.decode("bf16", D2).tolist() == [[1.0, 1 + 2 ** -7, 1.5, 2.0 ** -14]]
     assert np.array_equal(oracle.cascade(["f16", "f16", "f16"], A, [I16, I16]), A)
+
+
+@pytest.mark.parametrize("lims,dims", [([2047, 3, 1], [16, 16, 16]), ([40, 40, 2, 1], [32, 32, 16, 8])])
+def test_tf32_cascade_integers_exact(lims, dims):
+    """Integer operands exact in tf32 (below 2^11) whose stage results grow
+    past 2^11, so they are rounded to tf32 when the next GEMM takes them;
+    every partial sum is an integer below 2^24, exact in float32.  The oracle
+    must equal the exact int64 stages with the float64 tf32 reference rounding
+    each intermediate, and D unrounded."""
+    rng = np.random.default_rng(29)
+    A = rng.integers(-lims[0], lims[0] + 1, (50, dims[0])).astype(np.float32)
+    Bs = [rng.integers(-lims[s + 1], lims[s + 1] + 1, (dims[s], dims[s + 1])).astype(np.float32)
+          for s in range(len(dims) - 1)]
+    D = oracle.cascade("tf32", A, Bs)
+    x = A.astype(np.int64)
+    rounded = False
+    for s, B in enumerate(Bs):
+        y = x @ B.astype(np.int64)
+        assert np.abs(y).max() < 2 ** 24
+        if s + 1 < len(Bs):
+            r = _tf32_ref(y.astype(np.float64))
+            rounded |= bool((r != y).any())
+            x = r.astype(np.int64)
+        else:
+            x = y
+    assert rounded
+    assert D.dtype == np.float32 and np.array_equal(D.astype(np.float64), x.astype(np.float64))
+
+
+def test_tf32_identity_and_permutation():
+    """Identity weights give tf32(A) (the first GEMM rounds A, the second
+    takes an exact tf32 value); permutation weights permute those columns."""
+    n = 32
+    A = synth.tensor(13, 0, (2, 40, n), "tf32", "normal")
+    eye = np.broadcast_to(np.eye(n, dtype=np.float32), (2, n, n)).copy()
+    D = oracle.cascade("tf32", A, [eye, eye])
+    want = _tf32_ref(A).astype(np.float32)
+    assert np.array_equal(D, want) and not np.array_equal(D, A)
+    p = np.random.default_rng(4).permutation(n)
+    P = np.zeros((n, n), np.float32); P[p, np.arange(n)] = 1.0
+    D2 = oracle.cascade("tf32", A[0], [P, eye[0]])
+    assert np.array_equal(D2, want[0][:, p])
 
 
 # ----------------------------------------------------------------------------
