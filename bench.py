@@ -20,9 +20,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"f16": 2516.6e12, "bf16": 2516.6e12, "f64": 78.6e12}   # dense MFMA, FLOP/s
+# dense MFMA, FLOP/s; tf32 has no matrix instruction on gfx950 and runs as
+# bf16 passes, so its peak is the bf16 peak over the passes per product
+PEAK = {"f16": 2516.6e12, "bf16": 2516.6e12, "f64": 78.6e12, "tf32": 2516.6e12 / 3, "tf32x4": 2516.6e12 / 4}
 HBM = 8.0e12                                                   # B/s
-ELT = {"f16": 2, "bf16": 2, "f64": 8}
+ELT = {"f16": 2, "bf16": 2, "f64": 8, "tf32": 4}
 
 
 def workload_numbers(c):
@@ -50,6 +52,9 @@ def main():
     ap.add_argument("--dims", default=None,
                     help="comma-separated widths K,N1,N2[,N3] replacing the workload's (same batch, M, "
                          "distribution and seed)")
+    ap.add_argument("--dtype", default=None, choices=["f16", "bf16", "f64", "tf32"],
+                    help="run the workload's shape, distribution and seed in another type")
+    ap.add_argument("--tf32-exact", action="store_true", help="tf32 with four bf16 passes per product")
     ap.add_argument("--types", default=None,
                     help="comma-separated 16-bit type per GEMM and one for D (e.g. f16,bf16,f16): "
                          "a cascade with a type per stage on the workload's shape")
@@ -88,6 +93,12 @@ def main():
     import synth
 
     c = dict(synth.CONFIGS[args.config])
+    if args.dtype and args.dtype != c["dtype"]:
+        c["name"] = c["name"].replace(c["dtype"], args.dtype, 1)
+        c["dtype"] = args.dtype
+    if args.tf32_exact and c["dtype"] != "tf32":
+        print("--tf32-exact needs --dtype tf32", file=sys.stderr)
+        sys.exit(2)
     if args.dims:
         c["dims"] = [int(x) for x in args.dims.split(",")]
         c["name"] = (f"{c['dtype']} b{c['batch']} {c['M']}x{c['dims'][0]} . "
@@ -121,10 +132,11 @@ def main():
         plan = cf.Chain(types, c["batch"], c["M"], dims, remap=args.remap, unfused=args.unfused)
     elif len(dims) <= 4:
         plan = cf.Plan(dt, c["batch"], c["M"], *dims[:3], dims[3] if len(dims) > 3 else 0,
-                       remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32)
+                       remap=args.remap, orient_n=args.orient_n, unfused=args.unfused, mfma32=args.mfma32,
+                       tf32_exact=args.tf32_exact)
     else:   # longer cascades: the chain entry points
         plan = cf.Chain(dt, c["batch"], c["M"], dims, remap=args.remap, unfused=args.unfused,
-                        mfma32=args.mfma32)
+                        mfma32=args.mfma32, tf32_exact=args.tf32_exact)
     stream = torch.cuda.current_stream()
     if args.tune:
         plan.tune(sets, reps=2 * R, stream=stream)
@@ -194,12 +206,13 @@ def main():
 
     value = flop / (ms_per_step * 1e-3) / 1e12
     ai = flop / algo_bytes
-    ridge = PEAK[dt] / HBM
+    pk = PEAK["tf32x4" if args.tf32_exact else dt]
+    ridge = pk / HBM
     if ai < ridge:
         roof = {"bound": "hbm", "achieved": algo_bytes / (launch_ms * 1e-3) / 1e9, "peak": HBM / 1e9,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flop / (launch_ms * 1e-3) / 1e12, "peak": PEAK[dt] / 1e12,
+        roof = {"bound": "mfma", "achieved": flop / (launch_ms * 1e-3) / 1e12, "peak": pk / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch from the committed rocprofv3 counters, valid only
@@ -211,7 +224,7 @@ def main():
         ent = tr["configs"].get(str(args.config))
         if (ent and tr["source_digest"] == _b.source_digest() and not args.unfused
                 and args.remap == "auto" and not args.orient_n and not args.mfma32 and not args.dims
-                and not args.tune and not types):
+                and not args.tune and not types and not args.dtype):
             roof["traffic"] = ent["hbm_bytes"]
             roof["traffic_unit"] = "bytes per launch (FETCH_SIZE x %.3f + WRITE_SIZE x %.3f)" % (
                 tr["fetch_scale"], tr["write_scale"])
@@ -263,7 +276,7 @@ def main():
         "vs_baseline": None,
         "dtype": "/".join(types) if types else dt,
         "data": "synthetic",
-        "pct_of_mfma_peak": 100.0 * value * 1e12 / PEAK[dt],
+        "pct_of_mfma_peak": 100.0 * value * 1e12 / pk,
         "config": {"workload": c["name"], "batch": c["batch"], "M": c["M"], "dims": dims,
                    "path": "unfused" if args.unfused else "fused", "remap": args.remap,
                    "orientation": "N" if args.orient_n else "T", "rotating_buffer_sets": R,

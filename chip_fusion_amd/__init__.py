@@ -13,11 +13,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libb2b.so")
 
-F16, BF16, F64 = 0, 1, 2
-DTYPES = {"f16": F16, "bf16": BF16, "f64": F64}
-TORCH_DTYPES = {F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64}
+F16, BF16, F64, TF32 = 0, 1, 2, 3
+DTYPES = {"f16": F16, "bf16": BF16, "f64": F64, "tf32": TF32}
+# tf32 cascades take and return float32 tensors (the GEMMs round their operands to tf32)
+TORCH_DTYPES = {F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64, TF32: torch.float32}
 REMAP = {"auto": 0, "bpermute": 1, "permlane": 2, "lds": 3, "relabel": 4}
-FLAG_UNFUSED, FLAG_ORIENT_N, FLAG_MFMA_32X32 = 1, 2, 4
+FLAG_UNFUSED, FLAG_ORIENT_N, FLAG_MFMA_32X32, FLAG_TF32_EXACT = 1, 2, 4, 8
 SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x16": 3,
           "f16_16x16x16": 4, "f64_16x16x4": 5}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
@@ -92,11 +93,11 @@ class Plan:
     """A planned cascade D = rnd(rnd(A.B0).B1)[.B2] (b2b_gemm_create)."""
 
     def __init__(self, dtype, batch, M, K, N1, N2, N3=0, ld=None, batch_stride=None,
-                 remap="auto", orient_n=False, unfused=False, mfma32=False):
+                 remap="auto", orient_n=False, unfused=False, mfma32=False, tf32_exact=False):
         self.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
         self.batch, self.M, self.dims = batch, M, [K, N1, N2] + ([N3] if N3 else [])
         flags = ((REMAP[remap] << 4) | (FLAG_ORIENT_N if orient_n else 0) | (FLAG_UNFUSED if unfused else 0)
-                 | (FLAG_MFMA_32X32 if mfma32 else 0))
+                 | (FLAG_MFMA_32X32 if mfma32 else 0) | (FLAG_TF32_EXACT if tf32_exact else 0))
         arr = ctypes.c_int64 * 5
         h = ctypes.c_void_p()
         st = lib().b2b_gemm_create(ctypes.byref(h), self.dtype, batch, M, K, N1, N2, N3,
@@ -151,14 +152,15 @@ class Chain(Plan):
     (b2b_chain_create_typed)."""
 
     def __init__(self, dtype, batch, M, widths, ld=None, batch_stride=None, remap="auto",
-                 unfused=False, mfma32=False):
+                 unfused=False, mfma32=False, tf32_exact=False):
         code = lambda t: DTYPES[t] if isinstance(t, str) else int(t)
         typed = isinstance(dtype, (list, tuple))
         self.dtypes = [code(t) for t in dtype] if typed else None
         self.dtype = self.dtypes[0] if typed else code(dtype)
         self.batch, self.M, self.dims = batch, M, list(widths)
         nst = len(self.dims) - 1
-        flags = ((REMAP[remap] << 4) | (FLAG_UNFUSED if unfused else 0) | (FLAG_MFMA_32X32 if mfma32 else 0))
+        flags = ((REMAP[remap] << 4) | (FLAG_UNFUSED if unfused else 0) | (FLAG_MFMA_32X32 if mfma32 else 0)
+                 | (FLAG_TF32_EXACT if tf32_exact else 0))
         w = (ctypes.c_int64 * (nst + 1))(*self.dims)
         arr = ctypes.c_int64 * (nst + 2)
         h = ctypes.c_void_p()
@@ -261,17 +263,19 @@ def mfma_probe(shape, a, b, stream=None):
 
 
 def to_device(x, dtype, device="cuda"):
-    """numpy input (uint16 encodings or float64) -> torch tensor of the dtype."""
+    """numpy input (uint16 encodings, float64, or float32 for tf32) -> torch tensor of the dtype."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     if dt == F64:
         return torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(device)
+    if dt == TF32:
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
     t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TORCH_DTYPES[dt])
     return t.to(device)
 
 
 def to_host(t):
-    """torch tensor -> numpy (uint16 encodings for 16-bit types, float64)."""
+    """torch tensor -> numpy (uint16 encodings for 16-bit types, float64, float32)."""
     t = t.detach().cpu().contiguous()
-    if t.dtype == torch.float64:
+    if t.dtype in (torch.float64, torch.float32):
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)

@@ -45,6 +45,7 @@ constexpr int kMaxSt = b2bk::kMaxStages;
 struct b2b_gemm_plan {
     int dtype = 0, nst = 0, mode = 0, orn = 0;
     int tm = -1;                                 // type per stage (bit s: bf16), or -1: dtype throughout
+    int passes = 0;                              // tf32: bf16 passes per product (3 or 4)
     int64_t batch = 0, M = 0, dims[kMaxSt + 1] = {};
     // leading dimensions and batch strides (elements): [0] A, [1 + s] B_s, [nst + 1] D
     int64_t ld[kMaxSt + 2] = {}, bs[kMaxSt + 2] = {};
@@ -62,7 +63,7 @@ struct b2b_gemm_plan {
 
 namespace {
 
-int elt_size(int dt) { return dt == B2B_DTYPE_F64 ? 8 : 2; }
+int elt_size(int dt) { return dt == B2B_DTYPE_F64 ? 8 : (dt == B2B_DTYPE_TF32 ? 4 : 2); }
 
 b2b::Shape shape_of(int dt) {
     return dt == B2B_DTYPE_F64 ? b2b::SH_F64_16x16x4
@@ -84,8 +85,8 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
 // Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
 // 16x16x4 for fp64): the smallest width bound that holds them all, or null
 // when a granule, a bound or LDS rules the cascade out.
-bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1) {
-    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm) return false;
+bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1, int passes = 0) {
+    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm || d.passes != passes) return false;
     const bool f64 = dt == B2B_DTYPE_F64;
     if (dims[0] % (f64 ? 8 : 32) || dims[0] > d.maxd) return false;
     int64_t lds = 0;
@@ -95,10 +96,10 @@ bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm 
     return lds <= 160 * 1024;
 }
 
-const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1) {
+const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!gen_fits(d, dt, nst, dims, tm) || (nst > 1 && d.mode != mode)) continue;
+        if (!gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd) best = &d;
     }
     return best;
@@ -217,22 +218,27 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
                          const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1) {
     if (!plan) return B2B_ERROR_INVALID_VALUE;
     *plan = nullptr;
-    if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
+    if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64 && dt != B2B_DTYPE_TF32)
+        return B2B_ERROR_NOT_SUPPORTED;
     if (nst < 1 || nst > kMaxSt || !d) return B2B_ERROR_INVALID_VALUE;
     if (batch < 1 || M < 1) return B2B_ERROR_INVALID_VALUE;
     for (int i = 0; i <= nst; ++i)
         if (d[i] < 1 || d[i] > (int64_t)1 << 24) return B2B_ERROR_INVALID_VALUE;
     if (batch > (int64_t)1 << 30 || M > (int64_t)1 << 31) return B2B_ERROR_INVALID_VALUE;
-    const uint32_t known = B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_FLAG_MFMA_32X32 | B2B_REMAP_MASK;
+    const uint32_t known =
+        B2B_FLAG_UNFUSED | B2B_FLAG_ORIENT_N | B2B_FLAG_MFMA_32X32 | B2B_FLAG_TF32_EXACT | B2B_REMAP_MASK;
     if (flags & ~known) return B2B_ERROR_INVALID_VALUE;
+    const bool tf32 = dt == B2B_DTYPE_TF32;
+    if ((flags & B2B_FLAG_TF32_EXACT) && !tf32) return B2B_ERROR_INVALID_VALUE;
+    const int passes = tf32 ? ((flags & B2B_FLAG_TF32_EXACT) ? 4 : 3) : 0;
     const int mode = pick_mode(dt, flags);
     if (mode > b2bk::MODE_RELABEL) return B2B_ERROR_INVALID_VALUE;
     const int orn = (flags & B2B_FLAG_ORIENT_N) ? 1 : 0;
     if (orn && mode != b2bk::MODE_BPERM && mode != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
     const bool typed = tm >= 0;
-    if (typed && (orn || (mode != b2bk::MODE_RELABEL && (flags & B2B_REMAP_MASK) != B2B_REMAP_AUTO)))
-        return B2B_ERROR_NOT_SUPPORTED;   // typed cascades are relabelled on the 32x32x16 kernels
-    const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0 || typed;
+    // typed and tf32 cascades are relabelled on the 32x32x16 kernels
+    if ((typed || tf32) && (orn || mode != b2bk::MODE_RELABEL)) return B2B_ERROR_NOT_SUPPORTED;
+    const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0 || typed || tf32;
     if (s32 && (orn || dt == B2B_DTYPE_F64)) return B2B_ERROR_NOT_SUPPORTED;
     // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
     const int mode32 = (flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO ? b2bk::MODE_RELABEL : mode;
@@ -258,6 +264,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     if (!p) return B2B_ERROR_OUT_OF_MEMORY;
     p->dtype = dt;
     p->tm = tm;
+    p->passes = passes;
     p->nst = nst;
     p->mode = mode;
     p->orn = orn;
@@ -274,7 +281,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         if (s32 || nst > 3) {
             // the fixed-width kernels cover up to three GEMMs
             if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
-            p->fused = find_gen(dt, nst, dims, mode32, tm);
+            p->fused = find_gen(dt, nst, dims, mode32, tm, passes);
             p->mode = mode32;
         } else if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
             // the cheapest rearrangement compiled for this shape
@@ -309,7 +316,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
             const int sdt = typed ? ((sub & 1) ? B2B_DTYPE_BF16 : B2B_DTYPE_F16) : dt;
             const int stm = (sub == 1 || sub == 2) ? sub : -1;
             p->stage_k[s] = (s32 || stm >= 0) ? nullptr : find_kernel(sdt, 1, d2, 0, 0, km0);
-            if (!p->stage_k[s]) p->stage_k[s] = find_gen(sdt, 1, d2, 0, stm);
+            if (!p->stage_k[s]) p->stage_k[s] = find_gen(sdt, 1, d2, 0, stm, passes);
             if (!p->stage_k[s]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         }
         for (int s = 0; s + 1 < nst; ++s) {
@@ -406,7 +413,8 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
     bool same = true;
     int tm = 0;
     for (int s = 0; s <= nst; ++s) {
-        if (dtypes[s] != B2B_DTYPE_F16 && dtypes[s] != B2B_DTYPE_BF16 && dtypes[s] != B2B_DTYPE_F64)
+        if (dtypes[s] != B2B_DTYPE_F16 && dtypes[s] != B2B_DTYPE_BF16 && dtypes[s] != B2B_DTYPE_F64 &&
+            dtypes[s] != B2B_DTYPE_TF32)
             return B2B_ERROR_NOT_SUPPORTED;
         same = same && dtypes[s] == dtypes[0];
         if (dtypes[s] == B2B_DTYPE_BF16) tm |= 1 << s;
@@ -414,7 +422,7 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
     // one type throughout: exactly the plan of b2b_chain_create
     if (same) return create_impl(plan, (int)dtypes[0], batch, M, nst, widths, ld, batch_stride, flags, true);
     for (int s = 0; s <= nst; ++s)
-        if (dtypes[s] == B2B_DTYPE_F64) return B2B_ERROR_NOT_SUPPORTED;
+        if (dtypes[s] == B2B_DTYPE_F64 || dtypes[s] == B2B_DTYPE_TF32) return B2B_ERROR_NOT_SUPPORTED;
     return create_impl(plan, (int)dtypes[0], batch, M, nst, widths, ld, batch_stride, flags, true, tm);
 }
 
@@ -456,7 +464,7 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
     for (const KernelDesc& d : b2b::registry()) {
         if (d.dtype != p->dtype || d.nst != p->nst || d.tm != p->tm) continue;
         if (d.rtw) {
-            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims, p->tm)) continue;
+            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims, p->tm, p->passes)) continue;
         } else {
             if (s32 || d.orn != p->orn) continue;
             bool ok = true;
@@ -556,12 +564,15 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
 
 b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     if (!p || !buf || len == 0) return B2B_ERROR_INVALID_VALUE;
-    static const char* dts[] = {"f16", "bf16", "f64"};
+    static const char* dts[] = {"f16", "bf16", "f64", "tf32"};
     static const char* modes[] = {"none", "bpermute", "permlane", "lds", "relabel"};
     const KernelDesc* k = p->unfused ? p->stage_k[0] : p->fused;
     int64_t work = 0;
     for (int64_t w : p->work_bytes) work += w;
-    const char* mfma = p->dtype == B2B_DTYPE_F64 ? "f64_16x16x4" : k->shape32 ? "32x32x16" : "16x16x32";
+    const char* mfma = p->dtype == B2B_DTYPE_F64    ? "f64_16x16x4"
+                       : p->dtype == B2B_DTYPE_TF32 ? (p->passes == 4 ? "bf16x4_32x32x16" : "bf16x3_32x32x16")
+                       : k->shape32                 ? "32x32x16"
+                                                    : "16x16x32";
     int lds_bytes = k->lds_bytes;
     if (k->dyn_lds) {
         int32_t d32[kMaxSt + 1] = {};

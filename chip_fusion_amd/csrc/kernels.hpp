@@ -39,7 +39,7 @@ typedef double d4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u2_t __attribute__((ext_vector_type(2)));
 
-enum { DT_F16 = 0, DT_BF16 = 1, DT_F64 = 2 };
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F64 = 2, DT_TF32 = 3 };
 enum { MODE_BPERM = 1, MODE_PERMLANE = 2, MODE_LDS = 3, MODE_RELABEL = 4 };
 // How the K index of a GEMM stage is laid over (K-step, lane group, slot).
 enum {

@@ -8,6 +8,7 @@
 #include "kernels_cs.hpp"
 #include "kernels_gen.hpp"
 #include "kernels_gen64.hpp"
+#include "kernels_tf32.hpp"
 
 namespace b2b {
 
@@ -18,6 +19,7 @@ struct KernelDesc {
     int rtw = 0;      // 1: widths read at run time, up to maxd (dims are 0)
     int maxd = 0;
     int tm = -1;      // type per stage (bit s: bf16 operands of GEMM s, bit nst: D), or -1: all dtype
+    int passes = 0;   // tf32: bf16 matrix-instruction passes per product (3 or 4)
     const void* fn;   // the __global__ function, for occupancy queries
     // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
     int64_t (*dyn_lds)(const int32_t* d) = nullptr;
@@ -107,6 +109,38 @@ KernelDesc describe_gen() {
         if (attr != hipSuccess) return attr;
         const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST);
         hipLaunchKernelGGL(b2bk::gen_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+// tf32 instances (bf16 passes on the 32x32x16 instruction), run-time widths.
+template <class C>
+KernelDesc describe_tf32() {
+    KernelDesc d;
+    d.dtype = C::DT;
+    d.nst = C::NST;
+    for (int& x : d.dims) x = 0;   // never matched by width
+    d.mode = C::NST > 1 ? C::MODE : 0;
+    d.orn = 0;
+    d.km0 = b2bk::KM_NAT;
+    d.mt = C::ROWS_WAVE / 16;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::ROWS_WG;
+    d.lds_bytes = 0;
+    d.shape32 = 1;
+    d.rtw = 1;
+    d.maxd = C::MAXD;
+    d.passes = C::PASSES;
+    d.fn = (const void*)&b2bk::tf32_kernel<C>;
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::tf32_lds_bytes(w, C::NST); };
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void*)&b2bk::tf32_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
+        if (attr != hipSuccess) return attr;
+        const size_t shm = (size_t)b2bk::tf32_lds_bytes(a.dims, C::NST);
+        hipLaunchKernelGGL(b2bk::tf32_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };
     return d;
@@ -210,6 +244,10 @@ ProbeDesc describe_probe() {
 // B2B_GEN_TYPED(stages, max width, A tiles ahead, type mask): relabelled, a type per stage
 #define B2B_GEN_TYPED(NST, MAXD, PF, TM)                                                \
     B2B_GEN_INSTANCE(((TM) & 1) ? ::b2bk::DT_BF16 : ::b2bk::DT_F16, NST, MAXD, ::b2bk::MODE_RELABEL, PF, TM)
+// B2B_TF32_INSTANCE(stages, max width, passes)
+#define B2B_TF32_INSTANCE(...)                                                         \
+    static ::b2b::Registrar B2B_CAT(b2b_tf32_reg_, __LINE__)(                          \
+        ::b2b::describe_tf32<::b2bk::Tf32Cfg<__VA_ARGS__>>())
 // B2B_GEN64_INSTANCE(stages, max width, A tiles ahead, tiles per group)
 #define B2B_GEN64_INSTANCE(...)                                                        \
     static ::b2b::Registrar B2B_CAT(b2b_gen64_reg_, __LINE__)(                         \

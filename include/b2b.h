@@ -47,7 +47,21 @@ extern "C" {
 typedef enum {
     B2B_DTYPE_F16 = 0,   /* IEEE binary16 inputs and outputs, float32 accumulation */
     B2B_DTYPE_BF16 = 1,  /* bfloat16 inputs and outputs, float32 accumulation */
-    B2B_DTYPE_F64 = 2    /* binary64 throughout */
+    B2B_DTYPE_F64 = 2,   /* binary64 throughout */
+    B2B_DTYPE_TF32 = 3   /* the type of page 1's worked example: binary32 inputs,
+                            intermediates and outputs; every GEMM rounds both operands
+                            to tf32 (10 fraction bits, nearest-even), multiplies them
+                            and sums the products in binary32.  gfx950 has no tf32
+                            matrix instruction: each tf32 operand is split exactly into
+                            two bfloat16 parts and a product takes three bf16 passes
+                            (the part product of the two low parts, at most 2^-16 of
+                            the product, dropped) or, with B2B_FLAG_TF32_EXACT, four
+                            (every product exact).  Run-time widths on the 32x32x16
+                            instruction: K and every N multiples of 32, each at most
+                            128, weights at most 160 KB at 4 bytes per element; one to
+                            three GEMMs fused, any number unfused; rearrangement
+                            RELABEL.  Non-finite inputs give NaN where tf32 arithmetic
+                            would give an infinity. */
 } b2b_dtype_t;
 
 typedef enum {
@@ -65,6 +79,7 @@ enum {
     B2B_FLAG_ORIENT_N = 1u << 1,   /* first GEMM computed as A.B0 (accumulator lanes hold
                                       columns); default computes it transposed so that lanes
                                       hold rows.  Only with REMAP_BPERMUTE or REMAP_LDS. */
+    B2B_FLAG_TF32_EXACT = 1u << 3, /* tf32 only: four bf16 passes per product instead of three */
     B2B_FLAG_MFMA_32X32 = 1u << 2, /* fp16/bf16 only: kernels on v_mfma_f32_32x32x16 with the
                                       widths taken at run time (K, N1..N3 multiples of
                                       32, each at most 256, the fused path's weights at most

@@ -263,6 +263,39 @@ def test_typed_rejects(dtypes, widths, flags, status):
     assert st == status
 
 
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=3, widths=(128, 128, 128)), dict(dtype="tf32", mfma="bf16x3_32x32x16", waves="8",
+                                                 lds_bytes=str(128 * 128 * 2 * 4 + 8 * 4096))),
+    (dict(dtype=3, widths=(128, 128, 128), flags=8), dict(mfma="bf16x4_32x32x16")),
+    (dict(dtype=3, widths=(128, 128, 128, 64)), dict(mfma="bf16x3_32x32x16", waves="4", rows_per_wg="128",
+                                                     lds_bytes=str(160 * 1024))),
+    (dict(dtype=3, widths=(96, 64)), dict(dims="96x64", launches="1")),
+])
+def test_tf32_plan_selection(kw, expect):
+    info = _chain_info(**kw)
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3, widths=(256, 128, 128)), 2),                   # widths up to 128
+    (dict(dtype=3, widths=(128, 80, 128)), 2),                    # multiples of 32
+    (dict(dtype=3, widths=(128,) * 5), 2),                        # fused: up to three GEMMs
+    (dict(dtype=3, widths=(128, 128, 128), flags=2 << 4), 2),     # relabelled only
+    (dict(dtype=0, widths=(128, 128, 128), flags=8), 1),          # the four-pass flag is for tf32
+])
+def test_tf32_rejects(kw, status):
+    st, h = _chain(**kw)
+    assert st == status and h.value is None
+
+
+def test_typed_rejects_tf32_mix():
+    st, _ = _typed((3, 0, 3), (128, 128, 128))
+    assert st == 2
+    st, info = _typed((3, 3, 3), (128, 128, 128))
+    assert st == 0 and info["dtype"] == "tf32"
+
+
 def test_gemm_run_rejects_chain_plans():
     st, h = _chain()
     assert st == 0
