@@ -2,12 +2,12 @@
 // gfx950, which has no tf32 matrix instruction.
 //
 // A tf32 value t (binary32 with 10 fraction bits) is the exact sum of two
-// bfloat16 values: hi, t rounded to 8 significant bits, and lo = t - hi,
-// which holds the remaining 3 bits.  A product of two tf32 values is then
+// bfloat16 values: hi, the leading 8 significant bits of t, and lo = t - hi,
+// which holds the remaining 3.  A product of two tf32 values is then
 //     a b = ah bh + ah bl + al bh + al bl,
 // each term an exact product of bfloat16 values, which the bf16 matrix
-// instruction forms exactly and sums in fp32.  PASSES = 3 drops al bl (at
-// most 2^-16 of |a b|); PASSES = 4 keeps it, so every tf32 product is exact
+// instruction forms exactly and sums in fp32.  PASSES = 3 drops al bl (less
+// than 2^-14 of |a b|); PASSES = 4 keeps it, so every tf32 product is exact
 // and only the order of the fp32 sums differs from a tf32 dot product.
 //
 // Layouts are those of the 32x32x16 run-time-width kernels: the first GEMM
@@ -59,26 +59,21 @@ __host__ __device__ inline int64_t tf32_lds_bytes(const int32_t* d, int nst) {
     return tf32_weight_bytes(d, nst) + (tf32_stage_d(d, nst) ? 8 * 4096 : 0);
 }
 
-// binary32 encoding -> tf32 encoding: nearest-even on the low 13 bits (a
-// carry moves to the next binade, or to infinity); infinities stay, NaN
-// stays a quiet NaN.
+// binary32 encoding of a finite value -> tf32 encoding: nearest-even on the
+// low 13 bits (a carry moves to the next binade, or to infinity).  A NaN may
+// come out as an infinity; the split below turns either into a NaN product.
 __device__ __forceinline__ uint32_t tf32_round_bits(uint32_t u) {
-    const uint32_t r = (u + 0xFFFu + ((u >> 13) & 1u)) & 0xFFFFE000u;
-    const uint32_t special = (u & 0xFFFFE000u) | ((u & 0x7FFFFFu) ? 0x400000u : 0u);
-    return (u & 0x7F800000u) == 0x7F800000u ? special : r;
+    return (u + 0xFFFu + ((u >> 13) & 1u)) & 0xFFFFE000u;
 }
 
 // tf32 encoding t -> hi, lo (binary32 encodings with zero low halves, so
-// their upper halves are bfloat16 values) with hi + lo = t exactly: hi is t
-// rounded to 8 significant bits (half-way cases away from zero; truncated
-// where that would overflow), lo = t - hi has at most 3 significant bits.
-// A non-finite t gives hi = t and lo = NaN or 0, so the emulated products of
-// an infinity are NaN.
+// their upper halves are bfloat16 values) with hi + lo = t exactly: hi keeps
+// the leading 8 significant bits of t, lo = t - hi the other 3 (same sign,
+// below 2^-7 |t|).  An infinite t gives lo = inf - inf = NaN, so every
+// emulated product of a non-finite operand is NaN.
 __device__ __forceinline__ void tf32_split(uint32_t t, uint32_t& hi, uint32_t& lo) {
-    uint32_t h = (t + 0x8000u) & 0xFFFF0000u;
-    if ((h & 0x7F800000u) == 0x7F800000u) h = t & 0xFFFF0000u;
-    hi = h;
-    lo = __float_as_uint(__uint_as_float(t) - __uint_as_float(h));
+    hi = t & 0xFFFF0000u;
+    lo = __float_as_uint(__uint_as_float(t) - __uint_as_float(hi));
 }
 
 // upper halves of two binary32 encodings -> one packed pair of bfloat16 (x0 low)

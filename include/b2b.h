@@ -54,13 +54,14 @@ typedef enum {
                             and sums the products in binary32.  gfx950 has no tf32
                             matrix instruction: each tf32 operand is split exactly into
                             two bfloat16 parts and a product takes three bf16 passes
-                            (the part product of the two low parts, at most 2^-16 of
+                            (the part product of the two low parts, below 2^-14 of
                             the product, dropped) or, with B2B_FLAG_TF32_EXACT, four
                             (every product exact).  Run-time widths on the 32x32x16
                             instruction: K and every N multiples of 32, each at most
                             128, weights at most 160 KB at 4 bytes per element; one to
                             three GEMMs fused, any number unfused; rearrangement
-                            RELABEL.  Non-finite inputs give NaN where tf32 arithmetic
+                            RELABEL.  Non-finite inputs (and values that round past
+                            the largest tf32 value) give NaN where tf32 arithmetic
                             would give an infinity. */
 } b2b_dtype_t;
 
