@@ -21,9 +21,9 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, F64, TF32 = 0, 1, 2, 3
+F16, BF16, F64, TF32, FP8 = 0, 1, 2, 3, 4
 _NAMES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16,
-          "f64": F64, "fp64": F64, "float64": F64, "tf32": TF32}
+          "f64": F64, "fp64": F64, "float64": F64, "tf32": TF32, "fp8": FP8, "e4m3": FP8}
 
 _lib = None
 
@@ -44,7 +44,8 @@ def _load():
         lib.oracle_cascade_typed.argtypes = [vp, ctypes.c_int, vp, i64, i64, vp, vp, vp, i64, vp, ctypes.c_int]
         lib.oracle_cascade_typed.restype = ctypes.c_int
         for n in ("oracle_encode_f16_array", "oracle_encode_bf16_array",
-                  "oracle_decode_f16_array", "oracle_decode_bf16_array", "oracle_round_tf32_array"):
+                  "oracle_decode_f16_array", "oracle_decode_bf16_array", "oracle_round_tf32_array",
+                  "oracle_encode_fp8_array", "oracle_decode_fp8_array"):
             getattr(lib, n).argtypes = [vp, vp, i64]
             getattr(lib, n).restype = None
         _lib = lib
@@ -70,6 +71,11 @@ def _as_input(dt, x):
         x = np.ascontiguousarray(x)
         if x.dtype != np.float32:
             raise TypeError("tf32 oracle inputs are float32 values")
+        return x
+    if dt == FP8:
+        x = np.ascontiguousarray(x)
+        if x.dtype != np.uint8:
+            raise TypeError("fp8 oracle inputs are uint8 E4M3 codes")
         return x
     x = np.ascontiguousarray(x)
     if x.dtype != np.uint16:
@@ -105,6 +111,21 @@ def decode_bf16(h):
     return y
 
 
+def encode_fp8(x):
+    """float32 -> fp8 E4M3 codes (nearest-even; NaN beyond 464 in magnitude)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, np.uint8)
+    _load().oracle_encode_fp8_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def decode_fp8(c):
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    y = np.empty(c.shape, np.float32)
+    _load().oracle_decode_fp8_array(_ptr(c), _ptr(y), c.size)
+    return y
+
+
 def round_tf32(x):
     """float32 -> float32 rounded to tf32 (10 fraction bits, nearest-even)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -119,6 +140,8 @@ def decode(dtype, x):
         return np.asarray(x, dtype=np.float64)
     if dt == TF32:
         return np.asarray(x, dtype=np.float32)
+    if dt == FP8:
+        return decode_fp8(x)
     return decode_f16(x) if dt == F16 else decode_bf16(x)
 
 
@@ -128,6 +151,8 @@ def encode(dtype, x):
         return np.asarray(x, dtype=np.float64)
     if dt == TF32:
         return np.asarray(x, dtype=np.float32)
+    if dt == FP8:
+        return encode_fp8(x)
     return encode_f16(x) if dt == F16 else encode_bf16(x)
 
 
@@ -160,8 +185,9 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
     """
     if isinstance(dtype, (list, tuple)):
         types = [dtype_code(t) for t in dtype]
-        if len(types) != len(Bs) + 1 or any(t in (F64, TF32) for t in types):
-            raise ValueError("one 16-bit type per GEMM and one for D")
+        if (len(types) != len(Bs) + 1 or any(t in (F64, TF32) for t in types)
+                or FP8 in (types[0], types[-1])):
+            raise ValueError("one 16-bit type per GEMM (fp8 after the first) and a 16-bit one for D")
         if len(set(types)) == 1:
             return cascade(types[0], A, Bs, rows, nthreads)
     else:
@@ -172,7 +198,7 @@ def cascade(dtype, A, Bs, rows=None, nthreads=None):
     if squeeze:
         A = A[None]
         Bs = [b[None] for b in Bs]
-    Bs = [_as_input(dt, b) for b in Bs]
+    Bs = [_as_input(dt if types is None else types[s], b) for s, b in enumerate(Bs)]
     batch, M, K = A.shape
     dims = [K] + [b.shape[2] for b in Bs]
     for s, b in enumerate(Bs):

@@ -13,7 +13,9 @@
  * evaluated independently for every batch and every row.  With a type per
  * stage (oracle_cascade_typed; the pages let each fused operator have its own
  * data type and layout), GEMM s takes X_s and B_s in type t_s and its result is
- * rounded into t_{s+1}, the next GEMM's operand type (t_S is D's type).  The pages fuse the
+ * rounded into t_{s+1}, the next GEMM's operand type (t_S is D's type).
+ * The 16-bit types serve everywhere; fp8 E4M3 (a format the pages do not
+ * name) may be the operand type of a GEMM after the first.  The pages fuse the
  * cascade so that the intermediate never leaves the chip; the value of the
  * cascade itself is the plain matrix product written out here.
  *
@@ -45,7 +47,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_BF16 = 1, OR_F64 = 2, OR_TF32 = 3 };
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F64 = 2, OR_TF32 = 3, OR_FP8 = 4 };
 
 static uint32_t f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
 static float bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
@@ -148,6 +150,54 @@ float oracle_round_tf32(float x)
 void oracle_round_tf32_array(const float* x, float* y, int64_t n)
 { for (int64_t i = 0; i < n; ++i) y[i] = oracle_round_tf32(x[i]); }
 
+/* ---------------------------------------------------------------------------
+ * fp8 E4M3 (the OCP 8-bit format without infinities): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 fraction bits; exponent field 0 holds the subnormals
+ * m * 2^-9, the all-ones exponent with fraction 111 is NaN, so the largest
+ * value is 1.75 * 2^8 = 448.  Encoding rounds to nearest-even on the quantum
+ * 2^(e-3) of the binade 2^e (2^-9 below 2^-6); a result above 448 (any
+ * value beyond 464, the half-way point to the odd 480, which would need the
+ * NaN code) becomes NaN.
+ * ------------------------------------------------------------------------- */
+float oracle_fp8_to_f32(uint8_t c)
+{
+    int sign = c >> 7, ef = (c >> 3) & 0xF, fr = c & 7;
+    float v;
+    if (ef == 0xF && fr == 7) return sign ? -NAN : NAN;
+    if (ef == 0) v = (float)fr * 0x1p-9f;
+    else v = ldexpf(1.0f + (float)fr / 8.0f, ef - 7);
+    return sign ? -v : v;
+}
+
+uint8_t oracle_f32_to_fp8(float x)
+{
+    uint32_t u = f32_bits(x);
+    uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+    if (isnan(x)) return sign | 0x7Fu;
+    double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);                   /* a = f 2^e, 0.5 <= f < 1: leading bit 2^(e-1) */
+    int lead = e - 1;
+    double quantum = ldexp(1.0, (lead >= -6 ? lead : -6) - 3);
+    double q = a / quantum;               /* exact: a power-of-two scaling */
+    double fl = floor(q), rem = q - fl;
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;
+    if (r > 448.0) return sign | 0x7Fu;   /* no infinity: NaN */
+    if (r < 0x1p-6) return sign | (uint8_t)(r / 0x1p-9);            /* subnormal (or the smallest normal) */
+    int re;
+    double rf = frexp(r, &re);            /* r = rf 2^re */
+    int ef = re - 1 + 7;
+    int fr = (int)((rf * 2.0 - 1.0) * 8.0);
+    return sign | (uint8_t)((ef << 3) | fr);
+}
+
+void oracle_encode_fp8_array(const float* x, uint8_t* y, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) y[i] = oracle_f32_to_fp8(x[i]); }
+void oracle_decode_fp8_array(const uint8_t* x, float* y, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) y[i] = oracle_fp8_to_f32(x[i]); }
+
 void oracle_encode_f16_array(const float* x, uint16_t* y, int64_t n)
 { for (int64_t i = 0; i < n; ++i) y[i] = oracle_f32_to_f16(x[i]); }
 void oracle_encode_bf16_array(const float* x, uint16_t* y, int64_t n)
@@ -161,6 +211,9 @@ static float dec16(int dtype, uint16_t h)
 { return dtype == OR_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h); }
 static uint16_t enc16(int dtype, float x)
 { return dtype == OR_F16 ? oracle_f32_to_f16(x) : oracle_f32_to_bf16(x); }
+/* the value of x rounded into a stage type (16-bit or fp8) */
+static float round_to(int dtype, float x)
+{ return dtype == OR_FP8 ? oracle_fp8_to_f32(oracle_f32_to_fp8(x)) : dec16(dtype, enc16(dtype, x)); }
 
 /* ---------------------------------------------------------------------------
  * One GEMM stage without the final rounding: acc[m][n] = sum_k X[m][k]*B[k][n],
@@ -297,9 +350,8 @@ static void* cascade_worker(void* arg)
                    exactly what the next stage consumes, and what D holds at
                    the end */
                 for (int64_t n = 0; n < N; ++n) {
-                    uint16_t h = enc16(j->st[s + 1], y[n]);
-                    if (s + 1 == j->nst) drow[n] = h;
-                    else y[n] = dec16(j->st[s + 1], h);
+                    if (s + 1 == j->nst) drow[n] = enc16(j->st[s + 1], y[n]);
+                    else y[n] = round_to(j->st[s + 1], y[n]);
                 }
                 void* t = xin; xin = xout; xout = t; x = (float*)xin;
             }
@@ -317,7 +369,8 @@ static int cascade_run(int dtype, const int* types, int nstages, const int64_t* 
     if (dtype != OR_F16 && dtype != OR_BF16 && dtype != OR_F64 && dtype != OR_TF32) return 2;
     if (types && dtype == OR_TF32) return 2;
     for (int s = 0; s <= nstages; ++s)
-        if (types && types[s] != OR_F16 && types[s] != OR_BF16) return 2;
+        if (types && types[s] != OR_F16 && types[s] != OR_BF16 &&
+            !(types[s] == OR_FP8 && s > 0 && s < nstages)) return 2;   /* fp8: operands of a later GEMM */
     for (int s = 0; s <= nstages; ++s) if (dims[s] <= 0) return 1;
     if (!rows) nrows = batch * M;
     if (nrows == 0) return 0;
@@ -341,6 +394,8 @@ static int cascade_run(int dtype, const int* types, int nstages, const int64_t* 
         if (!dec[s]) { rc = 3; goto done; }
         if (dtype == OR_TF32)
             for (int64_t i = 0; i < n; ++i) dec[s][i] = oracle_round_tf32(((const float*)B[s])[i]);
+        else if (base.st[s] == OR_FP8)
+            for (int64_t i = 0; i < n; ++i) dec[s][i] = oracle_fp8_to_f32(((const uint8_t*)B[s])[i]);
         else
             for (int64_t i = 0; i < n; ++i) dec[s][i] = dec16(base.st[s], ((const uint16_t*)B[s])[i]);
         base.Bf[s] = dec[s];

@@ -136,6 +136,25 @@ def _rne_bf16_bits(x):
     return (bits >> np.uint32(16)).astype(np.uint16)
 
 
+def _rne_fp8_codes(x):
+    """float64 values within +-448 -> nearest-even fp8 E4M3 codes (4
+    significant bits; fixed quantum 2^-9 below 2^-6)."""
+    x = np.asarray(x, np.float64)
+    if np.any(np.abs(x) > 448):
+        raise ValueError("fp8 inputs must lie within +-448")
+    a = np.abs(x)
+    m, e = np.frexp(a)                                   # a = m 2^e, leading bit 2^(e-1)
+    lead = np.where(a > 0, e - 1, -6)
+    qexp = np.maximum(lead, -6) - 3
+    q = np.ldexp(np.rint(np.ldexp(a, -qexp)), qexp)      # rounded magnitude
+    m2, e2 = np.frexp(q)
+    normal = q >= 2.0 ** -6
+    ef = np.where(normal, e2 - 1 + 7, 0)
+    fr = np.where(normal, np.rint((m2 * 2 - 1) * 8), np.rint(q / 2.0 ** -9))
+    code = (ef.astype(np.int64) << 3) + fr.astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
 def to_dtype(x, dtype):
     x = np.asarray(x, np.float64)
     shape = x.shape
@@ -148,6 +167,9 @@ def to_dtype(x, dtype):
                         np.empty(x.size, np.uint16)).reshape(shape)
     if dtype == "f64":
         return x.reshape(shape)
+    if dtype == "fp8":                  # E4M3 codes, nearest-even (inputs stay within +-448)
+        return _chunked(x.size, lambda a, b: _rne_fp8_codes(x[a:b]),
+                        np.empty(x.size, np.uint8)).reshape(shape)
     if dtype == "tf32":                 # float32 storage; the cascade rounds operands to tf32 itself
         return _chunked(x.size, lambda a, b: x[a:b].astype(np.float32),
                         np.empty(x.size, np.float32)).reshape(shape)

@@ -195,6 +195,48 @@ def test_tf32_rounding_points():
 
 
 # ----------------------------------------------------------------------------
+# fp8 E4M3
+# ----------------------------------------------------------------------------
+def test_fp8_decode_all_codes_match_torch():
+    c = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_fp8(c).astype(np.float64)
+    want = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want)) and np.isnan(got).sum() == 2
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch():
+    """Every float32 within +-480 on a fine grid (all ties of every binade
+    included: the grid step 2^-12 divides every fp8 half-quantum), plus
+    random float32 values across the whole range."""
+    grid = np.arange(-480 * 4096, 480 * 4096 + 1, dtype=np.float64) / 4096.0
+    rng = np.random.default_rng(9)
+    rnd = (rng.standard_normal(1 << 20) * np.exp(rng.uniform(-20, 8, 1 << 20))).astype(np.float64)
+    x = np.concatenate([grid, rnd, [2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -7 + 2.0 ** -10]]).astype(np.float32)
+    got = oracle.encode_fp8(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = got != want
+    assert not bad.any(), (x[bad][:5], got[bad][:5], want[bad][:5])
+
+
+def test_fp8_encode_is_nearest_even():
+    """Brute force: the code's value is a nearest finite fp8 value to x, and
+    of two equally near ones the one with an even code."""
+    vals = oracle.decode_fp8(np.arange(128, dtype=np.uint8)).astype(np.float64)[:127]   # +0 .. 448
+    rng = np.random.default_rng(10)
+    x = np.abs(rng.standard_normal(20000) * np.exp(rng.uniform(-12, 6, 20000)))
+    x = x[x < 464].astype(np.float32)
+    codes = oracle.encode_fp8(x)
+    d = np.abs(vals[None, :] - x.astype(np.float64)[:, None])
+    best = d.min(axis=1)
+    assert np.array_equal(d[np.arange(x.size), codes], best)
+    ties = (d == best[:, None]).sum(axis=1) == 2
+    assert np.all(codes[ties] % 2 == 0)
+
+
+# ----------------------------------------------------------------------------
 # One stage against exact rational arithmetic (tiny sizes)
 # ----------------------------------------------------------------------------
 def _exact(Xd, Bd):
@@ -336,6 +378,25 @@ def test_typed_intermediate_rounding_exact(types, lims, dims):
     assert rounded
     got = oracle.decode(types[-1], D).astype(np.float64)
     assert np.array_equal(got, x.astype(np.float64))
+
+
+@pytest.mark.parametrize("types", [("f16", "fp8", "f16"), ("bf16", "fp8", "bf16")])
+def test_fp8_stage_integers_exact(types):
+    """A 16-bit first GEMM feeding an fp8 second: small non-negative integers
+    make intermediates up to ~200, which fp8 holds only to 4 significant bits,
+    so they are really rounded (by the library cast, torch float8_e4m3fn); the
+    fp8 weights are ternary; every partial sum is an exact float32 integer."""
+    rng = np.random.default_rng(31)
+    A = synth.to_dtype(rng.integers(0, 4, (60, 64)), types[0])
+    B0 = synth.to_dtype(rng.integers(0, 2, (64, 64)), types[0])
+    B1 = synth.to_dtype(rng.integers(-1, 2, (64, 32)), "fp8")
+    D = oracle.cascade(list(types), A, [B0, B1])
+    x = oracle.decode(types[0], A).astype(np.int64) @ oracle.decode(types[0], B0).astype(np.int64)
+    assert x.max() > 64                                   # past 16: spacing 2 and more
+    xr = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert not np.array_equal(xr, x)
+    y = xr.astype(np.int64) @ oracle.decode("fp8", B1).astype(np.int64)
+    assert np.array_equal(oracle.decode(types[2], D).astype(np.float64), _np_round(types[2], y))
 
 
 def test_typed_rounding_points():
