@@ -24,15 +24,17 @@ sys.path.insert(0, ROOT)
 # bf16 passes, so its peak is the bf16 peak over the passes per product
 PEAK = {"f16": 2516.6e12, "bf16": 2516.6e12, "f64": 78.6e12, "tf32": 2516.6e12 / 3, "tf32x4": 2516.6e12 / 4}
 HBM = 8.0e12                                                   # B/s
-ELT = {"f16": 2, "bf16": 2, "f64": 8, "tf32": 4}
+ELT = {"f16": 2, "bf16": 2, "f64": 8, "tf32": 4, "fp8": 1}
 
 
-def workload_numbers(c):
+def workload_numbers(c, types=None):
+    """FLOP and algorithmic bytes (A + weights + D) of a step; types: one per
+    GEMM and D's, when the stages differ."""
     dims, b, M = c["dims"], c["batch"], c["M"]
+    t = types or [c["dtype"]] * len(dims)
     flop = 2.0 * b * M * sum(dims[s] * dims[s + 1] for s in range(len(dims) - 1))
-    e = ELT[c["dtype"]]
-    wbytes = b * sum(dims[s] * dims[s + 1] for s in range(len(dims) - 1)) * e
-    byts = b * M * dims[0] * e + wbytes + b * M * dims[-1] * e
+    wbytes = b * sum(dims[s] * dims[s + 1] * ELT[t[s]] for s in range(len(dims) - 1))
+    byts = b * M * dims[0] * ELT[t[0]] + wbytes + b * M * dims[-1] * ELT[t[-1]]
     return flop, byts
 
 
@@ -106,17 +108,20 @@ def main():
     dt = c["dtype"]
     types = args.types.split(",") if args.types else None
     if types:
-        if len(types) != len(c["dims"]) or any(t not in ("f16", "bf16") for t in types) or dt == "f64":
-            print("--types takes one of f16/bf16 per GEMM and one for D on a 16-bit workload", file=sys.stderr)
+        ok = (len(types) == len(c["dims"]) and dt != "f64" and types[0] != "fp8" and types[-1] != "fp8"
+              and all(t in ("f16", "bf16", "fp8") for t in types))
+        if not ok:
+            print("--types takes f16/bf16 per GEMM (fp8 for a later one) and f16/bf16 for D, on a 16-bit "
+                  "workload", file=sys.stderr)
             sys.exit(2)
         c["name"] += " types " + "/".join(types)
-    flop, algo_bytes = workload_numbers(c)
+    flop, algo_bytes = workload_numbers(c, types)
     print(f"[bench] config {args.config}: {c['name']}; generating inputs", file=sys.stderr, flush=True)
     A, Bs = synth.make_inputs(c, types=types)
     st_types = types or [dt] * len(c["dims"])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[dt]
+    set_bytes = A.nbytes + sum(b.nbytes for b in Bs) + c["batch"] * c["M"] * c["dims"][-1] * ELT[(types or [dt])[-1]]
     R = max(1, min(64, int(np.ceil(args.rotate_bytes / set_bytes))))
     A0 = cf.to_device(A, st_types[0])
     B0 = [cf.to_device(b, st_types[s]) for s, b in enumerate(Bs)]

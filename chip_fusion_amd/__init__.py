@@ -13,21 +13,21 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libb2b.so")
 
-F16, BF16, F64, TF32 = 0, 1, 2, 3
-DTYPES = {"f16": F16, "bf16": BF16, "f64": F64, "tf32": TF32}
+F16, BF16, F64, TF32, FP8 = 0, 1, 2, 3, 4
+DTYPES = {"f16": F16, "bf16": BF16, "f64": F64, "tf32": TF32, "fp8": FP8}
 # tf32 cascades take and return float32 tensors (the GEMMs round their operands to tf32)
 TORCH_DTYPES = {F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64, TF32: torch.float32}
 REMAP = {"auto": 0, "bpermute": 1, "permlane": 2, "lds": 3, "relabel": 4}
 FLAG_UNFUSED, FLAG_ORIENT_N, FLAG_MFMA_32X32, FLAG_TF32_EXACT = 1, 2, 4, 8
 SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x16": 3,
-          "f16_16x16x16": 4, "f64_16x16x4": 5}
+          "f16_16x16x16": 4, "f64_16x16x4": 5, "fp8_32x32x64": 6}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
           4: "out of memory"}
 EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_create_typed", "b2b_chain_run", "b2b_gemm_tune",
            "b2b_gemm_destroy", "b2b_status_string",
            "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_compile",
            "b2b_remap_execute", "b2b_remap_probe",
-           "b2b_mfma_probe")
+           "b2b_mfma_probe", "b2b_fp8_convert_probe")
 
 
 class B2BError(RuntimeError):
@@ -68,6 +68,7 @@ def lib():
         L.b2b_remap_compile.argtypes = [i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]
         L.b2b_remap_execute.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
         L.b2b_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
+        L.b2b_fp8_convert_probe.argtypes = [vp, vp, vp]
         for n in EXPORTS:
             if n not in ("b2b_status_string",):
                 getattr(L, n).restype = i32
@@ -256,19 +257,32 @@ def mfma_probe(shape, a, b, stream=None):
     returns the accumulator registers, [64, 4] ([64, 16] for 32x32x16) (b2b_mfma_probe)."""
     sh = SHAPES[shape] if isinstance(shape, str) else shape
     acc_dtype = torch.float64 if a.dtype == torch.float64 else torch.float32
-    nacc = 16 if sh in (SHAPES["f16_32x32x16"], SHAPES["bf16_32x32x16"]) else 4
+    nacc = 16 if sh in (SHAPES["f16_32x32x16"], SHAPES["bf16_32x32x16"], SHAPES["fp8_32x32x64"]) else 4
     c = torch.empty((64, nacc), dtype=acc_dtype, device=a.device)
     _check(lib().b2b_mfma_probe(sh, _ptr(a), _ptr(b), _ptr(c), _stream_ptr(stream)), "b2b_mfma_probe")
     return c
 
 
+def fp8_convert_probe(x, stream=None):
+    """The kernels' fp32 -> fp8 E4M3 conversion of 256 values (a float32
+    device tensor); returns the 256 codes as a uint8 device tensor."""
+    if x.numel() != 256 or x.dtype != torch.float32:
+        raise ValueError("256 float32 values expected")
+    y = torch.empty(256, dtype=torch.uint8, device=x.device)
+    _check(lib().b2b_fp8_convert_probe(_ptr(x), _ptr(y), _stream_ptr(stream)), "b2b_fp8_convert_probe")
+    return y
+
+
 def to_device(x, dtype, device="cuda"):
-    """numpy input (uint16 encodings, float64, or float32 for tf32) -> torch tensor of the dtype."""
+    """numpy input (uint16 encodings, float64, float32 for tf32, uint8 codes
+    for fp8) -> torch tensor of the dtype (fp8: uint8)."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     if dt == F64:
         return torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(device)
     if dt == TF32:
         return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+    if dt == FP8:
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint8)).to(device)
     t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TORCH_DTYPES[dt])
     return t.to(device)
 

@@ -46,6 +46,7 @@ struct b2b_gemm_plan {
     int dtype = 0, nst = 0, mode = 0, orn = 0;
     int tm = -1;                                 // type per stage (bit s: bf16), or -1: dtype throughout
     int passes = 0;                              // tf32: bf16 passes per product (3 or 4)
+    int f8 = 0, dtd = 0;                         // second GEMM in fp8 E4M3, D's type
     int64_t batch = 0, M = 0, dims[kMaxSt + 1] = {};
     // leading dimensions and batch strides (elements): [0] A, [1 + s] B_s, [nst + 1] D
     int64_t ld[kMaxSt + 2] = {}, bs[kMaxSt + 2] = {};
@@ -96,10 +97,24 @@ bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm 
     return lds <= 160 * 1024;
 }
 
+// Two GEMMs, the second in fp8: first GEMM's type dt, D's type dtd; K a
+// multiple of 32, N1 of 64, N2 of 32, each within the bound, weights in LDS.
+const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
+    const KernelDesc* best = nullptr;
+    for (const KernelDesc& d : b2b::registry()) {
+        if (!d.f8 || d.dtype != dt || d.dtd != dtd) continue;
+        if (dims[0] % 32 || dims[1] % 64 || dims[2] % 32) continue;
+        if (dims[0] > d.maxd || dims[1] > d.maxd || dims[2] > d.maxd) continue;
+        if (dims[0] * dims[1] * 2 + dims[1] * dims[2] > 160 * 1024) continue;
+        if (!best || d.maxd < best->maxd) best = &d;
+    }
+    return best;
+}
+
 const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
+        if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd) best = &d;
     }
     return best;
@@ -214,8 +229,11 @@ namespace {
 // or are null (dense).
 // tm >= 0: a 16-bit type per stage (bit s set: GEMM s in bf16; bit nst: D), dt
 // the type of bit 0; the cascade then runs on the 32x32x16 kernels.
+// f8_dtd >= 0: two GEMMs, the second in fp8 E4M3 (B1 one byte per element),
+// D in type f8_dtd.
 b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
-                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1) {
+                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1,
+                         int f8_dtd = -1) {
     if (!plan) return B2B_ERROR_INVALID_VALUE;
     *plan = nullptr;
     if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64 && dt != B2B_DTYPE_TF32)
@@ -235,9 +253,10 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     if (mode > b2bk::MODE_RELABEL) return B2B_ERROR_INVALID_VALUE;
     const int orn = (flags & B2B_FLAG_ORIENT_N) ? 1 : 0;
     if (orn && mode != b2bk::MODE_BPERM && mode != b2bk::MODE_LDS) return B2B_ERROR_INVALID_VALUE;
-    const bool typed = tm >= 0;
-    // typed and tf32 cascades are relabelled on the 32x32x16 kernels
-    if ((typed || tf32) && (orn || mode != b2bk::MODE_RELABEL)) return B2B_ERROR_NOT_SUPPORTED;
+    const bool typed = tm >= 0, f8 = f8_dtd >= 0;
+    // typed, tf32 and fp8 cascades are relabelled on the 32x32x16 kernels
+    if ((typed || tf32 || f8) && (orn || mode != b2bk::MODE_RELABEL)) return B2B_ERROR_NOT_SUPPORTED;
+    if (f8 && (nst != 2 || (flags & B2B_FLAG_UNFUSED))) return B2B_ERROR_NOT_SUPPORTED;
     const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0 || typed || tf32;
     if (s32 && (orn || dt == B2B_DTYPE_F64)) return B2B_ERROR_NOT_SUPPORTED;
     // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
@@ -252,11 +271,12 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         // operand i: A (rows M, width K), B_s (rows d[s], width d[s+1]), D (rows M, width d[nst])
         const int64_t rows = (i == 0 || i == n - 1) ? M : dims[i - 1];
         const int64_t width = i == 0 ? dims[0] : (i == n - 1 ? dims[nst] : dims[i]);
+        const int eo = (f8 && i == 2) ? 1 : es;    // the fp8 weights: one byte an element
         L[i] = Lin ? Lin[i] : width;
         if (L[i] < width) return B2B_ERROR_INVALID_VALUE;
-        if ((L[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
+        if ((L[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
         S[i] = Sin ? Sin[i] : rows * L[i];
-        if (S[i] < 0 || (S[i] * es) % 16) return B2B_ERROR_INVALID_VALUE;
+        if (S[i] < 0 || (S[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
     }
     if (batch > 1 && (S[0] == 0 || S[n - 1] < M * L[n - 1])) return B2B_ERROR_INVALID_VALUE;
 
@@ -265,6 +285,8 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     p->dtype = dt;
     p->tm = tm;
     p->passes = passes;
+    p->f8 = f8 ? 1 : 0;
+    p->dtd = f8 ? f8_dtd : dt;
     p->nst = nst;
     p->mode = mode;
     p->orn = orn;
@@ -277,7 +299,11 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
     std::memset(p->sched, 0, sizeof p->sched);
 
-    if (!p->unfused) {
+    if (!p->unfused && f8) {
+        p->fused = find_f8(dt, f8_dtd, dims);
+        p->mode = b2bk::MODE_RELABEL;
+        if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+    } else if (!p->unfused) {
         if (s32 || nst > 3) {
             // the fixed-width kernels cover up to three GEMMs
             if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
@@ -410,6 +436,16 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
                                     const int64_t* batch_stride, uint32_t flags) {
     if (plan) *plan = nullptr;
     if (!widths || !dtypes || nst < 1 || nst > kMaxSt) return B2B_ERROR_INVALID_VALUE;
+    // an fp8 second GEMM between 16-bit types
+    bool any_f8 = false;
+    for (int s = 0; s <= nst; ++s) any_f8 = any_f8 || dtypes[s] == B2B_DTYPE_FP8_E4M3;
+    if (any_f8) {
+        auto b16 = [](b2b_dtype_t t) { return t == B2B_DTYPE_F16 || t == B2B_DTYPE_BF16; };
+        if (nst != 2 || dtypes[1] != B2B_DTYPE_FP8_E4M3 || !b16(dtypes[0]) || !b16(dtypes[2]))
+            return B2B_ERROR_NOT_SUPPORTED;
+        return create_impl(plan, (int)dtypes[0], batch, M, nst, widths, ld, batch_stride, flags, true, -1,
+                           (int)dtypes[2]);
+    }
     bool same = true;
     int tm = 0;
     for (int s = 0; s <= nst; ++s) {
@@ -462,7 +498,11 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
     // every compiled kernel that computes this cascade under the plan's flags
     std::vector<const KernelDesc*> cands;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.dtype != p->dtype || d.nst != p->nst || d.tm != p->tm) continue;
+        if (d.dtype != p->dtype || d.nst != p->nst || d.tm != p->tm || d.f8 != p->f8) continue;
+        if (p->f8) {
+            if (d.dtd == p->dtd && find_f8(p->dtype, p->dtd, p->dims)) cands.push_back(&d);
+            continue;
+        }
         if (d.rtw) {
             if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims, p->tm, p->passes)) continue;
         } else {
@@ -569,7 +609,8 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     const KernelDesc* k = p->unfused ? p->stage_k[0] : p->fused;
     int64_t work = 0;
     for (int64_t w : p->work_bytes) work += w;
-    const char* mfma = p->dtype == B2B_DTYPE_F64    ? "f64_16x16x4"
+    const char* mfma = p->f8                        ? "32x32x16+f8_32x32x64"
+                       : p->dtype == B2B_DTYPE_F64  ? "f64_16x16x4"
                        : p->dtype == B2B_DTYPE_TF32 ? (p->passes == 4 ? "bf16x4_32x32x16" : "bf16x3_32x32x16")
                        : k->shape32                 ? "32x32x16"
                                                     : "16x16x32";
@@ -580,6 +621,7 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
         lds_bytes = (int)k->dyn_lds(d32);
     }
     std::string dts_s = dts[p->dtype];
+    if (p->f8) dts_s = std::string(dts[p->dtype]) + "/fp8/" + dts[p->dtd];
     if (p->tm >= 0) {
         // a type per stage: GEMM 0's, GEMM 1's, ..., then D's
         dts_s.clear();
@@ -717,12 +759,22 @@ b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, voi
     else if (shape == B2B_SHAPE_F16_32X32X16) dt = B2B_DTYPE_F16, s32 = 1;
     else if (shape == B2B_SHAPE_BF16_32X32X16) dt = B2B_DTYPE_BF16, s32 = 1;
     else if (shape == B2B_SHAPE_F64_16X16X4) dt = B2B_DTYPE_F64;
-    else return B2B_ERROR_NOT_SUPPORTED;
+    else if (shape == B2B_SHAPE_FP8_32X32X64) {
+        if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
+        hipLaunchKernelGGL(b2bk::mfma_f8_probe_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, c);
+        return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+    } else return B2B_ERROR_NOT_SUPPORTED;
     if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
     for (const b2b::MfmaProbeDesc& d : b2b::mfma_probe_registry())
         if (d.dtype == dt && d.shape32 == s32)
             return d.launch(a, b, c, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
     return B2B_ERROR_NOT_SUPPORTED;
+}
+
+b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, void* stream) {
+    if (!x || !y) return B2B_ERROR_INVALID_VALUE;
+    hipLaunchKernelGGL(b2bk::cvt_f8_probe_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, x, (int*)y);
+    return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
 }
 
 }  // extern "C"

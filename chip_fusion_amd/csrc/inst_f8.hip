@@ -1,0 +1,10 @@
+// Two-GEMM cascades with an fp8 (E4M3) second GEMM: (first GEMM's type, D's
+// type, max width, A tiles ahead).  K a multiple of 32, N1 of 64, N2 of 32.
+#include "registry.hpp"
+using namespace b2bk;
+B2B_F8_INSTANCE(DT_F16, DT_F16, 128, 1);
+B2B_F8_INSTANCE(DT_F16, DT_F16, 256, 0);
+B2B_F8_INSTANCE(DT_BF16, DT_BF16, 128, 1);
+B2B_F8_INSTANCE(DT_BF16, DT_BF16, 256, 0);
+B2B_F8_INSTANCE(DT_F16, DT_BF16, 128, 1);
+B2B_F8_INSTANCE(DT_BF16, DT_F16, 128, 1);

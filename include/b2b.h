@@ -48,7 +48,7 @@ typedef enum {
     B2B_DTYPE_F16 = 0,   /* IEEE binary16 inputs and outputs, float32 accumulation */
     B2B_DTYPE_BF16 = 1,  /* bfloat16 inputs and outputs, float32 accumulation */
     B2B_DTYPE_F64 = 2,   /* binary64 throughout */
-    B2B_DTYPE_TF32 = 3   /* the type of page 1's worked example: binary32 inputs,
+    B2B_DTYPE_TF32 = 3,  /* the type of page 1's worked example: binary32 inputs,
                             intermediates and outputs; every GEMM rounds both operands
                             to tf32 (10 fraction bits, nearest-even), multiplies them
                             and sums the products in binary32.  gfx950 has no tf32
@@ -63,6 +63,13 @@ typedef enum {
                             RELABEL.  Non-finite inputs (and values that round past
                             the largest tf32 value) give NaN where tf32 arithmetic
                             would give an infinity. */
+    B2B_DTYPE_FP8_E4M3 = 4 /* OCP fp8 E4M3 (bias 7, largest value 448, no infinities),
+                            one byte per element: only as the type of the second GEMM
+                            of a two-GEMM b2b_chain_create_typed cascade (its B1 and the
+                            intermediate, rounded to nearest-even on chip; results
+                            beyond 448 in magnitude after rounding give NaN).  The
+                            second GEMM runs on v_mfma_scale_f32_32x32x64_f8f6f4 with
+                            unit scales, products exact, sums in float32. */
 } b2b_dtype_t;
 
 typedef enum {
@@ -159,7 +166,7 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
                               uint32_t flags);
 
 /*
- * A cascade with a 16-bit type per stage (page 1: each fused operator may
+ * A cascade with a type per stage (page 1: each fused operator may
  * have its own data type, and the rearrangement relation follows the type):
  * GEMM s multiplies X_s by B_s in dtypes[s] with fp32 accumulation, and its
  * result is rounded to nearest-even into dtypes[s + 1], the next GEMM's
@@ -177,6 +184,11 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
  * for b2b_chain_create.  Runs with b2b_chain_run (or b2b_gemm_run for two or
  * three GEMMs).
  */
+/* An fp8 stage: dtypes = {t0, B2B_DTYPE_FP8_E4M3, tD} with t0, tD fp16 or bf16
+ * and nst = 2 -- the first GEMM in t0, its result rounded to fp8 and
+ * multiplied by the fp8 B1 on the fp8 instruction, D in tD; K a multiple of 32,
+ * N1 of 64, N2 of 32, each at most 256, B0 (2 bytes an element) and B1 (one)
+ * within 160 KB; fused only (NOT_SUPPORTED with B2B_FLAG_UNFUSED). */
 b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes, int64_t batch, int64_t M,
                                     int32_t nst, const int64_t* widths, const int64_t* ld,
                                     const int64_t* batch_stride, uint32_t flags);
@@ -229,7 +241,8 @@ typedef enum {
     B2B_SHAPE_F16_32X32X16 = 2,
     B2B_SHAPE_BF16_32X32X16 = 3,
     B2B_SHAPE_F16_16X16X16 = 4,
-    B2B_SHAPE_F64_16X16X4 = 5
+    B2B_SHAPE_F64_16X16X4 = 5,
+    B2B_SHAPE_FP8_32X32X64 = 6   /* b2b_mfma_probe only (no relation tables) */
 } b2b_shape_t;
 
 /*
@@ -302,12 +315,22 @@ b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, con
 /*
  * Runs one matrix instruction of `shape` on raw operand registers and writes
  * every lane's accumulator registers (a probe of the layout catalogue).
- *   a, b  device, 64 lanes x operand elements (8 x 16-bit, or 1 x fp64) each
+ *   a, b  device, 64 lanes x operand elements (8 x 16-bit, 1 x fp64, or
+ *         32 x fp8 E4M3 bytes) each
  *   c     device, 64 lanes x accumulator elements (4 x float32, 16 x float32 for
- *         32x32x16, or 4 x fp64)
- * Accumulators start at zero.  Shapes: 16x16x32 and 32x32x16 f16/bf16, 16x16x4 f64.
+ *         32x32x16 and 32x32x64, or 4 x fp64)
+ * Accumulators start at zero.  Shapes: 16x16x32 and 32x32x16 f16/bf16, 16x16x4
+ * f64, 32x32x64 fp8 (E4M3 operands, unit scales).
  */
 b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream);
+
+/*
+ * The kernels' fp32 -> fp8 E4M3 conversion (v_cvt_pk_fp8_f32, used to round
+ * the intermediate of an fp8 second GEMM) applied to 256 values: a probe of
+ * its rounding against the format's definition.
+ *   x  device, 256 float32;  y  device, 256 bytes (the codes in order)
+ */
+b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, void* stream);
 
 #ifdef __cplusplus
 }

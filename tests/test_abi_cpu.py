@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     txt = open(os.path.join(ROOT, "include", "b2b.h")).read()
-    return sorted(set(re.findall(r"\b(b2b_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(b2b_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_symbol():
@@ -294,6 +294,51 @@ def test_typed_rejects_tf32_mix():
     assert st == 2
     st, info = _typed((3, 3, 3), (128, 128, 128))
     assert st == 0 and info["dtype"] == "tf32"
+
+
+@pytest.mark.parametrize("dtypes,widths,expect", [
+    ((0, 4, 0), (128, 128, 128), dict(dtype="f16/fp8/f16", mfma="32x32x16+f8_32x32x64",
+                                      lds_bytes=str(128 * 128 * 2 + 128 * 128 + 8 * 4096))),
+    ((1, 4, 1), (256, 128, 256), dict(dtype="bf16/fp8/bf16", lds_bytes=str(256 * 128 * 2 + 128 * 256 + 8 * 4096))),
+    ((0, 4, 1), (96, 64, 32), dict(dtype="f16/fp8/bf16", launches="1")),
+])
+def test_fp8_plan_selection(dtypes, widths, expect):
+    st, info = _typed(dtypes, widths)
+    assert st == 0
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
+
+
+@pytest.mark.parametrize("dtypes,widths,flags,status", [
+    ((0, 4, 0), (128, 96, 128), 0, 2),                 # N1 a multiple of 64
+    ((0, 4, 0), (256, 256, 256), 0, 2),                # 192 KB of weights
+    ((4, 0, 0), (128, 128, 128), 0, 2),                # fp8 is a later GEMM's type
+    ((0, 0, 4), (128, 128, 128), 0, 2),                # not D's
+    ((0, 4, 0, 0), (128, 128, 128, 64), 0, 2),         # two GEMMs
+    ((0, 4, 0), (128, 128, 128), 1, 2),                # fused only
+    ((0, 4, 0), (128, 128, 128), 2 << 4, 2),           # relabelled only
+    ((0, 4, 0), (128, 128, 144), 0, 2),                # N2 a multiple of 32
+])
+def test_fp8_rejects(dtypes, widths, flags, status):
+    st, _ = _typed(dtypes, widths, flags)
+    assert st == status
+
+
+def test_fp8_weights_leading_dimension_in_bytes():
+    """B1 is one byte an element: its leading dimension needs 16 bytes, not 32."""
+    h = ctypes.c_void_p(123)
+    ts = (ctypes.c_int32 * 3)(0, 4, 0)
+    w = (ctypes.c_int64 * 3)(128, 128, 32)
+    ld = (ctypes.c_int64 * 4)(128, 128, 48, 32)
+    assert cf.lib().b2b_chain_create_typed(ctypes.byref(h), ts, 1, 64, 2, w, ld, None, 0) == 0
+    cf.lib().b2b_gemm_destroy(h)
+    ld2 = (ctypes.c_int64 * 4)(128, 136, 48, 32)         # B0 (16-bit) needs multiples of 8 elements
+    h2 = ctypes.c_void_p(123)
+    assert cf.lib().b2b_chain_create_typed(ctypes.byref(h2), ts, 1, 64, 2, w, ld2, None, 0) == 0
+    cf.lib().b2b_gemm_destroy(h2)
+    ld3 = (ctypes.c_int64 * 4)(128, 128, 40, 32)         # 40 bytes: not a multiple of 16
+    h3 = ctypes.c_void_p(123)
+    assert cf.lib().b2b_chain_create_typed(ctypes.byref(h3), ts, 1, 64, 2, w, ld3, None, 0) == 1
 
 
 def test_gemm_run_rejects_chain_plans():
