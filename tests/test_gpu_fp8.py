@@ -111,3 +111,32 @@ def test_fp8_second_gemm_integers_exact(types):
     assert x.max() > 64
     got, _ = _run(types, A, [B0, B1])
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+
+
+def test_fp8_padded_and_broadcast():
+    types, M, batch, widths = ("f16", "fp8", "f16"), 300, 3, (64, 128, 96)
+    _flush(f"fp8 strided widths={widths}")
+    A, Bs = _inputs(types, batch, M, widths)
+    Bs = [Bs[0], Bs[1].copy()]
+    Bs[1][:] = Bs[1][0]                       # B1 broadcast to every batch
+    lda, ldb0, ldb1, ldd = widths[0] + 8, widths[1] + 16, widths[2] + 32, widths[2] + 8
+    sA, sB0, sD = M * lda + 8, widths[0] * ldb0 + 24, M * ldd + 16
+
+    def padded(x, b, rows, cols, ld, stride, dt, fill):
+        buf = torch.full(((b - 1) * stride + rows * ld + 64,), fill, dtype=dt, device="cuda")
+        buf.as_strided((b, rows, cols), (stride, ld, 1)).copy_(x)
+        return buf
+
+    Ad = padded(cf.to_device(A, "f16"), batch, M, widths[0], lda, sA, torch.float16, float("nan"))
+    B0d = padded(cf.to_device(Bs[0], "f16"), batch, widths[0], widths[1], ldb0, sB0, torch.float16, float("nan"))
+    B1d = padded(cf.to_device(Bs[1][:1], "fp8"), 1, widths[1], widths[2], ldb1, 0, torch.uint8, 0x7F)
+    Dd = torch.full(((batch - 1) * sD + M * ldd + 64,), float("nan"), dtype=torch.float16, device="cuda")
+    p = cf.Chain(list(types), batch, M, list(widths), ld=[lda, ldb0, ldb1, ldd], batch_stride=[sA, sB0, 0, sD])
+    p.run(Ad, B0d, B1d, D=Dd)
+    torch.cuda.synchronize()
+    p.close()
+    view = Dd.as_strided((batch, M, widths[2]), (sD, ldd, 1))
+    assert_close("f16", cf.to_host(view.contiguous()), oracle.cascade(list(types), A, Bs), "fp8 strided")
+    mask = torch.ones_like(Dd, dtype=torch.bool)
+    mask.as_strided((batch, M, widths[2]), (sD, ldd, 1)).fill_(False)
+    assert torch.isnan(Dd[mask]).all().item(), "writes outside the output windows"

@@ -47,3 +47,45 @@ def test_tune(cfg, M, batch, kw, expect):
     torch.cuda.synchronize()
     p.close()
     assert np.array_equal(cf.to_host(D2), tuned), "the plan runs the kernel the tuning kept"
+
+
+@pytest.mark.parametrize("types,widths", [(("f16", "bf16", "f16"), (128, 128, 128)),
+                                          (("f16", "fp8", "f16"), (128, 128, 128)),
+                                          (("tf32", "tf32", "tf32"), (128, 128, 64))])
+def test_tune_typed_fp8_tf32(types, widths):
+    """Tuning a plan with a type per stage, an fp8 second GEMM or tf32 keeps a
+    kernel of that same kind (its result equals the planned kernel's within
+    the tolerance and the plan then reproduces it)."""
+    M, batch = 1024, 2
+    _flush(f"tune {types} {widths}")
+    if types[0] == "tf32":
+        A = synth.tensor(5, 0, (batch, M, widths[0]), "tf32", "normal")
+        Bs = [synth.tensor(5, 1 + s, (batch, widths[s], widths[s + 1]), "tf32", "normal", widths[s] ** -0.5)
+              for s in range(2)]
+        p = cf.Chain("tf32", batch, M, list(widths))
+        Ad = torch.from_numpy(A).cuda()
+        Bd = [torch.from_numpy(b).cuda() for b in Bs]
+        D = torch.full((batch, M, widths[-1]), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        A = synth.tensor(5, 0, (batch, M, widths[0]), types[0], "normal")
+        Bs = [synth.tensor(5, 1 + s, (batch, widths[s], widths[s + 1]), types[s], "normal", widths[s] ** -0.5)
+              for s in range(2)]
+        p = cf.Chain(list(types), batch, M, list(widths))
+        Ad = cf.to_device(A, types[0])
+        Bd = [cf.to_device(b, types[s]) for s, b in enumerate(Bs)]
+        D = nan_output(types[-1], batch, M, widths[-1])
+    before = p.info().split(" grid=")[0]
+    p.tune([(Ad, Bd, D)], reps=3)
+    after = p.info().split(" grid=")[0]
+    assert after == before, (before, after)      # one kernel of the kind: it stays
+    tuned = cf.to_host(D)
+    if types[0] == "tf32":
+        ref = oracle.cascade("tf32", A, Bs).astype(np.float64)
+        assert np.linalg.norm(tuned - ref) / np.linalg.norm(ref) < 1e-3
+    else:
+        assert_close(types[-1], tuned, oracle.cascade(list(types), A, Bs), f"tune {types}")
+    D2 = torch.full_like(D, float("nan"))
+    p.run(Ad, *Bd, D=D2)
+    torch.cuda.synchronize()
+    p.close()
+    assert np.array_equal(cf.to_host(D2), tuned)

@@ -106,3 +106,37 @@ def test_typed_integer_exact(types, widths, lims, kw):
     assert not np.array_equal(oracle.decode(types[-1], ref), oracle.decode(types[0], other))
     got, _ = _run(types, A, Bs, **kw)
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+
+
+def test_typed_padded_and_broadcast():
+    types, M, batch, widths = ("bf16", "f16", "f16", "bf16"), 300, 3, (64, 96, 128, 32)
+    _flush(f"typed strided {types} widths={widths}")
+    A, Bs = _normal_inputs(types, batch, M, widths)
+    Bs = [b.copy() for b in Bs]
+    Bs[1][:] = Bs[1][0]                       # B_1 broadcast to every batch
+    nst = 3
+    lda, ldd = widths[0] + 8, widths[-1] + 16
+    ldb = [widths[s + 1] + 8 * (s + 1) for s in range(nst)]
+    sA, sD = M * lda + 8, M * ldd + 24
+    sB = [widths[s] * ldb[s] + 16 for s in range(nst)]
+    sB[1] = 0
+
+    def padded(x, b, rows, cols, ld, stride, t):
+        dt = cf.TORCH_DTYPES[cf.DTYPES[t]]
+        buf = torch.full(((b - 1) * stride + rows * ld + 64,), float("nan"), dtype=dt, device="cuda")
+        buf.as_strided((b, rows, cols), (stride, ld, 1)).copy_(cf.to_device(x, t))
+        return buf
+
+    Ad = padded(A, batch, M, widths[0], lda, sA, types[0])
+    Bd = [padded(Bs[s] if s != 1 else Bs[s][:1], batch if s != 1 else 1, widths[s], widths[s + 1], ldb[s], sB[s],
+                 types[s]) for s in range(nst)]
+    Dd = torch.full(((batch - 1) * sD + M * ldd + 64,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    p = cf.Chain(list(types), batch, M, list(widths), ld=[lda] + ldb + [ldd], batch_stride=[sA] + sB + [sD])
+    p.run(Ad, *Bd, D=Dd)
+    torch.cuda.synchronize()
+    p.close()
+    view = Dd.as_strided((batch, M, widths[-1]), (sD, ldd, 1))
+    assert_close(types[-1], cf.to_host(view.contiguous()), oracle.cascade(list(types), A, Bs), "typed strided")
+    mask = torch.ones_like(Dd, dtype=torch.bool)
+    mask.as_strided((batch, M, widths[-1]), (sD, ldd, 1)).fill_(False)
+    assert torch.isnan(Dd[mask]).all().item(), "writes outside the output windows"
