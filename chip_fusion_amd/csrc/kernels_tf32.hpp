@@ -142,12 +142,12 @@ __device__ inline void tf32_stage_weights(unsigned char* lds, const GenMat (&mh)
 // A of one wave's 32 rows in natural K order: K-step j is a[2j] (k = 16j +
 // 8(l/32) + 0..3) and a[2j+1] (+4..7) of row l%32.  Loads past K go through
 // the empty resource (zeros, no memory access).
-template <class C>
+template <class C, int J0 = 0, int J1 = C::MKS>
 __device__ __forceinline__ void tf32_load_a(u4_t (&a)[2 * C::MKS], __amdgpu_buffer_rsrc_t rs,
                                             __amdgpu_buffer_rsrc_t none, int64_t lda, int ks, int lane) {
     const int m = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < C::MKS; ++j) {
+    for (int j = J0; j < J1; ++j) {
         const auto src = j < ks ? rs : none;
         const uint32_t off = (uint32_t)((m * lda + 16 * j + 8 * h) * 4);
         a[2 * j] = ld128(src, off);
@@ -332,13 +332,16 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
             u4_t xh[C::MKS], xl[C::MKS];
 #pragma unroll
             for (int j = 0; j < C::MKS; ++j) tf32_operand(a[2 * j], a[2 * j + 1], xh[j], xl[j]);
-            // this tile's A is consumed: the next one's loads go out -- at
-            // once for a single GEMM, else before the last GEMM, when the
-            // split operands of the first are no longer live
+            // this tile's A is consumed: the next one's loads go out -- all
+            // at once where the registers allow (a single GEMM, or one wave
+            // per SIMD), else a quarter now and the rest before the last
+            // GEMM, when the split operands of the first are no longer live
+            constexpr bool EARLY = C::NST == 1 || C::WAVES == 4;
             auto issue_next = [&]() __attribute__((always_inline)) {
-                tf32_load_a<C>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                tf32_load_a<C, C::MKS / 4, C::MKS>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
             };
-            if constexpr (C::NST == 1) issue_next();
+            tf32_load_a<C, 0, C::MKS / 4>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+            if constexpr (EARLY) issue_next();
 
             const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
             const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 4,
@@ -370,7 +373,7 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
                         tf32_gemm_kouter<C>(lds, fh[S], fl[S], oBh, oBl, d[S] / 16, d[S + 1] / 32, to_ops(oAh, oAl));
                 });
                 constexpr int L = C::NST - 1;
-                issue_next();
+                if constexpr (!EARLY) issue_next();
                 if constexpr (L % 2 == 1) tf32_gemm<C>(lds, fh[L], fl[L], oAh, oAl, d[L] / 16, dn / 32, to_d);
                 else tf32_gemm<C>(lds, fh[L], fl[L], oBh, oBl, d[L] / 16, dn / 32, to_d);
             }
