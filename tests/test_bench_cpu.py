@@ -41,3 +41,22 @@ def test_more_than_one_gpu_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_workload_numbers_per_stage_types():
+    """An fp8 second GEMM counts its weights at one byte an element; tf32 at four."""
+    c = dict(synth.CONFIGS[2])
+    flop, byts = bench.workload_numbers(c, ["f16", "fp8", "f16"])
+    assert flop == EXPECTED[2][0]
+    assert byts == 64 * (2 * 4096 * 128 + 2 * 128 * 128 + 1 * 128 * 128 + 2 * 4096 * 128)
+    c["dtype"] = "tf32"
+    assert bench.workload_numbers(c)[1] == 2 * EXPECTED[2][1]
+
+
+@pytest.mark.parametrize("args", [["--types", "fp8,f16,f16"], ["--types", "f16,f16"], ["--types", "f16,f16,fp8"],
+                                  ["--config", "4", "--types", "f64,f64,f64"], ["--tf32-exact"]])
+def test_bad_type_options_refused(args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2, r.stderr[-500:]
+    assert r.stdout.strip() == ""
