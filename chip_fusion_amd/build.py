@@ -24,15 +24,24 @@ def library_path():
     return LIB
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed: what the
+    compiler sees, so that an edited comment does not count as a new kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest():
-    """sha256 over the kernel and host sources the library is built from (used
-    to tell whether stored profiler counters still describe the current kernels)."""
+    """sha256 over the code (comments and layout aside) of the kernel and host
+    sources the library is built from, used to tell whether stored profiler
+    counters still describe the current kernels."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
         if f.endswith((".hip", ".hpp", ".cpp")):
             h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+            h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

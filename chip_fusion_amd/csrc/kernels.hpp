@@ -121,8 +121,10 @@ __device__ inline u4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline u2_t ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
-// Cache policy of the streaming accesses: A is read once and D written once,
-// so both go non-temporal (nt) and do not displace the weights from the caches.
+// Cache policy of D's stores: D is written once, so it goes non-temporal (nt)
+// and does not displace the weights from the caches.  A's loads keep the
+// default policy: non-temporal A loads measured no better on the two-GEMM
+// fp16 workload and 1-3 % slower on the three-GEMM and fp64 ones.
 constexpr int kStreamPolicy = 2;
 
 __device__ inline void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, u4_t v) {

@@ -363,3 +363,14 @@ def test_tune_rejects_bad_arguments():
     assert L.b2b_gemm_tune(h, 0, As, ptrs, Ds, None, 5) == 1
     assert L.b2b_gemm_tune(h, 1, As, ptrs, Ds, None, 0) == 1
     L.b2b_gemm_destroy(h)
+
+
+def test_source_digest_ignores_comments_only():
+    """The digest that ties stored profiler counters to the kernels reads code,
+    not comments or layout."""
+    from chip_fusion_amd import build
+    a = "int f(int x) {\n  // doubled\n  return 2 * x; /* all */\n}\n"
+    b = "int f(int x)\n{ return 2 * x;   // twice\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert build._code_only(a) == build._code_only(b) != build._code_only(c)
+    assert len(build.source_digest()) == 16
