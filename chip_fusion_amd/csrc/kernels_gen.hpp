@@ -59,11 +59,11 @@ template <> struct Ty32<DT_BF16> {
 // (page 1 lets each fused operator have its own data type): bit s set means
 // bf16, clear fp16, for the operands of GEMM s (A, B_s and the intermediate
 // rounded for it) and, at bit NST, for D.  DT_ is then the type of bit 0.
-template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1>
+template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8>
 struct GenCfg {
     static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_, TM = TM_;
     static constexpr int stype(int s) { return TM < 0 ? DT : (((TM >> s) & 1) ? DT_BF16 : DT_F16); }
-    static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
+    static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
     static constexpr int LDS_MAX = 160 * 1024;
     static_assert(DT != DT_F64, "the 32x32x16 instruction exists for 16-bit types");
@@ -95,11 +95,11 @@ __host__ __device__ inline int64_t gen_weight_bytes(const int32_t* d, int nst) {
     for (int s = 0; s < nst; ++s) b += (int64_t)d[s] * d[s + 1] * 2;
     return b;
 }
-__host__ __device__ inline bool gen_stage_d(const int32_t* d, int nst) {
-    return gen_weight_bytes(d, nst) + 8 * 4096 <= 160 * 1024;
+__host__ __device__ inline bool gen_stage_d(const int32_t* d, int nst, int waves = 8) {
+    return gen_weight_bytes(d, nst) + waves * 4096 <= 160 * 1024;
 }
-__host__ __device__ inline int64_t gen_lds_bytes(const int32_t* d, int nst) {
-    return gen_weight_bytes(d, nst) + (gen_stage_d(d, nst) ? 8 * 4096 : 0);
+__host__ __device__ inline int64_t gen_lds_bytes(const int32_t* d, int nst, int waves = 8) {
+    return gen_weight_bytes(d, nst) + (gen_stage_d(d, nst, waves) ? waves * 4096 : 0);
 }
 
 // Per-lane constants of the weight fragments of one matrix: fragment
@@ -327,7 +327,7 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
     }
     const int ks0 = d[0] / 16, dn = d[C::NST];
     // the wave's D staging region follows the weights, where LDS allows
-    const int stg = gen_stage_d(d, C::NST) ? off + wave * 4096 : -1;
+    const int stg = gen_stage_d(d, C::NST, C::WAVES) ? off + wave * 4096 : -1;
     constexpr bool REL = C::MODE == MODE_RELABEL;
     GenFrag fr[C::NST];
 #pragma unroll

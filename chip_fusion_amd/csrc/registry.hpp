@@ -104,13 +104,13 @@ KernelDesc describe_gen() {
     d.maxd = C::MAXD;
     d.tm = C::TM;
     d.fn = (const void*)&b2bk::gen_kernel<C>;
-    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST); };
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST, C::WAVES); };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
         // dynamic LDS up to the whole 160 KB of a CU
         static const hipError_t attr = hipFuncSetAttribute(
             (const void*)&b2bk::gen_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
         if (attr != hipSuccess) return attr;
-        const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST);
+        const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST, C::WAVES);
         hipLaunchKernelGGL(b2bk::gen_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };

@@ -94,7 +94,8 @@ def _info(**kw):
     (dict(dtype=2, K=8, N1=128, N2=16, N3=64), dict(mfma="f64_16x16x4", dims="8x128x16x64")),
     # the configurations' widths keep their fixed-width kernels unless asked
     (dict(), dict(mfma="16x16x32", remap="relabel")),
-    (dict(flags=4), dict(mfma="32x32x16", remap="relabel", lds_bytes=str(16384 + 32768))),
+    # four waves (two workgroups a CU): 4 x 4 KB of D staging
+    (dict(flags=4), dict(mfma="32x32x16", remap="relabel", waves="4", lds_bytes=str(16384 + 16384))),
     (dict(K=128, N1=128, N2=128, N3=64, flags=4 | (2 << 4)), dict(mfma="32x32x16", remap="permlane")),
     # the 256-wide cascade (256 KB of weights) keeps its column-split kernel
     (dict(dtype=1, K=256, N1=256, N2=256), dict(mfma="16x16x32", remap="lds")),
