@@ -99,6 +99,15 @@ bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm 
 
 // Two GEMMs, the second in fp8: first GEMM's type dt, D's type dtd; K a
 // multiple of 32, N1 of 64, N2 of 32, each within the bound, weights in LDS.
+// Four-wave instances rank first where two of their workgroups fit a CU's
+// LDS, then eight-wave ones, then four-wave ones alone on a CU.
+int wave_rank(const KernelDesc& d, const int64_t* dims, int nst) {
+    int32_t d32[kMaxSt + 1] = {};
+    for (int i = 0; i <= nst; ++i) d32[i] = (int32_t)dims[i];
+    const bool pair = d.waves == 4 && d.dyn_lds && 2 * d.dyn_lds(d32) <= 160 * 1024;
+    return d.waves == 4 ? (pair ? 0 : 2) : 1;
+}
+
 const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
@@ -106,7 +115,9 @@ const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
         if (dims[0] % 32 || dims[1] % 64 || dims[2] % 32) continue;
         if (dims[0] > d.maxd || dims[1] > d.maxd || dims[2] > d.maxd) continue;
         if (dims[0] * dims[1] * 2 + dims[1] * dims[2] > 160 * 1024) continue;
-        if (!best || d.maxd < best->maxd) best = &d;
+        if (!best || d.maxd < best->maxd ||
+            (d.maxd == best->maxd && wave_rank(d, dims, 2) < wave_rank(*best, dims, 2)))
+            best = &d;
     }
     return best;
 }
@@ -116,15 +127,11 @@ const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
 // (twice the tiles in flight per CU, measured 3 % faster), else the eight-wave one.
 const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0) {
     const KernelDesc* best = nullptr;
-    int32_t d32[kMaxSt + 1] = {};
-    for (int i = 0; i <= nst; ++i) d32[i] = (int32_t)dims[i];
-    auto rank = [&](const KernelDesc& d) {
-        const bool pair = d.waves == 4 && d.dyn_lds && 2 * d.dyn_lds(d32) <= 160 * 1024;
-        return d.waves == 4 ? (pair ? 0 : 2) : 1;
-    };
     for (const KernelDesc& d : b2b::registry()) {
         if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
-        if (!best || d.maxd < best->maxd || (d.maxd == best->maxd && rank(d) < rank(*best))) best = &d;
+        if (!best || d.maxd < best->maxd ||
+            (d.maxd == best->maxd && wave_rank(d, dims, nst) < wave_rank(*best, dims, nst)))
+            best = &d;
     }
     return best;
 }

@@ -24,22 +24,21 @@ namespace b2bk {
 
 typedef int i8v_t __attribute__((ext_vector_type(8)));
 
-constexpr int WAVES_OF_F8 = 8;
-
 // DT0_: type of A, B0 and the first GEMM (DT_F16 / DT_BF16); DTD_: type of D;
-// MAXD_: bound on K, N1, N2; PF_: A tiles fetched ahead (0 or 1).  The
-// members are those the 32x32x16 run-time-width building blocks read.
-template <int DT0_, int DTD_, int MAXD_, int PF_>
+// MAXD_: bound on K, N1, N2; PF_: A tiles fetched ahead (0 or 1); WAVES_: 8
+// (256-row tiles) or 4 (128-row tiles, two workgroups a CU where LDS allows).
+// The members are those the 32x32x16 run-time-width building blocks read.
+template <int DT0_, int DTD_, int MAXD_, int PF_, int WAVES_ = 8>
 struct F8Cfg {
     static constexpr int DT = DT0_, DTD = DTD_, NST = 2, MAXD = MAXD_, MODE = MODE_RELABEL, PF = PF_;
-    static constexpr int WAVES = WAVES_OF_F8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
+    static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32, MKS8 = MAXD / 64;
     static constexpr int LDS_MAX = 160 * 1024;
     static constexpr int stype(int s) { return s == 0 ? DT : DTD; }   // s == 2: D (the fp8 stage is not 16-bit)
     static_assert(DT != DT_F64 && DTD != DT_F64 && MAXD % 64 == 0 && (PF == 0 || PF == 1), "config");
     // the 16-bit weights (B0 alone) for gen_stage_weights
     struct Stage0 {
-        static constexpr int NST = 1, THREADS = 64 * WAVES_OF_F8;
+        static constexpr int NST = 1, THREADS = 64 * WAVES_;
     };
 };
 
@@ -47,9 +46,11 @@ struct F8Cfg {
 __host__ __device__ inline int64_t f8_weight_bytes(const int32_t* d) {
     return (int64_t)d[0] * d[1] * 2 + (int64_t)d[1] * d[2];
 }
-__host__ __device__ inline bool f8_stage_d(const int32_t* d) { return f8_weight_bytes(d) + 8 * 4096 <= 160 * 1024; }
-__host__ __device__ inline int64_t f8_lds_bytes(const int32_t* d) {
-    return f8_weight_bytes(d) + (f8_stage_d(d) ? 8 * 4096 : 0);
+__host__ __device__ inline bool f8_stage_d(const int32_t* d, int waves = 8) {
+    return f8_weight_bytes(d) + waves * 4096 <= 160 * 1024;
+}
+__host__ __device__ inline int64_t f8_lds_bytes(const int32_t* d, int waves = 8) {
+    return f8_weight_bytes(d) + (f8_stage_d(d, waves) ? waves * 4096 : 0);
 }
 
 // fp8 x fp8 -> fp32 on the 32x32x64 instruction, E4M3 operands, scales 2^0
@@ -115,7 +116,7 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
     m0[0].init(0, d0, d1);
     const int off1 = d0 * d1 * 2;                       // B1 fragments follow B0
     const int32_t dd[3] = {d0, d1, d2};
-    const int stg = f8_stage_d(dd) ? off1 + d1 * d2 + wave * 4096 : -1;
+    const int stg = f8_stage_d(dd, C::WAVES) ? off1 + d1 * d2 + wave * 4096 : -1;
     GenFrag fr0;
     fr0.init(m0[0], false, lane);
     const int ks0 = d0 / 16, ks8 = d1 / 64, nt2 = d2 / 32;

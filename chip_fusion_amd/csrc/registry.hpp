@@ -170,12 +170,12 @@ KernelDesc describe_f8() {
     d.f8 = 1;
     d.dtd = C::DTD;
     d.fn = (const void*)&b2bk::f8_kernel<C>;
-    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::f8_lds_bytes(w); };
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::f8_lds_bytes(w, C::WAVES); };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
         static const hipError_t attr = hipFuncSetAttribute(
             (const void*)&b2bk::f8_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
         if (attr != hipSuccess) return attr;
-        const size_t shm = (size_t)b2bk::f8_lds_bytes(a.dims);
+        const size_t shm = (size_t)b2bk::f8_lds_bytes(a.dims, C::WAVES);
         hipLaunchKernelGGL(b2bk::f8_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };
@@ -277,9 +277,11 @@ ProbeDesc describe_probe() {
 #define B2B_GEN_INSTANCE(...)                                                          \
     static ::b2b::Registrar B2B_CAT(b2b_gen_reg_, __LINE__)(                           \
         ::b2b::describe_gen<::b2bk::GenCfg<__VA_ARGS__>>())
-// B2B_GEN_TYPED(stages, max width, A tiles ahead, type mask): relabelled, a type per stage
-#define B2B_GEN_TYPED(NST, MAXD, PF, TM)                                                \
-    B2B_GEN_INSTANCE(((TM) & 1) ? ::b2bk::DT_BF16 : ::b2bk::DT_F16, NST, MAXD, ::b2bk::MODE_RELABEL, PF, TM)
+// B2B_GEN_TYPED(stages, max width, A tiles ahead, type mask[, waves]): relabelled, a type per stage
+#define B2B_GEN_TYPED(NST, MAXD, PF, ...)                                               \
+    B2B_GEN_INSTANCE(((B2B_FIRST(__VA_ARGS__)) & 1) ? ::b2bk::DT_BF16 : ::b2bk::DT_F16, NST, MAXD, \
+                     ::b2bk::MODE_RELABEL, PF, __VA_ARGS__)
+#define B2B_FIRST(a, ...) a
 // B2B_TF32_INSTANCE(stages, max width, passes)
 #define B2B_TF32_INSTANCE(...)                                                         \
     static ::b2b::Registrar B2B_CAT(b2b_tf32_reg_, __LINE__)(                          \

@@ -298,8 +298,9 @@ def test_typed_rejects_tf32_mix():
 
 
 @pytest.mark.parametrize("dtypes,widths,expect", [
-    ((0, 4, 0), (128, 128, 128), dict(dtype="f16/fp8/f16", mfma="32x32x16+f8_32x32x64",
-                                      lds_bytes=str(128 * 128 * 2 + 128 * 128 + 8 * 4096))),
+    # four waves: two workgroups a CU (48 KB of weights, 4 x 4 KB of D staging)
+    ((0, 4, 0), (128, 128, 128), dict(dtype="f16/fp8/f16", mfma="32x32x16+f8_32x32x64", waves="4",
+                                      lds_bytes=str(128 * 128 * 2 + 128 * 128 + 4 * 4096))),
     ((1, 4, 1), (256, 128, 256), dict(dtype="bf16/fp8/bf16", lds_bytes=str(256 * 128 * 2 + 128 * 256 + 8 * 4096))),
     ((0, 4, 1), (96, 64, 32), dict(dtype="f16/fp8/bf16", launches="1")),
 ])
