@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -370,6 +371,18 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
                 return B2B_ERROR_OUT_OF_MEMORY;
             }
         }
+    }
+    // the kernels count tiles (rows_wg rows of one batch) in 32 bits
+    auto tiles_fit = [&](const KernelDesc* k) {
+        return !k || ((M + k->rows_wg - 1) / k->rows_wg) * batch <= (int64_t)INT32_MAX;
+    };
+    bool fit = tiles_fit(p->fused);
+    for (const KernelDesc* k : p->stage_k) fit = fit && tiles_fit(k);
+    if (!fit) {
+        for (void* w : p->work)
+            if (w) (void)hipFree(w);
+        delete p;
+        return B2B_ERROR_INVALID_VALUE;
     }
     *plan = p;
     return B2B_SUCCESS;

@@ -123,7 +123,8 @@ typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
  *                 0 for a B* broadcasts it
  *   flags         B2B_FLAG_* | B2B_REMAP_*
  * Returns INVALID_VALUE for non-positive sizes, ld below the row width, ld
- * not a multiple of 16 bytes, or unknown flags; NOT_SUPPORTED for cascades no
+ * not a multiple of 16 bytes, unknown flags, or more than 2^31 - 1 row tiles
+ * (batch x ceil(M / rows a workgroup takes)); NOT_SUPPORTED for cascades no
  * kernel covers: widths that break the granules or bounds of the run-time-width
  * kernels (see B2B_FLAG_MFMA_32X32) and have no fixed-width kernel, or weights
  * beyond LDS (then the caller may retry with B2B_FLAG_UNFUSED, whose per-GEMM

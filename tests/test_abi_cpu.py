@@ -376,3 +376,13 @@ def test_source_digest_ignores_comments_only():
     c = "int f(int x) { return 3 * x; }"
     assert build._code_only(a) == build._code_only(b) != build._code_only(c)
     assert len(build.source_digest()) == 16
+
+
+def test_tile_count_beyond_32_bits_refused():
+    """The kernels count row tiles in 32 bits: a plan whose batch x tiles would
+    not fit is refused at creation (such inputs could not be allocated anyway)."""
+    st, h = _create(batch=1 << 30, M=1 << 20)
+    assert st == 1 and h.value is None
+    st, h = _create(batch=1 << 10, M=1 << 20)           # 2^23 tiles of 128 rows: fine
+    assert st == 0
+    cf.lib().b2b_gemm_destroy(h)
