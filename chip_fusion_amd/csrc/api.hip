@@ -87,8 +87,9 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
 // Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
 // 16x16x4 for fp64): the smallest width bound that holds them all, or null
 // when a granule, a bound or LDS rules the cascade out.
-bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1, int passes = 0) {
-    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm || d.passes != passes) return false;
+bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1, int passes = 0,
+              int out8 = 0) {
+    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm || d.passes != passes || d.out8 != out8) return false;
     const bool f64 = dt == B2B_DTYPE_F64;
     if (dims[0] % (f64 ? 8 : 32) || dims[0] > d.maxd) return false;
     int64_t lds = 0;
@@ -109,10 +110,21 @@ int wave_rank(const KernelDesc& d, const int64_t* dims, int nst) {
     return d.waves == 4 ? (pair ? 0 : 2) : 1;
 }
 
+// One fp8 GEMM (K = dims[0] a multiple of 64, N = dims[1] of 32), D in dtd.
+const KernelDesc* find_f8a(int dtd, const int64_t* dims) {
+    const KernelDesc* best = nullptr;
+    for (const KernelDesc& d : b2b::registry()) {
+        if (d.f8 != 2 || d.dtd != dtd || dims[0] % 64 || dims[1] % 32) continue;
+        if (dims[0] > d.maxd || dims[1] > d.maxd || dims[0] * dims[1] > 160 * 1024) continue;
+        if (!best || d.maxd < best->maxd) best = &d;
+    }
+    return best;
+}
+
 const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (!d.f8 || d.dtype != dt || d.dtd != dtd) continue;
+        if (d.f8 != 1 || d.dtype != dt || d.dtd != dtd) continue;
         if (dims[0] % 32 || dims[1] % 64 || dims[2] % 32) continue;
         if (dims[0] > d.maxd || dims[1] > d.maxd || dims[2] > d.maxd) continue;
         if (dims[0] * dims[1] * 2 + dims[1] * dims[2] > 160 * 1024) continue;
@@ -126,10 +138,11 @@ const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
 // Among the fitting instances the smallest width bound wins; of two with the
 // same bound, the four-wave one where two of its workgroups fit a CU's LDS
 // (twice the tiles in flight per CU, measured 3 % faster), else the eight-wave one.
-const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0) {
+const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0,
+                           int out8 = 0) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes) || (nst > 1 && d.mode != mode)) continue;
+        if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes, out8) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd ||
             (d.maxd == best->maxd && wave_rank(d, dims, nst) < wave_rank(*best, dims, nst)))
             best = &d;
@@ -273,7 +286,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     const bool typed = tm >= 0, f8 = f8_dtd >= 0;
     // typed, tf32 and fp8 cascades are relabelled on the 32x32x16 kernels
     if ((typed || tf32 || f8) && (orn || mode != b2bk::MODE_RELABEL)) return B2B_ERROR_NOT_SUPPORTED;
-    if (f8 && (nst != 2 || (flags & B2B_FLAG_UNFUSED))) return B2B_ERROR_NOT_SUPPORTED;
+    if (f8 && nst != 2) return B2B_ERROR_NOT_SUPPORTED;
     const bool s32 = (flags & B2B_FLAG_MFMA_32X32) != 0 || typed || tf32;
     if (s32 && (orn || dt == B2B_DTYPE_F64)) return B2B_ERROR_NOT_SUPPORTED;
     // the 32x32x16 kernels rearrange by relabelling or by lane-half swaps
@@ -348,6 +361,18 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
                 delete p;
                 return B2B_ERROR_NOT_SUPPORTED;
             }
+        }
+    } else if (f8) {
+        // unfused: the first GEMM writes its result as fp8, the second reads it
+        const int64_t d0[4] = {dims[0], dims[1], 0, 0}, d1[4] = {dims[1], dims[2], 0, 0};
+        p->stage_k[0] = dims[1] % 64 ? nullptr : find_gen(dt, 1, d0, 0, -1, 0, 1);
+        p->stage_k[1] = find_f8a(f8_dtd, d1);
+        if (!p->stage_k[0] || !p->stage_k[1]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        p->work_bytes[0] = batch * M * dims[1];      // one byte an element
+        if (hipMalloc(&p->work[0], (size_t)p->work_bytes[0]) != hipSuccess) {
+            (void)hipGetLastError();
+            delete p;
+            return B2B_ERROR_OUT_OF_MEMORY;
         }
     } else {
         if (orn) { delete p; return B2B_ERROR_INVALID_VALUE; }

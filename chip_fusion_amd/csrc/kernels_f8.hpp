@@ -58,12 +58,6 @@ __device__ __forceinline__ f16x_t f8_mma(const i8v_t& a, const i8v_t& b, const f
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// four fp32 values -> four E4M3 bytes (round to nearest even), x0 lowest
-__device__ __forceinline__ int f8_pack4(float x0, float x1, float x2, float x3) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-    return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-}
-
 // result tiles 2j (acc0) and 2j+1 (acc1) -> fp8 operand of K-step j (slots
 // 0-15 from acc0's registers 0-15, 16-31 from acc1's)
 __device__ __forceinline__ i8v_t f8_operand(const f16x_t& acc0, const f16x_t& acc1) {
@@ -87,9 +81,9 @@ __device__ __forceinline__ i8v_t f8_wfrag(const unsigned char* lds, int off, int
 // B1 (fp8, n1 x n2, row-major with leading dimension ldb bytes) of batch b ->
 // LDS fragments in the relabelled K order: piece (t, j, q, lane (n', h))
 // gathers rows 64j + 32q + 8(i/4) + 4h + i%4 (i < 16) of column 32t + n'.
-template <class C>
+template <class C, int S = 1>
 __device__ inline void f8_stage_b1(unsigned char* lds, int off, const KArgs& args, int b, int n1, int n2) {
-    const auto rs = make_rsrc((const char*)args.B[1] + (int64_t)b * args.sB[1], (uint32_t)(n1 * args.ldb[1]));
+    const auto rs = make_rsrc((const char*)args.B[S] + (int64_t)b * args.sB[S], (uint32_t)(n1 * args.ldb[S]));
     const int ks8 = n1 / 64, pieces = (n2 / 32) * ks8 * 2 * 64;
     for (int p = (int)threadIdx.x; p < pieces; p += C::THREADS) {
         const int lane = p & 63, q = (p >> 6) & 1, tj = p >> 7;
@@ -99,7 +93,7 @@ __device__ inline void f8_stage_b1(unsigned char* lds, int off, const KArgs& arg
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = 64 * j + 32 * q + 8 * (i >> 2) + 4 * h + (i & 3);
-            const unsigned v = __builtin_amdgcn_raw_buffer_load_b8(rs, row * (int)args.ldb[1] + col, 0, 0);
+            const unsigned v = __builtin_amdgcn_raw_buffer_load_b8(rs, row * (int)args.ldb[S] + col, 0, 0);
             w[i >> 2] |= v << (8 * (i & 3));
         }
         *(u4_t*)(lds + off + tj * 2048 + q * 1024 + lane * 16) = u4_t{w[0], w[1], w[2], w[3]};
@@ -208,6 +202,119 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void f8_kernel(KArgs args) {
     f8_body<C>(args);
+}
+
+// The second kernel of the unfused comparison of such a cascade: one GEMM of
+// an fp8 A (the intermediate the first kernel wrote as E4M3 bytes) and an fp8
+// B on the fp8 instruction, D in DTD_.  A is read in the relabelled slot
+// order of the fused kernel: dword 4q + i of K-step j holds bytes 64j + 32q +
+// 8i + 4(l/32) + 0..3 of row l%32.  K a multiple of 64, N of 32.
+template <int DTD_, int MAXD_>
+struct F8ACfg {
+    static constexpr int DT = DT_F16, DTD = DTD_, NST = 1, MAXD = MAXD_, MODE = MODE_RELABEL, PF = 1;
+    static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
+    static constexpr int MKS = MAXD / 16, MNT = MAXD / 32, MKS8 = MAXD / 64;
+    static constexpr int LDS_MAX = 160 * 1024;
+    static constexpr int stype(int) { return DTD; }   // D, for gen_store_pair
+    static_assert(MAXD % 64 == 0, "config");
+};
+
+// LDS bytes: the fp8 weights, then 4 KB of D staging per wave when it fits
+__host__ __device__ inline int64_t f8a_lds_bytes(const int32_t* d) {
+    const int64_t w = (int64_t)d[0] * d[1];
+    return w + (w + 8 * 4096 <= 160 * 1024 ? 8 * 4096 : 0);
+}
+
+template <class C>
+__device__ __forceinline__ void f8a_load(i8v_t (&x)[C::MKS8], __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t none,
+                                         int64_t lda, int ks8, int lane) {
+    const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < C::MKS8; ++j) {
+        const auto src = j < ks8 ? rs : none;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            x[j][d] = __builtin_amdgcn_raw_buffer_load_b32(
+                src, (int)(m * lda + 64 * j + 32 * (d >> 2) + 8 * (d & 3) + 4 * h), 0, 0);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void f8a_body(const KArgs& args) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int d0 = args.dims[0], d1 = args.dims[1];
+    const int stg = (int64_t)d0 * d1 + 8 * 4096 <= 160 * 1024 ? d0 * d1 + wave * 4096 : -1;
+    const int ks8 = d0 / 64, nt = d1 / 32;
+
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+    const int per = args.total_tiles / G, extra = args.total_tiles % G;
+    const int t0 = lid * per + (lid < extra ? lid : extra);
+    const int t1 = t0 + per + (lid < extra ? 1 : 0);
+    if (t0 >= t1) return;
+    const int TB = args.tiles_per_batch;
+
+    int t_end = t1;
+    auto rows_of = [&](int t) {
+        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        const int64_t r = args.M - row0;
+        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
+    };
+    auto a_rsrc = [&](int t) {
+        const bool live = t < t_end;
+        const int tc = live ? t : t0;
+        const int64_t rows = live ? rows_of(tc) : 0;
+        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        return make_rsrc((const char*)args.A + (int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda,
+                         (uint32_t)(rows * args.lda));
+    };
+    auto process = [&](int t, const i8v_t (&x)[C::MKS8]) __attribute__((always_inline)) {
+        const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
+        const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 2,
+                                    (uint32_t)(rows * args.ldd * 2));
+#pragma unroll
+        for (int t2 = 0; t2 < C::MNT; t2 += 2) {
+            if (t2 < nt) {
+                const bool two = t2 + 1 < nt;
+                const int t2b = two ? t2 + 1 : t2;
+                f16x_t acc0 = {}, acc1 = {};
+#pragma unroll
+                for (int j = 0; j < C::MKS8; ++j)
+                    if (j < ks8) {
+                        acc0 = f8_mma(f8_wfrag(lds, 0, ks8, t2, j, lane), x[j], acc0);
+                        acc1 = f8_mma(f8_wfrag(lds, 0, ks8, t2b, j, lane), x[j], acc1);
+                    }
+                gen_store_pair<C>(lds, stg, acc0, acc1, two, d_rs, args.ldd, 32 * t2, lane);
+            }
+        }
+    };
+
+    const auto no_rsrc = make_rsrc(args.A, 0u);
+    i8v_t ring[2][C::MKS8];
+    int t = t0;
+    while (t < t1) {
+        const int b = t / TB;
+        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+        __syncthreads();   // the previous segment's weight reads are over
+        f8_stage_b1<C, 0>(lds, 0, args, b, d0, d1);
+        __syncthreads();
+        f8a_load<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks8, lane);
+        for (;;) {
+            f8a_load<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks8, lane);
+            process(t, ring[0]);
+            if (++t >= t_end) break;
+            f8a_load<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks8, lane);
+            process(t, ring[1]);
+            if (++t >= t_end) break;
+        }
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void f8a_kernel(KArgs args) {
+    f8a_body<C>(args);
 }
 
 // One fp8 instruction on raw operands (64 lanes x 32 E4M3 bytes each) and the

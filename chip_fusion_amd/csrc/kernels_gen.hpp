@@ -59,9 +59,13 @@ template <> struct Ty32<DT_BF16> {
 // (page 1 lets each fused operator have its own data type): bit s set means
 // bf16, clear fp16, for the operands of GEMM s (A, B_s and the intermediate
 // rounded for it) and, at bit NST, for D.  DT_ is then the type of bit 0.
-template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8>
+// OUT8_: D is written as fp8 E4M3 bytes (the first kernel of an unfused
+// cascade whose second GEMM is fp8), else in the last stage's 16-bit type.
+template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8, bool OUT8_ = false>
 struct GenCfg {
     static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_, TM = TM_;
+    static constexpr bool OUT8 = OUT8_;
+    static constexpr int DE = OUT8 ? 1 : 2;   // bytes of a D element
     static constexpr int stype(int s) { return TM < 0 ? DT : (((TM >> s) & 1) ? DT_BF16 : DT_F16); }
     static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
@@ -274,6 +278,51 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
     asm volatile("" ::: "memory");
 }
 
+// four fp32 values -> four E4M3 bytes (round to nearest even), x0 lowest
+__device__ __forceinline__ int f8_pack4(float x0, float x1, float x2, float x3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+}
+
+// A pair of result tiles -> fp8 D (one byte an element).  Lane (m, h) packs
+// columns 8a + 4h + 0..3 of tile q into one dword at byte 32q + 8a + 4h of
+// row m's 64-byte segment; through the staging region each store writes 16
+// rows x 64 (or 32) contiguous bytes, else the dwords go straight out.
+__device__ __forceinline__ void gen_store_pair_f8(unsigned char* lds, int stg, const f16x_t& acc0, const f16x_t& acc1,
+                                                  bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    unsigned w[2][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        w[0][a] = (unsigned)f8_pack4(acc0[4 * a], acc0[4 * a + 1], acc0[4 * a + 2], acc0[4 * a + 3]);
+        w[1][a] = (unsigned)f8_pack4(acc1[4 * a], acc1[4 * a + 1], acc1[4 * a + 2], acc1[4 * a + 3]);
+    }
+    if (stg < 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                if (q == 0 || two)
+                    __builtin_amdgcn_raw_buffer_store_b32(w[q][a], rs, (int)(m * ldd + n0 + 32 * q + 8 * a + 4 * h), 0,
+                                                          kStreamPolicy);
+        return;
+    }
+    unsigned char* st = lds + stg;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) *(unsigned*)(st + m * 64 + 32 * q + 8 * a + 4 * h) = w[q][a];
+    asm volatile("" ::: "memory");
+    const int ch = lane & 3, nch = two ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * i + (lane >> 2);
+        const u4_t v = *(const u4_t*)(st + r * 64 + 16 * ch);
+        if (ch < nch) st128(rs, (uint32_t)(r * ldd + n0 + 16 * ch), v);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // One GEMM of the cascade on one wave's 32 rows: x holds the operand K-steps
 // (ks of them), the result has nt tiles of 32 columns, each handed to sink(t, acc).
 // Tiles go in pairs: two independent accumulation chains keep the matrix
@@ -363,10 +412,12 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         for (int j = 0; j < C::MKS; ++j) a[j] = a_in[j];
         gen_arrange_a<C>(a);
         const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 2,
-                                    (uint32_t)(rows * args.ldd * 2));
+        const auto d_rs =
+            make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * C::DE,
+                      (uint32_t)(rows * args.ldd * C::DE));
         auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
-            gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
+            if constexpr (C::OUT8) gen_store_pair_f8(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
+            else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
         };
         if constexpr (C::NST == 1) {
             gen_gemm<C, C::stype(0)>(lds, fr[0], a, ks0, dn / 32, to_d);

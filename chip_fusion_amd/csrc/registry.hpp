@@ -21,8 +21,9 @@ struct KernelDesc {
     int maxd = 0;
     int tm = -1;      // type per stage (bit s: bf16 operands of GEMM s, bit nst: D), or -1: all dtype
     int passes = 0;   // tf32: bf16 matrix-instruction passes per product (3 or 4)
-    int f8 = 0;       // 1: two GEMMs, the second on the fp8 instruction (dtd: D's type)
+    int f8 = 0;       // 1: two GEMMs, the second on the fp8 instruction; 2: one fp8 GEMM (dtd: D's type)
     int dtd = -1;
+    int out8 = 0;     // 1: D written as fp8 E4M3 bytes
     const void* fn;   // the __global__ function, for occupancy queries
     // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
     int64_t (*dyn_lds)(const int32_t* d) = nullptr;
@@ -103,6 +104,7 @@ KernelDesc describe_gen() {
     d.rtw = 1;
     d.maxd = C::MAXD;
     d.tm = C::TM;
+    d.out8 = C::OUT8 ? 1 : 0;
     d.fn = (const void*)&b2bk::gen_kernel<C>;
     d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST, C::WAVES); };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
@@ -177,6 +179,39 @@ KernelDesc describe_f8() {
         if (attr != hipSuccess) return attr;
         const size_t shm = (size_t)b2bk::f8_lds_bytes(a.dims, C::WAVES);
         hipLaunchKernelGGL(b2bk::f8_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
+        return hipGetLastError();
+    };
+    return d;
+}
+
+// One fp8 GEMM (the second kernel of an unfused fp8 cascade), run-time widths.
+template <class C>
+KernelDesc describe_f8a() {
+    KernelDesc d;
+    d.dtype = -1;
+    d.nst = 1;
+    for (int& x : d.dims) x = 0;   // never matched by width
+    d.mode = 0;
+    d.orn = 0;
+    d.km0 = b2bk::KM_NAT;
+    d.mt = C::ROWS_WAVE / 16;
+    d.waves = C::WAVES;
+    d.threads = C::THREADS;
+    d.rows_wg = C::ROWS_WG;
+    d.lds_bytes = 0;
+    d.shape32 = 1;
+    d.rtw = 1;
+    d.maxd = C::MAXD;
+    d.f8 = 2;
+    d.dtd = C::DTD;
+    d.fn = (const void*)&b2bk::f8a_kernel<C>;
+    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::f8a_lds_bytes(w); };
+    d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
+        static const hipError_t attr = hipFuncSetAttribute(
+            (const void*)&b2bk::f8a_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
+        if (attr != hipSuccess) return attr;
+        const size_t shm = (size_t)b2bk::f8a_lds_bytes(a.dims);
+        hipLaunchKernelGGL(b2bk::f8a_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };
     return d;
@@ -290,6 +325,10 @@ ProbeDesc describe_probe() {
 #define B2B_F8_INSTANCE(...)                                                           \
     static ::b2b::Registrar B2B_CAT(b2b_f8_reg_, __LINE__)(                            \
         ::b2b::describe_f8<::b2bk::F8Cfg<__VA_ARGS__>>())
+// B2B_F8A_INSTANCE(D's type, max width)
+#define B2B_F8A_INSTANCE(...)                                                          \
+    static ::b2b::Registrar B2B_CAT(b2b_f8a_reg_, __LINE__)(                           \
+        ::b2b::describe_f8a<::b2bk::F8ACfg<__VA_ARGS__>>())
 // B2B_GEN64_INSTANCE(stages, max width, A tiles ahead, tiles per group)
 #define B2B_GEN64_INSTANCE(...)                                                        \
     static ::b2b::Registrar B2B_CAT(b2b_gen64_reg_, __LINE__)(                         \

@@ -189,7 +189,9 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
  * and nst = 2 -- the first GEMM in t0, its result rounded to fp8 and
  * multiplied by the fp8 B1 on the fp8 instruction, D in tD; K a multiple of 32,
  * N1 of 64, N2 of 32, each at most 256, B0 (2 bytes an element) and B1 (one)
- * within 160 KB; fused only (NOT_SUPPORTED with B2B_FLAG_UNFUSED). */
+ * within 160 KB.  With B2B_FLAG_UNFUSED the first GEMM writes its result as
+ * E4M3 bytes to a workspace and a second kernel multiplies them (the same
+ * values and order of sums: D equals the fused result bit for bit). */
 b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes, int64_t batch, int64_t M,
                                     int32_t nst, const int64_t* widths, const int64_t* ld,
                                     const int64_t* batch_stride, uint32_t flags);

@@ -317,7 +317,6 @@ def test_fp8_plan_selection(dtypes, widths, expect):
     ((4, 0, 0), (128, 128, 128), 0, 2),                # fp8 is a later GEMM's type
     ((0, 0, 4), (128, 128, 128), 0, 2),                # not D's
     ((0, 4, 0, 0), (128, 128, 128, 64), 0, 2),         # two GEMMs
-    ((0, 4, 0), (128, 128, 128), 1, 2),                # fused only
     ((0, 4, 0), (128, 128, 128), 2 << 4, 2),           # relabelled only
     ((0, 4, 0), (128, 128, 144), 0, 2),                # N2 a multiple of 32
 ])

@@ -140,3 +140,28 @@ def test_fp8_padded_and_broadcast():
     mask = torch.ones_like(Dd, dtype=torch.bool)
     mask.as_strided((batch, M, widths[2]), (sD, ldd, 1)).fill_(False)
     assert torch.isnan(Dd[mask]).all().item(), "writes outside the output windows"
+
+
+@pytest.mark.parametrize("types,widths", [(("f16", "fp8", "f16"), (128, 128, 128)),
+                                          (("bf16", "fp8", "bf16"), (256, 256, 64)),
+                                          (("f16", "fp8", "bf16"), (96, 64, 32))])
+def test_fp8_unfused_matches_fused_bitwise(types, widths):
+    """The unfused comparison (the first GEMM writes its result as E4M3 bytes,
+    a second kernel multiplies them on the fp8 instruction) reads the
+    intermediate in the fused kernel's slot order and sums in the same order:
+    D agrees bit for bit, and with the oracle within the tolerance."""
+    _flush(f"fp8 unfused {types} {widths}")
+    batch, M = 2, 300
+    A, Bs = _inputs(types, batch, M, widths)
+    fused, _ = _run(types, A, Bs)
+    Ad, B0d, B1d = cf.to_device(A, types[0]), cf.to_device(Bs[0], types[0]), cf.to_device(Bs[1], "fp8")
+    D = nan_output(types[2], batch, M, widths[2])
+    p = cf.Chain(list(types), batch, M, list(widths), unfused=True)
+    info = p.info()
+    p.run(Ad, B0d, B1d, D=D)
+    torch.cuda.synchronize()
+    p.close()
+    assert "path=unfused" in info and "launches=2" in info, info
+    unf = cf.to_host(D)
+    assert np.array_equal(unf, fused), f"{int((unf != fused).sum())} elements differ"
+    assert_close(types[2], unf, oracle.cascade(list(types), A, Bs), f"fp8 unfused {types}")
