@@ -164,13 +164,17 @@ def _tf32_ref(x):
 
 
 def test_tf32_rounding_against_float64_reference():
-    """Every fraction pattern of five binades (normal, the smallest normal,
-    a subnormal one, the largest), 2^22 random encodings, and the specials."""
-    pats = [np.arange(1 << 23, dtype=np.uint32) | np.uint32(e << 23) for e in (1, 2, 127, 254, 0)]
+    """Every fraction pattern of the binade at 1 and of the subnormals, the
+    lowest and highest 2^20 patterns of the smallest normal and the largest
+    binade (the carry into the next binade and into infinity), 2^22 random
+    encodings of either sign, and the specials."""
+    full = [np.arange(1 << 23, dtype=np.uint32) | np.uint32(e << 23) for e in (127, 0)]
+    low = np.arange(1 << 20, dtype=np.uint32)
+    high = np.arange((1 << 23) - (1 << 20), 1 << 23, dtype=np.uint32)
+    edges = [p | np.uint32(e << 23) for e in (1, 254) for p in (low, high)]
     rng = np.random.default_rng(5)
-    pats.append(rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32))
-    u = np.concatenate(pats)
-    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    rnd = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    u = np.concatenate(full + edges + [rnd])
     x = u.view(np.float32)
     x = x[np.isfinite(x)]
     got = oracle.round_tf32(x).astype(np.float64)
