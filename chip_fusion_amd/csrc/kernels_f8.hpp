@@ -115,37 +115,16 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
     fr0.init(m0[0], false, lane);
     const int ks0 = d0 / 16, ks8 = d1 / 64, nt2 = d2 / 32;
 
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int per = args.total_tiles / G, extra = args.total_tiles % G;
-    const int t0 = lid * per + (lid < extra ? lid : extra);
-    const int t1 = t0 + per + (lid < extra ? 1 : 0);
-    if (t0 >= t1) return;
-    const int TB = args.tiles_per_batch;
-
-    int t_end = t1;
-    auto rows_of = [&](int t) {
-        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const int64_t r = args.M - row0;
-        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
-    };
-    auto a_rsrc = [&](int t) {
-        const bool live = t < t_end;
-        const int tc = live ? t : t0;
-        const int64_t rows = live ? rows_of(tc) : 0;
-        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        return make_rsrc((const char*)args.A + ((int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda) * 2,
-                         (uint32_t)(rows * args.lda * 2));
-    };
+    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
+    if (!tr.init(args, wave)) return;
+    auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 2, t); };
 
     auto process = [&](int t, const u4_t (&a_in)[C::MKS]) __attribute__((always_inline)) {
         u4_t a[C::MKS];
 #pragma unroll
         for (int j = 0; j < C::MKS; ++j) a[j] = a_in[j];
         gen_arrange_a<C>(a);
-        const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 2,
-                                    (uint32_t)(rows * args.ldd * 2));
+        const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, 2, t);
         // first GEMM: result tiles in pairs, each pair one fp8 K-step
         i8v_t x8[C::MKS8];
         gen_gemm<C, C::DT>(lds, fr0, a, ks0, d1 / 32,
@@ -172,16 +151,16 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
 
     const auto no_rsrc = make_rsrc(args.A, 0u);
     u4_t ring[C::PF + 1][C::MKS];
-    int t = t0;
-    while (t < t1) {
-        const int b = t / TB;
-        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+    int t = tr.t0;
+    while (t < tr.t1) {
+        const int b = t / tr.TB;
+        tr.segment(t);
         __syncthreads();   // the previous segment's weight reads are over
         gen_stage_weights<typename C::Stage0>(lds, m0, args, b);
         f8_stage_b1<C>(lds, off1, args, b, d1, d2);
         __syncthreads();
         if constexpr (C::PF == 0) {
-            for (; t < t_end; ++t) {
+            for (; t < tr.t_end; ++t) {
                 gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[0]);
             }
@@ -190,10 +169,10 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
             for (;;) {
                 gen_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[0]);
-                if (++t >= t_end) break;
+                if (++t >= tr.t_end) break;
                 gen_load_a<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[1]);
-                if (++t >= t_end) break;
+                if (++t >= tr.t_end) break;
             }
         }
     }
@@ -248,32 +227,11 @@ __device__ __forceinline__ void f8a_body(const KArgs& args) {
     const int stg = (int64_t)d0 * d1 + 8 * 4096 <= 160 * 1024 ? d0 * d1 + wave * 4096 : -1;
     const int ks8 = d0 / 64, nt = d1 / 32;
 
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int per = args.total_tiles / G, extra = args.total_tiles % G;
-    const int t0 = lid * per + (lid < extra ? lid : extra);
-    const int t1 = t0 + per + (lid < extra ? 1 : 0);
-    if (t0 >= t1) return;
-    const int TB = args.tiles_per_batch;
-
-    int t_end = t1;
-    auto rows_of = [&](int t) {
-        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const int64_t r = args.M - row0;
-        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
-    };
-    auto a_rsrc = [&](int t) {
-        const bool live = t < t_end;
-        const int tc = live ? t : t0;
-        const int64_t rows = live ? rows_of(tc) : 0;
-        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        return make_rsrc((const char*)args.A + (int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda,
-                         (uint32_t)(rows * args.lda));
-    };
+    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
+    if (!tr.init(args, wave)) return;
+    auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 1, t); };
     auto process = [&](int t, const i8v_t (&x)[C::MKS8]) __attribute__((always_inline)) {
-        const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 2,
-                                    (uint32_t)(rows * args.ldd * 2));
+        const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, 2, t);
 #pragma unroll
         for (int t2 = 0; t2 < C::MNT; t2 += 2) {
             if (t2 < nt) {
@@ -293,10 +251,10 @@ __device__ __forceinline__ void f8a_body(const KArgs& args) {
 
     const auto no_rsrc = make_rsrc(args.A, 0u);
     i8v_t ring[2][C::MKS8];
-    int t = t0;
-    while (t < t1) {
-        const int b = t / TB;
-        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+    int t = tr.t0;
+    while (t < tr.t1) {
+        const int b = t / tr.TB;
+        tr.segment(t);
         __syncthreads();   // the previous segment's weight reads are over
         f8_stage_b1<C, 0>(lds, 0, args, b, d0, d1);
         __syncthreads();
@@ -304,10 +262,10 @@ __device__ __forceinline__ void f8a_body(const KArgs& args) {
         for (;;) {
             f8a_load<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks8, lane);
             process(t, ring[0]);
-            if (++t >= t_end) break;
+            if (++t >= tr.t_end) break;
             f8a_load<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks8, lane);
             process(t, ring[1]);
-            if (++t >= t_end) break;
+            if (++t >= tr.t_end) break;
         }
     }
 }

@@ -359,6 +359,57 @@ __device__ __forceinline__ void gen_static_for(F&& f) {
     }
 }
 
+// The row tiles of one workgroup: a contiguous range of the launch's tiles
+// (ROWS_WG rows of one batch each; consecutive workgroups on one XCD, as
+// block i runs on XCD i % 8, so a batch's weights are read by one XCD's L2),
+// walked one batch segment (one set of weights) at a time.  Everything here
+// is uniform across the wave and lives in scalar registers.
+template <int ROWS_WG, int ROWS_WAVE>
+struct TileRange {
+    int t0, t1, TB, t_end, wave;
+    int64_t M;
+    // false: no tiles for this workgroup
+    __device__ inline bool init(const KArgs& a, int wave_) {
+        const int G = gridDim.x, bid = blockIdx.x;
+        const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+        const int per = a.total_tiles / G, extra = a.total_tiles % G;
+        t0 = lid * per + (lid < extra ? lid : extra);
+        t1 = t0 + per + (lid < extra ? 1 : 0);
+        TB = a.tiles_per_batch;
+        t_end = t1;
+        wave = wave_;
+        M = a.M;
+        return t0 < t1;
+    }
+    // the tiles from t on that share t's batch
+    __device__ inline void segment(int t) {
+        const int b = t / TB;
+        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+    }
+    __device__ inline int64_t row0(int t) const { return (int64_t)(t % TB) * ROWS_WG + wave * ROWS_WAVE; }
+    // this wave's rows of tile t (fewer on the ragged last tile of M, 0 past it)
+    __device__ inline int64_t rows(int t) const {
+        const int64_t r = M - row0(t);
+        return r < 0 ? (int64_t)0 : (r > ROWS_WAVE ? (int64_t)ROWS_WAVE : r);
+    }
+    // buffer resource over this wave's rows of tile t of a row-major matrix
+    // (esz-byte elements, leading dimension ld, batch stride bs)
+    __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t ld, int64_t bs, int esz, int t) const {
+        const int64_t n = rows(t);
+        return make_rsrc((const char*)base + ((int64_t)(t / TB) * bs + (n ? row0(t) : 0) * ld) * esz,
+                         (uint32_t)(n * ld * esz));
+    }
+    // the same for an A tile about to be loaded: past the segment an empty
+    // resource, whose loads return zeros without touching memory
+    __device__ inline __amdgpu_buffer_rsrc_t a_rsrc(const void* base, int64_t ld, int64_t bs, int esz, int t) const {
+        const bool live = t < t_end;
+        const int tc = live ? t : t0;
+        const int64_t n = live ? rows(tc) : 0;
+        return make_rsrc((const char*)base + ((int64_t)(tc / TB) * bs + (n ? row0(tc) : 0) * ld) * esz,
+                         (uint32_t)(n * ld * esz));
+    }
+};
+
 template <class C>
 __device__ __forceinline__ void gen_body(const KArgs& args) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -382,39 +433,16 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
 #pragma unroll
     for (int s = 0; s < C::NST; ++s) fr[s].init(mat[s], REL && s > 0, lane);
 
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int per = args.total_tiles / G, extra = args.total_tiles % G;
-    const int t0 = lid * per + (lid < extra ? lid : extra);
-    const int t1 = t0 + per + (lid < extra ? 1 : 0);
-    if (t0 >= t1) return;
-    const int TB = args.tiles_per_batch;
-
-    int t_end = t1;
-    auto rows_of = [&](int t) {
-        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const int64_t r = args.M - row0;
-        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
-    };
-    // tiles past the segment get an empty resource (their loads return zeros)
-    auto a_rsrc = [&](int t) {
-        const bool live = t < t_end;
-        const int tc = live ? t : t0;
-        const int64_t rows = live ? rows_of(tc) : 0;
-        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        return make_rsrc((const char*)args.A + ((int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda) * 2,
-                         (uint32_t)(rows * args.lda * 2));
-    };
+    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
+    if (!tr.init(args, wave)) return;
+    auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 2, t); };
 
     auto process = [&](int t, const u4_t (&a_in)[C::MKS]) __attribute__((always_inline)) {
         u4_t a[C::MKS];
 #pragma unroll
         for (int j = 0; j < C::MKS; ++j) a[j] = a_in[j];
         gen_arrange_a<C>(a);
-        const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const auto d_rs =
-            make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * C::DE,
-                      (uint32_t)(rows * args.ldd * C::DE));
+        const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, C::DE, t);
         auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
             if constexpr (C::OUT8) gen_store_pair_f8(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
             else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
@@ -450,15 +478,15 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
 
     const auto no_rsrc = make_rsrc(args.A, 0u);
     u4_t ring[C::PF + 1][C::MKS];
-    int t = t0;
-    while (t < t1) {
-        const int b = t / TB;
-        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+    int t = tr.t0;
+    while (t < tr.t1) {
+        const int b = t / tr.TB;
+        tr.segment(t);
         __syncthreads();   // the previous segment's weight reads are over
         gen_stage_weights<C>(lds, mat, args, b);
         __syncthreads();
         if constexpr (C::PF == 0) {
-            for (; t < t_end; ++t) {
+            for (; t < tr.t_end; ++t) {
                 gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[0]);
             }
@@ -468,10 +496,10 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
             for (;;) {
                 gen_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[0]);
-                if (++t >= t_end) break;
+                if (++t >= tr.t_end) break;
                 gen_load_a<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[1]);
-                if (++t >= t_end) break;
+                if (++t >= tr.t_end) break;
             }
         }
     }

@@ -294,41 +294,21 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
         fl[s].init(ml[s], s > 0, lane);
     }
 
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    const int per = args.total_tiles / G, extra = args.total_tiles % G;
-    const int t0 = lid * per + (lid < extra ? lid : extra);
-    const int t1 = t0 + per + (lid < extra ? 1 : 0);
-    if (t0 >= t1) return;
-    const int TB = args.tiles_per_batch;
-
-    int t_end = t1;
-    auto rows_of = [&](int t) {
-        const int64_t row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        const int64_t r = args.M - row0;
-        return r < 0 ? (int64_t)0 : (r > C::ROWS_WAVE ? (int64_t)C::ROWS_WAVE : r);
-    };
-    // tiles past the segment get an empty resource (their loads return zeros)
-    auto a_rsrc = [&](int t) {
-        const bool live = t < t_end;
-        const int tc = live ? t : t0;
-        const int64_t rows = live ? rows_of(tc) : 0;
-        const int64_t row0 = (int64_t)(tc % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-        return make_rsrc((const char*)args.A + ((int64_t)(tc / TB) * args.sA + (rows ? row0 : 0) * args.lda) * 4,
-                         (uint32_t)(rows * args.lda * 4));
-    };
+    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
+    if (!tr.init(args, wave)) return;
+    auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 4, t); };
     const auto no_rsrc = make_rsrc(args.A, 0u);
 
     u4_t a[2 * C::MKS];
-    int t = t0;
-    while (t < t1) {
-        const int b = t / TB;
-        t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
+    int t = tr.t0;
+    while (t < tr.t1) {
+        const int b = t / tr.TB;
+        tr.segment(t);
         __syncthreads();   // the previous segment's weight reads are over
         tf32_stage_weights<C>(lds, mh, ml, args, b);
         tf32_load_a<C>(a, a_rsrc(t), no_rsrc, args.lda, ks0, lane);
         __syncthreads();
-        for (; t < t_end; ++t) {
+        for (; t < tr.t_end; ++t) {
             u4_t xh[C::MKS], xl[C::MKS];
 #pragma unroll
             for (int j = 0; j < C::MKS; ++j) tf32_operand(a[2 * j], a[2 * j + 1], xh[j], xl[j]);
@@ -343,9 +323,7 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
             tf32_load_a<C, 0, C::MKS / 4>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
             if constexpr (EARLY) issue_next();
 
-            const int64_t rows = rows_of(t), row0 = (int64_t)(t % TB) * C::ROWS_WG + wave * C::ROWS_WAVE;
-            const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 4,
-                                        (uint32_t)(rows * args.ldd * 4));
+            const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, 4, t);
             auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
                 tf32_store_tile(lds, stg, a0, d_rs, args.ldd, 32 * tt, lane);
                 if (two) tf32_store_tile(lds, stg, a1, d_rs, args.ldd, 32 * tt + 32, lane);
