@@ -94,7 +94,7 @@ def main():
     import chip_fusion_amd as cf
     import synth
 
-    c = dict(synth.CONFIGS[args.config])
+    c = dict(synth.WORKLOADS[args.config])
     if args.dtype and args.dtype != c["dtype"]:
         c["name"] = c["name"].replace(c["dtype"], args.dtype, 1)
         c["dtype"] = args.dtype

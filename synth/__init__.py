@@ -28,7 +28,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # The five workloads: (dtype, batch, M, [K, N1, N2(, N3)], distribution, scale, base seed)
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="fp16 b1 128x64 . 64x64 . 64x64", dtype="f16", batch=1, M=128,
             dims=[64, 64, 64], dist="uniform", scale=1.0, seed=0x5EED0001),
     2: dict(name="fp16 b64 4096x128 . 128x128 . 128x128", dtype="f16", batch=64, M=4096,
@@ -185,12 +185,12 @@ def tensor(seed, tensor_id, shape, dtype, dist, scale=1.0):
 def make_inputs(cfg, M=None, batch=None, dist=None, seed=None, types=None):
     """Inputs of a workload: returns (A, [B0, B1, (B2)]).
 
-    cfg: a CONFIGS key or dict.  M / batch / dist / seed override the
+    cfg: a WORKLOADS key or dict.  M / batch / dist / seed override the
     workload's values (smaller sizes for the parity tests, 'ternary' for the
     exactness variants).  types: one 16-bit type per GEMM (A and B_0 in
     types[0], B_s in types[s]) instead of the workload's single type.
     """
-    c = dict(CONFIGS[cfg]) if isinstance(cfg, int) else dict(cfg)
+    c = dict(WORKLOADS[cfg]) if isinstance(cfg, int) else dict(cfg)
     M = c["M"] if M is None else M
     batch = c["batch"] if batch is None else batch
     dist = c["dist"] if dist is None else dist

@@ -26,13 +26,13 @@ EXPECTED = {
 
 @pytest.mark.parametrize("cfg", sorted(EXPECTED))
 def test_workload_numbers(cfg):
-    flop, byts = bench.workload_numbers(synth.CONFIGS[cfg])
+    flop, byts = bench.workload_numbers(synth.WORKLOADS[cfg])
     assert (flop, byts) == EXPECTED[cfg]
 
 
 def test_headline_flop_count():
     # 17.18 GFLOP for the 64 x 4096 x 128^3 fp16 workload
-    assert abs(bench.workload_numbers(synth.CONFIGS[2])[0] / 1e9 - 17.18) < 0.01
+    assert abs(bench.workload_numbers(synth.WORKLOADS[2])[0] / 1e9 - 17.18) < 0.01
 
 
 def test_more_than_one_gpu_refused():
@@ -45,7 +45,7 @@ def test_more_than_one_gpu_refused():
 
 def test_workload_numbers_per_stage_types():
     """An fp8 second GEMM counts its weights at one byte an element; tf32 at four."""
-    c = dict(synth.CONFIGS[2])
+    c = dict(synth.WORKLOADS[2])
     flop, byts = bench.workload_numbers(c, ["f16", "fp8", "f16"])
     assert flop == EXPECTED[2][0]
     assert byts == 64 * (2 * 4096 * 128 + 2 * 128 * 128 + 1 * 128 * 128 + 2 * 4096 * 128)

@@ -93,7 +93,7 @@ def test_unfused_chain_matches_fused_bitwise(dtype):
 def test_short_chains_match_gemm_api(cfg):
     """Up to three GEMMs the chain call plans and runs exactly what
     b2b_gemm_create does (fp64 included)."""
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     dt, dims = c["dtype"], c["dims"]
     M, batch = min(c["M"], 300), min(c["batch"], 2)
     _flush(f"chain vs gemm api cfg{cfg}")

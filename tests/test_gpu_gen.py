@@ -81,7 +81,7 @@ def test_runtime_widths_ternary_exact(dims, dtype, mode):
 @pytest.mark.parametrize("mode", ["relabel", "permlane"])
 @pytest.mark.parametrize("cfg,M,batch", [(1, 128, 1), (2, 1000, 3), (5, 700, 2)])
 def test_configs_on_32x32(cfg, M, batch, mode):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     _flush(f"gen forced cfg{cfg} {mode} M={M} batch={batch}")
     A, Bs = synth.make_inputs(cfg, M=M, batch=batch)
     got, info = _run(c["dtype"], A, Bs, remap=mode, mfma32=True)

@@ -63,7 +63,7 @@ def _cases():
 
 @pytest.mark.parametrize("cfg,mode,orient_n", list(_cases()))
 def test_cascade_parity_small(cfg, mode, orient_n):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     _flush(f"cascade cfg{cfg} {mode} orientN={orient_n} {SMALL[cfg]}")
     A, Bs = synth.make_inputs(cfg, **SMALL[cfg])
     got = run_plan(c["dtype"], A, Bs, remap=mode, orient_n=orient_n)
@@ -75,7 +75,7 @@ def test_cascade_parity_small(cfg, mode, orient_n):
 def test_cascade_ternary_bit_exact(cfg, mode, orient_n):
     """Small-integer inputs: every partial sum is exact in the accumulator, so
     any summation order gives the oracle's result bit for bit."""
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     _flush(f"ternary cfg{cfg} {mode} orientN={orient_n}")
     A, Bs = synth.make_inputs(cfg, dist="ternary", **SMALL[cfg])
     got = run_plan(c["dtype"], A, Bs, remap=mode, orient_n=orient_n)
@@ -85,7 +85,7 @@ def test_cascade_ternary_bit_exact(cfg, mode, orient_n):
 
 @pytest.mark.parametrize("cfg", [1, 2, 4, 5])
 def test_unfused_path_parity(cfg):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     _flush(f"unfused cfg{cfg}")
     A, Bs = synth.make_inputs(cfg, **SMALL[cfg])
     got = run_plan(c["dtype"], A, Bs, unfused=True)
@@ -99,7 +99,7 @@ def test_fused_equals_unfused_bitwise(cfg, mode):
     """With the natural K order the fused kernel issues the same MFMA chain as
     the two-kernel path, whose intermediate goes through HBM already rounded:
     the results must agree bit for bit."""
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     _flush(f"fused==unfused cfg{cfg} {mode}")
     A, Bs = synth.make_inputs(cfg, **SMALL[cfg])
     f = run_plan(c["dtype"], A, Bs, remap=mode)
@@ -121,7 +121,7 @@ def _sample_rows(batch, M, n=384, seed=0):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_full_size_sampled(cfg):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     dt, dims = c["dtype"], c["dims"]
     _flush(f"full size cfg{cfg}: batch {c['batch']} M {c['M']} dims {dims}")
     A, Bs = synth.make_inputs(cfg)
@@ -197,7 +197,7 @@ def test_wide_cascade_ternary_bit_exact():
 
 def test_wide_cascade_f16_parity():
     """The same column-split kernel instantiated for fp16."""
-    A, Bs = synth.make_inputs(dict(synth.CONFIGS[3], dtype="f16"), M=600, batch=1)
+    A, Bs = synth.make_inputs(dict(synth.WORKLOADS[3], dtype="f16"), M=600, batch=1)
     f = run_plan("f16", A, Bs)
     ref = oracle.cascade("f16", A, Bs)
     assert_close("f16", f, ref, "f16 256^3")

@@ -39,7 +39,7 @@ CASES = {
 
 @pytest.mark.parametrize("cfg", sorted(CASES))
 def test_padded_and_broadcast(cfg):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     dt, dims = c["dtype"], c["dims"]
     M, batch = CASES[cfg]
     _flush(f"strided cfg{cfg} M={M} batch={batch} dims={dims}")

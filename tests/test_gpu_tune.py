@@ -25,7 +25,7 @@ def _flush(msg):
     (2, 1024, 2, dict(remap="bpermute"), "16x16x32"),         # only coordination rounds
 ])
 def test_tune(cfg, M, batch, kw, expect):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     dt, dims = c["dtype"], c["dims"]
     _flush(f"tune cfg{cfg} M={M} batch={batch} {kw}")
     A, Bs = synth.make_inputs(cfg, M=M, batch=batch)

@@ -320,7 +320,7 @@ def test_ternary_cascade_exact(cfg):
     """{-1,0,1} inputs at the workload's K and N: every partial sum is a small
     integer, so the result is independent of summation order and equals the
     int64 product rounded by the library cast (stage by stage)."""
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     A, Bs = synth.make_inputs(cfg, M=96, batch=min(2, c["batch"]), dist="ternary")
     D = oracle.cascade(c["dtype"], A, Bs)
     want = _exact_cascade(c["dtype"], A, Bs)
