@@ -385,3 +385,25 @@ def test_tile_count_beyond_32_bits_refused():
     st, h = _create(batch=1 << 10, M=1 << 20)           # 2^23 tiles of 128 rows: fine
     assert st == 0
     cf.lib().b2b_gemm_destroy(h)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the package raises ImportError at its first
+    call; there is no fallback path."""
+    pkg = tmp_path / "chip_fusion_amd"
+    pkg.mkdir()
+    src = os.path.join(ROOT, "chip_fusion_amd", "__init__.py")
+    (pkg / "__init__.py").write_text(open(src).read())
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import chip_fusion_amd as cf\n"
+            "for f in (cf.lib, lambda: cf.Plan('f16', 1, 128, 64, 64, 64)):\n"
+            "    try:\n"
+            "        f()\n"
+            "    except ImportError as e:\n"
+            "        print('ImportError', 'libb2b.so' in str(e))\n"
+            "    else:\n"
+            "        print('no error')\n") % str(tmp_path)
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.stdout.split() == ["ImportError", "True", "ImportError", "True"], r.stdout + r.stderr[-500:]
