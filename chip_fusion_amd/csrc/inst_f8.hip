@@ -7,7 +7,9 @@ B2B_F8_INSTANCE(DT_F16, DT_F16, 256, 0);
 B2B_F8_INSTANCE(DT_BF16, DT_BF16, 128, 1);
 B2B_F8_INSTANCE(DT_BF16, DT_BF16, 256, 0);
 B2B_F8_INSTANCE(DT_F16, DT_BF16, 128, 1);
+B2B_F8_INSTANCE(DT_F16, DT_BF16, 256, 0);
 B2B_F8_INSTANCE(DT_BF16, DT_F16, 128, 1);
+B2B_F8_INSTANCE(DT_BF16, DT_F16, 256, 0);
 // four waves (128-row tiles): two workgroups a CU when the weights and staging fit 80 KB
 B2B_F8_INSTANCE(DT_F16, DT_F16, 128, 1, 4);
 B2B_F8_INSTANCE(DT_BF16, DT_BF16, 128, 1, 4);

@@ -17,7 +17,7 @@ import torch
 import chip_fusion_amd as cf
 import oracle
 import synth
-from gpu_common import assert_close, nan_output
+from gpu_common import assert_close, check_fp8_stage, nan_output
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +33,14 @@ def test_fp8_conversion_matches_oracle():
                448.0, 460.0, 464.0, -464.0, 15.5, 17.0, 0.3, -0.3, 240.0, 248.0]
     x = np.concatenate([special, rng.standard_normal(256 - len(special)) * np.exp(rng.uniform(-8, 5, 256 - len(special)))])
     x = np.clip(x, -464, 464).astype(np.float32)
+    x[-4:] = [-2.0 ** -11, -3 * 2.0 ** -12, -1e-6, -0.0]      # negative values that round to zero
     got = cf.fp8_convert_probe(torch.from_numpy(x).cuda()).cpu().numpy()
     want = oracle.encode_fp8(x)
-    bad = got != want
+    # a negative value that rounds to zero: the oracle keeps the sign (-0,
+    # 0x80), the hardware gives +0 (0x00); the same number either way
+    zero = (want & 0x7F) == 0
+    assert np.all(got[zero] & 0x7F == 0) and np.all(got[zero & (x > 0)] == 0)
+    bad = (got != want) & ~zero
     assert not bad.any(), (x[bad][:8], got[bad][:8], want[bad][:8])
 
 
@@ -93,7 +98,9 @@ def test_fp8_second_gemm_parity(case):
     A, Bs = _inputs(types, batch, M, widths)
     got, info = _run(types, A, Bs)
     assert "mfma=32x32x16+f8_32x32x64" in info and "dtype=" + "/".join(types) in info, info
-    assert_close(types[2], got, oracle.cascade(list(types), A, Bs), f"fp8 {types} {widths}")
+    flips = check_fp8_stage(types, A, Bs[0], Bs[1], got, lambda a, bs: _run(types, a, bs)[0],
+                            f"fp8 {types} {widths}")
+    print(f"intermediates rounded the other way at a tie: {flips}", flush=True)
 
 
 @pytest.mark.parametrize("types", [("f16", "fp8", "f16"), ("bf16", "fp8", "bf16")])
