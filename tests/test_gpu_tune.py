@@ -54,8 +54,9 @@ def test_tune(cfg, M, batch, kw, expect):
                                           (("tf32", "tf32", "tf32"), (128, 128, 64))])
 def test_tune_typed_fp8_tf32(types, widths):
     """Tuning a plan with a type per stage, an fp8 second GEMM or tf32 keeps a
-    kernel of that same kind (its result equals the planned kernel's within
-    the tolerance and the plan then reproduces it)."""
+    kernel of that same kind (the instances differ only in waves per
+    workgroup); its result is within the tolerance and the plan then
+    reproduces it."""
     M, batch = 1024, 2
     _flush(f"tune {types} {widths}")
     if types[0] == "tf32":
@@ -74,10 +75,11 @@ def test_tune_typed_fp8_tf32(types, widths):
         Ad = cf.to_device(A, types[0])
         Bd = [cf.to_device(b, types[s]) for s, b in enumerate(Bs)]
         D = nan_output(types[-1], batch, M, widths[-1])
-    before = p.info().split(" grid=")[0]
+    kind = lambda info: {k: v for k, v in (kv.split("=", 1) for kv in info.split())
+                         if k in ("path", "dtype", "mfma", "remap", "dims")}
+    before = kind(p.info())
     p.tune([(Ad, Bd, D)], reps=3)
-    after = p.info().split(" grid=")[0]
-    assert after == before, (before, after)      # one kernel of the kind: it stays
+    assert kind(p.info()) == before, (before, p.info())    # a kernel of the same kind (any wave count)
     tuned = cf.to_host(D)
     if types[0] == "tf32":
         ref = oracle.cascade("tf32", A, Bs).astype(np.float64)
