@@ -135,6 +135,18 @@ const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     return best;
 }
 
+// A type per stage read at run time: the instance for nst GEMMs whose width
+// bound holds dims (the smallest), whatever the mixture.
+const KernelDesc* find_gen_rt(int nst, const int64_t* dims) {
+    const KernelDesc* best = nullptr;
+    for (const KernelDesc& d : b2b::registry()) {
+        if (d.tm != b2bk::TM_RUNTIME || d.nst != nst) continue;
+        if (!gen_fits(d, d.dtype, nst, dims, b2bk::TM_RUNTIME)) continue;
+        if (!best || d.maxd < best->maxd) best = &d;
+    }
+    return best;
+}
+
 // Among the fitting instances the smallest width bound wins; of two with the
 // same bound, the four-wave one where two of its workgroups fit a CU's LDS
 // (twice the tiles in flight per CU, measured 3 % faster), else the eight-wave one.
@@ -211,6 +223,7 @@ b2b_status_t launch_one(b2b_gemm_plan* p, int idx, const KernelDesc* k, const vo
     // widths of this launch's GEMMs: the whole cascade, or stage idx alone
     const int64_t* w = idx == 0 && !p->unfused ? p->dims : p->dims + idx;
     for (int i = 0; i <= k->nst; ++i) a.dims[i] = (int32_t)w[i];
+    a.tmask = p->tm;
     a.A = A;
     a.D = D;
     a.M = p->M;
@@ -338,6 +351,8 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
             // the fixed-width kernels cover up to three GEMMs
             if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
             p->fused = find_gen(dt, nst, dims, mode32, tm, passes);
+            // a mixture without a compiled mask: the types read at run time
+            if (!p->fused && typed) p->fused = find_gen_rt(nst, dims);
             p->mode = mode32;
         } else if ((flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO) {
             // the cheapest rearrangement compiled for this shape
@@ -552,13 +567,14 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
     // every compiled kernel that computes this cascade under the plan's flags
     std::vector<const KernelDesc*> cands;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.dtype != p->dtype || d.nst != p->nst || d.tm != p->tm || d.f8 != p->f8) continue;
+        const bool rt = p->tm >= 0 && d.tm == b2bk::TM_RUNTIME;   // run-time types serve any mixture
+        if ((!rt && (d.dtype != p->dtype || d.tm != p->tm)) || d.nst != p->nst || d.f8 != p->f8) continue;
         if (p->f8) {
             if (d.dtd == p->dtd && find_f8(p->dtype, p->dtd, p->dims)) cands.push_back(&d);
             continue;
         }
         if (d.rtw) {
-            if (p->orn || !gen_fits(d, p->dtype, p->nst, p->dims, p->tm, p->passes)) continue;
+            if (p->orn || !gen_fits(d, d.dtype, p->nst, p->dims, d.tm, p->passes)) continue;
         } else {
             if (s32 || d.orn != p->orn) continue;
             bool ok = true;

@@ -61,6 +61,7 @@ struct KArgs {
     int32_t tiles_per_batch;
     int32_t total_tiles;
     int32_t dims[kMaxStages + 1];   // widths K, N1, N2, ... (kernels with run-time widths)
+    int32_t tmask;                  // a 16-bit type per stage read at run time (bit s: bf16), where compiled so
     // coordination rounds per lane, p | give<<6 | r<<9: table 0 for the first
     // rearrangement (after GEMM0), table 1 for the later ones
     uint16_t sched[2][kMaxRounds][64];

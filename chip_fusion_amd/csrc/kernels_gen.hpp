@@ -59,13 +59,19 @@ template <> struct Ty32<DT_BF16> {
 // (page 1 lets each fused operator have its own data type): bit s set means
 // bf16, clear fp16, for the operands of GEMM s (A, B_s and the intermediate
 // rounded for it) and, at bit NST, for D.  DT_ is then the type of bit 0.
+// TM_ = TM_RUNTIME: the same mask read from the kernel arguments (one
+// instance for every mixture of a long cascade; each GEMM branches, uniformly,
+// to its type's instruction and each rounding selects its type).
 // OUT8_: D is written as fp8 E4M3 bytes (the first kernel of an unfused
 // cascade whose second GEMM is fp8), else in the last stage's 16-bit type.
+constexpr int TM_RUNTIME = -2;
+
 template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8, bool OUT8_ = false>
 struct GenCfg {
     static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_, TM = TM_;
     static constexpr bool OUT8 = OUT8_;
     static constexpr int DE = OUT8 ? 1 : 2;   // bytes of a D element
+    static constexpr bool RTM = TM_ == TM_RUNTIME;
     static constexpr int stype(int s) { return TM < 0 ? DT : (((TM >> s) & 1) ? DT_BF16 : DT_F16); }
     static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;     // K-steps, 32-column tiles
@@ -73,7 +79,8 @@ struct GenCfg {
     static_assert(DT != DT_F64, "the 32x32x16 instruction exists for 16-bit types");
     static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= kMaxStages && (PF == 0 || PF == 1), "config");
     static_assert(MODE == MODE_RELABEL || MODE == MODE_PERMLANE, "rearrangement");
-    static_assert(TM < 0 || (TM < (2 << NST) && stype(0) == DT), "type mask");
+    static_assert(TM == -1 || TM == TM_RUNTIME || (TM >= 0 && TM < (2 << NST) && stype(0) == DT), "type mask");
+    static_assert(!RTM || MODE == MODE_RELABEL, "run-time types are relabelled");
 };
 
 // One weight matrix in LDS: `rows` x `n` 16-bit values in blocks of 32
@@ -203,13 +210,20 @@ __device__ __forceinline__ void gen_arrange_a(u4_t (&a)[C::MKS]) {
         }
 }
 
+// a pair of fp32 values rounded to the 16-bit type NDT, or (NDT < 0) to the
+// type `bf` picks at run time
+template <int NDT>
+__device__ __forceinline__ unsigned gen_pack(float x, float y, bool bf) {
+    if constexpr (NDT >= 0) return Ty<NDT>::pack(x, y);
+    else return bf ? Ty<DT_BF16>::pack(x, y) : Ty<DT_F16>::pack(x, y);
+}
+
 // Result tile -> two K-steps of the next GEMM's operand (rounded to its type NDT).
 template <class C, int NDT>
-__device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t& o1) {
-    using T = Ty<NDT>;
+__device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t& o1, bool bf = false) {
     unsigned p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
+    for (int i = 0; i < 8; ++i) p[i] = gen_pack<NDT>(acc[2 * i], acc[2 * i + 1], bf);
     // K-step s: result registers 8s..8s+7 (packed p[4s..4s+3])
     if constexpr (C::MODE == MODE_PERMLANE) {
         // natural K order: half 0 keeps registers 8s..8s+3 and takes the
@@ -227,11 +241,11 @@ __device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t
 // 8a + 4h + 0..3; one lane-half swap per pair of blocks leaves 8 consecutive
 // columns per lane: n0 + 8h.. and n0 + 16 + 8h.. of row l%32.
 template <class C>
-__device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t& hi) {
-    using T = Ty<C::stype(C::NST)>;
+__device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t& hi, bool bf = false) {
+    constexpr int DDT = C::RTM ? -1 : C::stype(C::NST);
     unsigned p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = T::pack(acc[2 * i], acc[2 * i + 1]);
+    for (int i = 0; i < 8; ++i) p[i] = gen_pack<DDT>(acc[2 * i], acc[2 * i + 1], bf);
     swap32(p[0], p[2]);
     swap32(p[1], p[3]);
     swap32(p[4], p[6]);
@@ -247,11 +261,12 @@ __device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t&
 // pieces go straight to memory.
 template <class C>
 __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, const f16x_t& acc0, const f16x_t& acc1,
-                                               bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane) {
+                                               bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane,
+                                               bool bf = false) {
     const int m = lane & 31, h = lane >> 5;
     u4_t c[4];
-    gen_regroup_d<C>(acc0, c[0], c[1]);
-    gen_regroup_d<C>(acc1, c[2], c[3]);
+    gen_regroup_d<C>(acc0, c[0], c[1], bf);
+    gen_regroup_d<C>(acc1, c[2], c[3], bf);
     if (stg < 0) {
         // chunk q of this lane sits at column n0 + 16 q + 8 h
 #pragma unroll
@@ -443,36 +458,53 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         for (int j = 0; j < C::MKS; ++j) a[j] = a_in[j];
         gen_arrange_a<C>(a);
         const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, C::DE, t);
+        // run-time types: bit s of args.tmask (uniform) picks GEMM s's instruction and
+        // the type its result is rounded into for GEMM s+1 (bit NST: D)
+        auto bf_at = [&](int s) { return C::RTM && ((args.tmask >> s) & 1); };
         auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
             if constexpr (C::OUT8) gen_store_pair_f8(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
-            else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
+            else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane, bf_at(C::NST));
         };
+        // GEMM S on operand x with the sink: its compiled type, or a uniform
+        // branch to the type the run-time mask gives
+        auto gemm_at = [&](auto sc, const GenFrag& f, const u4_t (&x)[C::MKS], int ks, int nt, auto&& sink)
+                           __attribute__((always_inline)) {
+            constexpr int S = decltype(sc)::value;
+            if constexpr (C::RTM) {
+                if (bf_at(S)) gen_gemm<C, DT_BF16>(lds, f, x, ks, nt, sink);
+                else gen_gemm<C, DT_F16>(lds, f, x, ks, nt, sink);
+            } else {
+                gen_gemm<C, C::stype(S)>(lds, f, x, ks, nt, sink);
+            }
+        };
+        using S0 = std::integral_constant<int, 0>;
         if constexpr (C::NST == 1) {
-            gen_gemm<C, C::stype(0)>(lds, fr[0], a, ks0, dn / 32, to_d);
+            gemm_at(S0{}, fr[0], a, ks0, dn / 32, to_d);
         } else {
             // the operands of stage s come from oA (s odd) or oB (s even, s > 0),
             // rounded into stage s's type
             u4_t oA[C::MKS], oB[C::MKS];
-            auto to_ops = [&](u4_t (&o)[C::MKS], auto nt) __attribute__((always_inline)) {
+            auto to_ops = [&](u4_t (&o)[C::MKS], auto nt, bool bf) __attribute__((always_inline)) {
                 constexpr int NDT = decltype(nt)::value;
-                return [&o](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
-                    gen_to_operand<C, NDT>(a0, o[2 * tt], o[2 * tt + 1]);
-                    if (two) gen_to_operand<C, NDT>(a1, o[2 * tt + 2], o[2 * tt + 3]);
+                return [&o, bf](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
+                    gen_to_operand<C, NDT>(a0, o[2 * tt], o[2 * tt + 1], bf);
+                    if (two) gen_to_operand<C, NDT>(a1, o[2 * tt + 2], o[2 * tt + 3], bf);
                 };
             };
-            using T1 = std::integral_constant<int, C::stype(1)>;
-            gen_gemm<C, C::stype(0)>(lds, fr[0], a, ks0, d[1] / 32, to_ops(oA, T1{}));
+            using T1 = std::integral_constant<int, C::RTM ? -1 : C::stype(1)>;
+            gemm_at(S0{}, fr[0], a, ks0, d[1] / 32, to_ops(oA, T1{}, bf_at(1)));
             gen_static_for<1, C::NST - 1>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int S = decltype(sc)::value;
-                using TN = std::integral_constant<int, C::stype(S + 1)>;
+                using TN = std::integral_constant<int, C::RTM ? -1 : C::stype(S + 1)>;
                 if constexpr (S % 2 == 1)
-                    gen_gemm<C, C::stype(S)>(lds, fr[S], oA, d[S] / 16, d[S + 1] / 32, to_ops(oB, TN{}));
+                    gemm_at(sc, fr[S], oA, d[S] / 16, d[S + 1] / 32, to_ops(oB, TN{}, bf_at(S + 1)));
                 else
-                    gen_gemm<C, C::stype(S)>(lds, fr[S], oB, d[S] / 16, d[S + 1] / 32, to_ops(oA, TN{}));
+                    gemm_at(sc, fr[S], oB, d[S] / 16, d[S + 1] / 32, to_ops(oA, TN{}, bf_at(S + 1)));
             });
             constexpr int L = C::NST - 1;
-            if constexpr (L % 2 == 1) gen_gemm<C, C::stype(L)>(lds, fr[L], oA, d[L] / 16, dn / 32, to_d);
-            else gen_gemm<C, C::stype(L)>(lds, fr[L], oB, d[L] / 16, dn / 32, to_d);
+            using SL = std::integral_constant<int, L>;
+            if constexpr (L % 2 == 1) gemm_at(SL{}, fr[L], oA, d[L] / 16, dn / 32, to_d);
+            else gemm_at(SL{}, fr[L], oB, d[L] / 16, dn / 32, to_d);
         }
     };
 

@@ -178,8 +178,9 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
  *                 b2b_chain_create plans)
  *   other arguments as for b2b_chain_create
  * Mixed types run relabelled on the 32x32x16 run-time-width kernels: fused
- * for two GEMMs (widths up to 256) and three (up to 128), and unfused for any
- * length (each GEMM then changes type on its way out).  NOT_SUPPORTED for fp64
+ * for two or three GEMMs (widths up to 256) and four to six (up to 128), all
+ * weights together within 160 KB, and unfused for any length (each GEMM then
+ * changes type on its way out).  NOT_SUPPORTED for fp64
  * mixed with a 16-bit type, B2B_FLAG_ORIENT_N, a rearrangement other than
  * RELABEL or AUTO, or widths those kernels do not cover; otherwise errors as
  * for b2b_chain_create.  Runs with b2b_chain_run (or b2b_gemm_run for two or

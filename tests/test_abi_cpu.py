@@ -239,6 +239,11 @@ def _typed(dtypes, widths, flags=0, batch=1, M=128):
     ((1, 0, 1), (256, 256, 64), dict(dtype="bf16/f16/bf16", mfma="32x32x16", lds_bytes="163840")),
     ((0, 1, 0, 1), (128, 96, 128, 64), dict(dtype="f16/bf16/f16/bf16", mfma="32x32x16", launches="1")),
     ((0, 0, 0, 1), (128, 128, 128, 64), dict(dtype="f16/f16/f16/bf16", path="fused")),
+    # mixtures without a compiled mask: the types read at run time
+    ((0, 1, 1, 0, 0), (128, 128, 128, 128, 64), dict(dtype="f16/bf16/bf16/f16/f16", mfma="32x32x16")),
+    ((1, 0, 1, 0, 1, 0, 1), (64, 96, 128, 32, 128, 64, 128), dict(dtype="bf16/f16/bf16/f16/bf16/f16/bf16")),
+    ((0, 1, 0, 1), (256, 64, 256, 64), dict(dtype="f16/bf16/f16/bf16", path="fused")),
+    ((0, 1, 0, 1, 1), (64, 32, 32, 32, 64), dict(dtype="f16/bf16/f16/bf16/bf16", path="fused")),
     # one type throughout: the plan of b2b_chain_create
     ((1, 1, 1), (128, 128, 128), dict(dtype="bf16", mfma="16x16x32")),
     ((2, 2, 2), (64, 64, 64), dict(dtype="f64", mfma="f64_16x16x4")),
@@ -255,8 +260,8 @@ def test_typed_plan_selection(dtypes, widths, expect):
     ((0, 1, 0), (128, 128, 128), 2 << 4, 2),                      # lane-half swaps: not compiled typed
     ((0, 1, 0), (128, 128, 128), 2 | (3 << 4), 2),                # orientation N
     ((0, 2, 0), (64, 64, 64), 0, 2),                              # fp64 mixed with a 16-bit type
-    ((0, 1, 0, 1, 0), (128, 128, 128, 128, 64), 0, 2),            # fused typed: up to three GEMMs
-    ((0, 1, 0, 1), (256, 128, 128, 64), 0, 2),                    # three typed GEMMs: widths up to 128
+    ((0, 1, 0, 1, 0, 1, 0, 1), (128,) * 8, 0, 2),                 # fused typed: up to six GEMMs
+    ((0, 1, 0, 1, 0), (256, 128, 128, 128, 64), 0, 2),            # four or more typed GEMMs: widths up to 128
     ((0, 5, 0), (128, 128, 128), 0, 2),                           # unknown type
 ])
 def test_typed_rejects(dtypes, widths, flags, status):

@@ -52,6 +52,11 @@ FUSED = [
     (("f16", "bf16", "f16", "bf16"), 2, 333, (128, 96, 128, 64)),
     (("bf16", "f16", "f16", "f16"), 1, 257, (64, 128, 32, 128)),
     (("f16", "f16", "f16", "bf16"), 2, 100, (128, 128, 128, 64)),
+    # mixtures read at run time: three GEMMs past 128 wide, four to six GEMMs
+    (("f16", "bf16", "f16", "bf16"), 2, 300, (256, 64, 256, 64)),
+    (("f16", "bf16", "bf16", "f16", "f16"), 2, 333, (128, 128, 128, 128, 64)),
+    (("bf16", "f16", "bf16", "f16", "bf16", "f16"), 1, 513, (64, 96, 128, 32, 128, 64)),
+    (("bf16", "f16", "bf16", "f16", "bf16", "f16", "bf16"), 2, 257, (64, 96, 128, 32, 128, 64, 128)),
 ]
 
 
@@ -95,6 +100,7 @@ def _integer_inputs(types, widths, lims, batch=2, M=300, seed=23):
     (("bf16", "f16", "bf16"), (128, 128, 64), (7, 7), {}),
     (("f16", "bf16", "f16", "bf16"), (64, 64, 32, 64), (3, 3, 1), {}),
     (("f16", "bf16", "f16"), (128, 128, 64), (3, 3), {"unfused": True}),
+    (("f16", "bf16", "f16", "bf16", "bf16"), (64, 32, 32, 32, 64), (3, 2, 1, 1), {}),  # run-time types
 ])
 def test_typed_integer_exact(types, widths, lims, kw):
     _flush(f"typed exact {types} widths={widths} {kw}")
