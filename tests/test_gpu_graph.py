@@ -26,6 +26,7 @@ CASES = [
     ("32x32x16", "f16", (128, 96, 128), {"mfma32": True}),
     ("tf32", "tf32", (64, 128, 64), {}),
     ("typed", ["f16", "bf16", "f16"], (128, 128, 64), {}),
+    ("typed, types read at run time", ["bf16", "f16", "f16", "bf16", "f16"], (64, 96, 64, 128, 64), {}),
     ("fp8 stage", ["f16", "fp8", "f16"], (64, 128, 64), {}),
     ("unfused", "bf16", (128, 128, 128), {"unfused": True}),
 ]

@@ -1,6 +1,6 @@
 """Seeded random sweep over the run-time-width kernels: widths drawn within
 each family's granules and LDS bound, M from 1 to a few thousand (ragged),
-batches 1-4, one to five GEMMs, both rearrangements, random type masks, tf32
+batches 1-4, one to six GEMMs, both rearrangements, random type masks, tf32
 with three and four passes, fp8 second GEMMs; every case against the
 oracle."""
 import math
@@ -40,12 +40,12 @@ def _case(i):
         maxd = 128 if (mode == "permlane" and nst > 3) else (256 if nst <= 3 else 128)
         return kind, [dt] * (nst + 1), _widths(rng, nst, 32, maxd, 2), M, batch, dict(mfma32=True, remap=mode)
     if kind == "typed":
-        nst = int(rng.integers(2, 4))
+        nst = int(rng.integers(2, 7))
         while True:
             types = [str(t) for t in rng.choice(["f16", "bf16"], nst + 1)]
             if len(set(types)) > 1:
                 break
-        return kind, types, _widths(rng, nst, 32, 256 if nst == 2 else 128, 2), M, batch, {}
+        return kind, types, _widths(rng, nst, 32, 256 if nst <= 3 else 128, 2), M, batch, {}
     if kind == "tf32":
         nst = int(rng.integers(1, 4))
         return kind, ["tf32"] * (nst + 1), _widths(rng, nst, 32, 128, 4), M, batch, dict(tf32_exact=bool(rng.random() < 0.5))
@@ -57,7 +57,7 @@ def _case(i):
     return kind, [t0, "fp8", td], w, M, batch, {}
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(50))
 def test_sweep_runtime_widths(i):
     kind, types, widths, M, batch, kw = _case(i)
     _flush(f"sweep {i}: {kind} types={types} widths={widths} M={M} batch={batch} {kw}")

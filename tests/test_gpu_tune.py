@@ -51,6 +51,8 @@ def test_tune(cfg, M, batch, kw, expect):
 
 @pytest.mark.parametrize("types,widths", [(("f16", "bf16", "f16"), (128, 128, 128)),
                                           (("f16", "fp8", "f16"), (128, 128, 128)),
+                                          # compiled masks and the run-time-typed instance compete
+                                          (("f16", "bf16", "f16", "bf16"), (128, 128, 128, 64)),
                                           (("tf32", "tf32", "tf32"), (128, 128, 64))])
 def test_tune_typed_fp8_tf32(types, widths):
     """Tuning a plan with a type per stage, an fp8 second GEMM or tf32 keeps a
@@ -62,7 +64,7 @@ def test_tune_typed_fp8_tf32(types, widths):
     if types[0] == "tf32":
         A = synth.tensor(5, 0, (batch, M, widths[0]), "tf32", "normal")
         Bs = [synth.tensor(5, 1 + s, (batch, widths[s], widths[s + 1]), "tf32", "normal", widths[s] ** -0.5)
-              for s in range(2)]
+              for s in range(len(widths) - 1)]
         p = cf.Chain("tf32", batch, M, list(widths))
         Ad = torch.from_numpy(A).cuda()
         Bd = [torch.from_numpy(b).cuda() for b in Bs]
@@ -70,7 +72,7 @@ def test_tune_typed_fp8_tf32(types, widths):
     else:
         A = synth.tensor(5, 0, (batch, M, widths[0]), types[0], "normal")
         Bs = [synth.tensor(5, 1 + s, (batch, widths[s], widths[s + 1]), types[s], "normal", widths[s] ** -0.5)
-              for s in range(2)]
+              for s in range(len(widths) - 1)]
         p = cf.Chain(list(types), batch, M, list(widths))
         Ad = cf.to_device(A, types[0])
         Bd = [cf.to_device(b, types[s]) for s, b in enumerate(Bs)]

@@ -114,13 +114,17 @@ def test_typed_integer_exact(types, widths, lims, kw):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
 
 
-def test_typed_padded_and_broadcast():
-    types, M, batch, widths = ("bf16", "f16", "f16", "bf16"), 300, 3, (64, 96, 128, 32)
+@pytest.mark.parametrize("types,widths", [
+    (("bf16", "f16", "f16", "bf16"), (64, 96, 128, 32)),
+    (("f16", "bf16", "bf16", "f16", "bf16"), (64, 96, 128, 32, 64)),     # run-time types
+])
+def test_typed_padded_and_broadcast(types, widths):
+    M, batch = 300, 3
     _flush(f"typed strided {types} widths={widths}")
     A, Bs = _normal_inputs(types, batch, M, widths)
     Bs = [b.copy() for b in Bs]
     Bs[1][:] = Bs[1][0]                       # B_1 broadcast to every batch
-    nst = 3
+    nst = len(widths) - 1
     lda, ldd = widths[0] + 8, widths[-1] + 16
     ldb = [widths[s + 1] + 8 * (s + 1) for s in range(nst)]
     sA, sD = M * lda + 8, M * ldd + 24
@@ -136,8 +140,10 @@ def test_typed_padded_and_broadcast():
     Ad = padded(A, batch, M, widths[0], lda, sA, types[0])
     Bd = [padded(Bs[s] if s != 1 else Bs[s][:1], batch if s != 1 else 1, widths[s], widths[s + 1], ldb[s], sB[s],
                  types[s]) for s in range(nst)]
-    Dd = torch.full(((batch - 1) * sD + M * ldd + 64,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Dd = torch.full(((batch - 1) * sD + M * ldd + 64,), float("nan"), dtype=cf.TORCH_DTYPES[cf.DTYPES[types[-1]]],
+                    device="cuda")
     p = cf.Chain(list(types), batch, M, list(widths), ld=[lda] + ldb + [ldd], batch_stride=[sA] + sB + [sD])
+    assert "path=fused" in p.info(), p.info()
     p.run(Ad, *Bd, D=Dd)
     torch.cuda.synchronize()
     p.close()
