@@ -260,12 +260,17 @@ def main():
         dt1 = time.perf_counter() - t0
         n2 = int(min(c["batch"] * c["M"], max(n, n * args.cpu_seconds / max(dt1, 1e-6))))
         idx = np.linspace(0, c["batch"] * c["M"] - 1, n2).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.cascade(otype, A, Bs, rows=idx, nthreads=nthreads)
-        el = time.perf_counter() - t0
-        cpu = {"value": n2 * per_row / el / 1e12, "unit": "TFLOP/s", "cores": nthreads,
-               "kind": "oracle", "seconds": el,
-               "sample": f"{n2} of {c['batch'] * c['M']} rows spread over all batches, full cascade per row"}
+        # a sample that is the whole workload and ends early is repeated until the target time
+        passes, el = 0, 0.0
+        while passes == 0 or (n2 == c["batch"] * c["M"] and el < args.cpu_seconds):
+            t0 = time.perf_counter()
+            oracle.cascade(otype, A, Bs, rows=idx, nthreads=nthreads)
+            el += time.perf_counter() - t0
+            passes += 1
+        what = (f"{n2} of {c['batch'] * c['M']} rows spread over all batches" if passes == 1 else
+                f"{passes} passes over all {n2} rows")
+        cpu = {"value": passes * n2 * per_row / el / 1e12, "unit": "TFLOP/s", "cores": nthreads,
+               "kind": "oracle", "seconds": el, "sample": what + ", full cascade per row"}
 
     out = {
         "metric": "fused B2B-GEMM TFLOP/s (" + dt + ") + % of MI355X dense MFMA peak, 1 GPU",
