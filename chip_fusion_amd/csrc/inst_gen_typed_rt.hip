@@ -1,5 +1,5 @@
 // Cascades with a 16-bit type per stage read at run time (one instance for
-// every mixture): three to six GEMMs, relabelled.  The two- and three-GEMM
+// every mixture): three to eight GEMMs, relabelled.  The two- and three-GEMM
 // mixtures up to 128 wide have compiled masks (inst_gen_typed*.hip).
 #include "registry.hpp"
 using namespace b2bk;
@@ -8,3 +8,5 @@ B2B_GEN_INSTANCE(DT_F16, 3, 256, MODE_RELABEL, 0, TM_RUNTIME);
 B2B_GEN_INSTANCE(DT_F16, 4, 128, MODE_RELABEL, 1, TM_RUNTIME);
 B2B_GEN_INSTANCE(DT_F16, 5, 128, MODE_RELABEL, 1, TM_RUNTIME);
 B2B_GEN_INSTANCE(DT_F16, 6, 128, MODE_RELABEL, 1, TM_RUNTIME);
+B2B_GEN_INSTANCE(DT_F16, 7, 128, MODE_RELABEL, 1, TM_RUNTIME);
+B2B_GEN_INSTANCE(DT_F16, 8, 128, MODE_RELABEL, 1, TM_RUNTIME);

@@ -156,8 +156,9 @@ b2b_status_t b2b_gemm_run(b2b_gemm_t plan, const void* A, const void* B0, const 
  *                 dense; 0 for a B_s broadcasts it
  *   flags         as for b2b_gemm_create
  * Up to three GEMMs this plans exactly what b2b_gemm_create plans.  Longer
- * fused cascades run on the run-time-width kernels (fp16/bf16 up to six GEMMs,
- * K and the widths multiples of 32, each at most 256; fp64 up to five, each at
+ * fused cascades run on the run-time-width kernels (fp16/bf16 up to eight GEMMs,
+ * K and the widths multiples of 32, each at most 256, or 128 for seven and
+ * eight GEMMs; fp64 up to five, each at
  * most 64; all weights together at most 160 KB); the unfused path takes any
  * cascade whose single GEMMs are covered.  Errors as for b2b_gemm_create; INVALID_VALUE also for nst outside
  * 1..8 or a NULL widths.
@@ -178,7 +179,7 @@ b2b_status_t b2b_chain_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch
  *                 b2b_chain_create plans)
  *   other arguments as for b2b_chain_create
  * Mixed types run relabelled on the 32x32x16 run-time-width kernels: fused
- * for two or three GEMMs (widths up to 256) and four to six (up to 128), all
+ * for two or three GEMMs (widths up to 256) and four to eight (up to 128), all
  * weights together within 160 KB, and unfused for any length (each GEMM then
  * changes type on its way out).  NOT_SUPPORTED for fp64
  * mixed with a 16-bit type, B2B_FLAG_ORIENT_N, a rearrangement other than

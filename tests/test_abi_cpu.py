@@ -205,6 +205,8 @@ def test_chain_create_rejects(kw, status):
      dict(mfma="32x32x16", dims="64x96x128x32x128x64x128", remap="permlane")),
     (dict(dtype=1, widths=(64, 96, 160, 32, 224, 64, 128)),
      dict(mfma="32x32x16", dims="64x96x160x32x224x64x128", remap="relabel")),
+    (dict(widths=(64, 96, 64, 128, 32, 64, 96, 64)), dict(path="fused", dims="64x96x64x128x32x64x96x64", launches="1")),
+    (dict(dtype=1, widths=(64, 64, 128, 64, 96, 32, 128, 64, 96)), dict(path="fused", mfma="32x32x16", launches="1")),
     # up to three GEMMs the chain call plans what b2b_gemm_create plans
     (dict(widths=(128, 128, 128)), dict(mfma="16x16x32", remap="relabel", mt="1")),
     (dict(widths=(128, 128, 128, 64)), dict(mfma="16x16x32", remap="relabel")),
@@ -243,6 +245,7 @@ def _typed(dtypes, widths, flags=0, batch=1, M=128):
     ((0, 1, 1, 0, 0), (128, 128, 128, 128, 64), dict(dtype="f16/bf16/bf16/f16/f16", mfma="32x32x16")),
     ((1, 0, 1, 0, 1, 0, 1), (64, 96, 128, 32, 128, 64, 128), dict(dtype="bf16/f16/bf16/f16/bf16/f16/bf16")),
     ((0, 1, 0, 1), (256, 64, 256, 64), dict(dtype="f16/bf16/f16/bf16", path="fused")),
+    ((1, 0, 0, 1, 1, 0, 1, 0, 1), (64, 64, 128, 64, 96, 32, 128, 64, 96), dict(path="fused", launches="1")),
     ((0, 1, 0, 1, 1), (64, 32, 32, 32, 64), dict(dtype="f16/bf16/f16/bf16/bf16", path="fused")),
     # one type throughout: the plan of b2b_chain_create
     ((1, 1, 1), (128, 128, 128), dict(dtype="bf16", mfma="16x16x32")),
@@ -260,7 +263,8 @@ def test_typed_plan_selection(dtypes, widths, expect):
     ((0, 1, 0), (128, 128, 128), 2 << 4, 2),                      # lane-half swaps: not compiled typed
     ((0, 1, 0), (128, 128, 128), 2 | (3 << 4), 2),                # orientation N
     ((0, 2, 0), (64, 64, 64), 0, 2),                              # fp64 mixed with a 16-bit type
-    ((0, 1, 0, 1, 0, 1, 0, 1), (128,) * 8, 0, 2),                 # fused typed: up to six GEMMs
+    ((0, 1, 0, 1, 0, 1, 0, 1), (128,) * 8, 0, 2),                 # 224 KB of weights
+    ((0, 1, 0, 1, 0, 1, 0, 1, 0, 1), (64,) * 10, 0, 1),           # nine GEMMs
     ((0, 1, 0, 1, 0), (256, 128, 128, 128, 64), 0, 2),            # four or more typed GEMMs: widths up to 128
     ((0, 5, 0), (128, 128, 128), 0, 2),                           # unknown type
 ])

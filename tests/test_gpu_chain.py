@@ -50,12 +50,15 @@ CHAINS = [
     (1, 513, (64, 96, 128, 32, 128, 64, 128)),         # six GEMMs
     (3, 260, (96, 224, 64, 160, 32)),                  # widths above 128
     (1, 700, (256, 64, 256, 32, 96, 128)),             # five GEMMs
+    (2, 300, (64, 96, 64, 128, 32, 64, 96, 64)),       # seven GEMMs
+    (1, 513, (64, 64, 128, 64, 96, 32, 128, 64, 96)),  # eight GEMMs
 ]
 
 
-# lane-half swaps are compiled for longer chains up to 128 wide
+# lane-half swaps are compiled for chains of up to six GEMMs up to 128 wide
 LONG_CASES = [(c, dt, mode) for c in range(len(CHAINS)) for dt in ("f16", "bf16")
-              for mode in ("relabel", "permlane") if mode == "relabel" or max(CHAINS[c][2]) <= 128]
+              for mode in ("relabel", "permlane")
+              if mode == "relabel" or (max(CHAINS[c][2]) <= 128 and len(CHAINS[c][2]) <= 7)]
 
 
 @pytest.mark.parametrize("case,dtype,mode", LONG_CASES)

@@ -57,6 +57,8 @@ FUSED = [
     (("f16", "bf16", "bf16", "f16", "f16"), 2, 333, (128, 128, 128, 128, 64)),
     (("bf16", "f16", "bf16", "f16", "bf16", "f16"), 1, 513, (64, 96, 128, 32, 128, 64)),
     (("bf16", "f16", "bf16", "f16", "bf16", "f16", "bf16"), 2, 257, (64, 96, 128, 32, 128, 64, 128)),
+    (("f16", "f16", "bf16", "f16", "bf16", "bf16", "f16", "bf16"), 2, 300, (64, 96, 64, 128, 32, 64, 96, 64)),
+    (("bf16", "f16", "f16", "bf16", "bf16", "f16", "bf16", "f16", "bf16"), 1, 513, (64, 64, 128, 64, 96, 32, 128, 64, 96)),
 ]
 
 
