@@ -90,6 +90,37 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _torch_dtype(code):
+    return torch.uint8 if code == FP8 else TORCH_DTYPES[code]
+
+
+def _dense(widths, batch, M, ld, batch_stride):
+    """Leading dimensions and batch strides of every operand (A, B_0..B_{n-1},
+    D), as the library takes them: the given ones, or the dense defaults."""
+    rows = [M] + list(widths[:-1]) + [M]
+    width = [widths[0]] + list(widths[1:]) + [widths[-1]]
+    L = list(ld) if ld is not None else width
+    S = list(batch_stride) if batch_stride is not None else [r * l for r, l in zip(rows, L)]
+    return rows, width, L, S
+
+
+def _check_operand(t, name, dtype, batch, rows, width, ld, bs):
+    """Raises ValueError unless tensor t can hold operand `name` as the plan
+    addresses it: a device tensor of the plan's type whose memory from its
+    first element covers (batch - 1) * bs + (rows - 1) * ld + width elements.
+    The kernels address by the plan's sizes, not by the tensor's shape, so a
+    smaller tensor would be read or written past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: a torch tensor is expected, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {dtype} expected, got {t.dtype}")
+    need = (batch - 1) * bs + (rows - 1) * ld + width
+    have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if have < need:
+        raise ValueError(f"{name}: the plan addresses {need} elements from its first one, "
+                         f"the tensor's memory holds {have}")
+
+
 class Plan:
     """A planned cascade D = rnd(rnd(A.B0).B1)[.B2] (b2b_gemm_create)."""
 
@@ -106,10 +137,31 @@ class Plan:
                                    arr(*batch_stride) if batch_stride is not None else None, flags)
         _check(st, "b2b_gemm_create")
         self._h = h
+        nst = len(self.dims) - 1
+        if ld is not None or batch_stride is not None:
+            pick = lambda v: None if v is None else [v[i] for i in range(5) if not (i == 3 and nst == 2)]
+            ld, batch_stride = pick(ld), pick(batch_stride)
+        self._layout = _dense(self.dims, batch, M, ld, batch_stride)
+        self._types = [self.dtype] * (nst + 1)
+
+    def _check_tensors(self, A, Bs, D):
+        """ValueError before any launch if a tensor does not fit the plan."""
+        rows, width, L, S = self._layout
+        nst = len(self.dims) - 1
+        if len(Bs) != nst:
+            raise ValueError(f"{nst} weight matrices expected, got {len(Bs)}")
+        ts = self._types
+        ops = [("A", A, ts[0])] + [(f"B{i}", b, ts[i]) for i, b in enumerate(Bs)] + [("D", D, ts[-1])]
+        for i, (name, t, code) in enumerate(ops):
+            _check_operand(t, name, _torch_dtype(code), self.batch, rows[i], width[i], L[i], S[i])
+        for name, t, _ in ops:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name}: a device (cuda) tensor is expected, got one on {t.device}")
 
     def run(self, A, B0, B1, B2=None, D=None, stream=None):
         if D is None:
             D = torch.empty((self.batch, self.M, self.dims[-1]), dtype=A.dtype, device=A.device)
+        self._check_tensors(A, [B0, B1] + ([B2] if B2 is not None else []), D)
         st = lib().b2b_gemm_run(self._h, _ptr(A), _ptr(B0), _ptr(B1), _ptr(B2), _ptr(D),
                                 _stream_ptr(stream))
         _check(st, "b2b_gemm_run")
@@ -120,9 +172,8 @@ class Plan:
         timed over `sets`, a list of (A, [B_0, ..], D) representative of the
         use; every D holds the kept kernel's result afterwards."""
         nst = len(self.dims) - 1
-        for _, Bs, _ in sets:
-            if len(Bs) != nst:
-                raise ValueError(f"{nst} weight matrices expected, got {len(Bs)}")
+        for a, Bs, d in sets:
+            self._check_tensors(a, list(Bs), d)
         n = len(sets)
         As = (ctypes.c_void_p * n)(*[a.data_ptr() for a, _, _ in sets])
         Bp = (ctypes.c_void_p * (n * nst))(*[b.data_ptr() for _, Bs, _ in sets for b in Bs])
@@ -177,6 +228,8 @@ class Chain(Plan):
             st = lib().b2b_chain_create(ctypes.byref(h), self.dtype, batch, M, nst, w, lds, bss, flags)
             _check(st, "b2b_chain_create")
         self._h = h
+        self._layout = _dense(self.dims, batch, M, ld, batch_stride)
+        self._types = list(self.dtypes) if typed else [self.dtype] * (nst + 1)
 
     def run(self, A, *Bs, D=None, stream=None):
         if len(Bs) != len(self.dims) - 1:
@@ -184,6 +237,7 @@ class Chain(Plan):
         if D is None:
             dt = TORCH_DTYPES[self.dtypes[-1]] if self.dtypes else A.dtype
             D = torch.empty((self.batch, self.M, self.dims[-1]), dtype=dt, device=A.device)
+        self._check_tensors(A, list(Bs), D)
         ptrs = (ctypes.c_void_p * len(Bs))(*[b.data_ptr() for b in Bs])
         st = lib().b2b_chain_run(self._h, _ptr(A), ptrs, _ptr(D), _stream_ptr(stream))
         _check(st, "b2b_chain_run")

@@ -121,13 +121,20 @@ const KernelDesc* find_f8a(int dtd, const int64_t* dims) {
     return best;
 }
 
+// Whether fp8-second-GEMM instance d computes the cascade dims[0..2] of a
+// first GEMM in dt with D in dtd: the granules, d's own width bound (the
+// kernel walks at most maxd of K and of each N), and both weights in LDS.
+bool f8_fits(const KernelDesc& d, int dt, int dtd, const int64_t* dims) {
+    if (d.f8 != 1 || d.dtype != dt || d.dtd != dtd) return false;
+    if (dims[0] % 32 || dims[1] % 64 || dims[2] % 32) return false;
+    if (dims[0] > d.maxd || dims[1] > d.maxd || dims[2] > d.maxd) return false;
+    return dims[0] * dims[1] * 2 + dims[1] * dims[2] <= 160 * 1024;
+}
+
 const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.f8 != 1 || d.dtype != dt || d.dtd != dtd) continue;
-        if (dims[0] % 32 || dims[1] % 64 || dims[2] % 32) continue;
-        if (dims[0] > d.maxd || dims[1] > d.maxd || dims[2] > d.maxd) continue;
-        if (dims[0] * dims[1] * 2 + dims[1] * dims[2] > 160 * 1024) continue;
+        if (!f8_fits(d, dt, dtd, dims)) continue;
         if (!best || d.maxd < best->maxd ||
             (d.maxd == best->maxd && wave_rank(d, dims, 2) < wave_rank(*best, dims, 2)))
             best = &d;
@@ -320,6 +327,10 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         if ((L[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
         S[i] = Sin ? Sin[i] : rows * L[i];
         if (S[i] < 0 || (S[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
+        // the kernels address a wave's rows of A or D (at most 32) and a whole
+        // weight matrix through one buffer resource, with 32-bit signed offsets
+        const int64_t span_rows = (i == 0 || i == n - 1) ? std::min<int64_t>(M, 32) : rows;
+        if (span_rows * L[i] * eo > (int64_t)INT32_MAX) return B2B_ERROR_INVALID_VALUE;
     }
     if (batch > 1 && (S[0] == 0 || S[n - 1] < M * L[n - 1])) return B2B_ERROR_INVALID_VALUE;
 
@@ -429,11 +440,11 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
 }
 
 // Enqueues the cascade; B holds the plan's nst weight pointers.
-b2b_status_t run_impl(b2b_gemm_t p, const void* A, const void* const* B, void* D, void* stream) {
+b2b_status_t run_impl(b2b_gemm_t p, const void* A, const void* const* B, void* D, hipStream_t stream) {
     if (!A || !D || (uintptr_t)A % 16 || (uintptr_t)D % 16 || A == (const void*)D) return B2B_ERROR_INVALID_VALUE;
     for (int s = 0; s < p->nst; ++s)
         if (!B[s] || (uintptr_t)B[s] % 16 || B[s] == (const void*)D) return B2B_ERROR_INVALID_VALUE;
-    hipStream_t st = (hipStream_t)stream;
+    hipStream_t st = stream;
     const int nd = p->nst + 1;    // index of D's leading dimension and stride
     if (!p->unfused)
         return launch_one(p, 0, p->fused, A, p->ld[0], p->bs[0], B, p->ld + 1, p->bs + 1, D, p->ld[nd],
@@ -532,14 +543,14 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
 }
 
 b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const void* B1,
-                          const void* B2, void* D, void* stream) {
+                          const void* B2, void* D, hipStream_t stream) {
     if (!p || p->nst < 2 || p->nst > 3) return B2B_ERROR_INVALID_VALUE;
     if ((p->nst == 3) != (B2 != nullptr)) return B2B_ERROR_INVALID_VALUE;
     const void* Bs[3] = {B0, B1, B2};
     return run_impl(p, A, Bs, D, stream);
 }
 
-b2b_status_t b2b_chain_run(b2b_gemm_t p, const void* A, const void* const* B, void* D, void* stream) {
+b2b_status_t b2b_chain_run(b2b_gemm_t p, const void* A, const void* const* B, void* D, hipStream_t stream) {
     if (!p || !B) return B2B_ERROR_INVALID_VALUE;
     return run_impl(p, A, B, D, stream);
 }
@@ -559,7 +570,7 @@ b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {
 }
 
 b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, const void* const* B,
-                           void* const* D, void* stream, int32_t reps) {
+                           void* const* D, hipStream_t stream, int32_t reps) {
     if (!p || nsets < 1 || !A || !B || !D || reps < 1 || reps > 10000) return B2B_ERROR_INVALID_VALUE;
     if (p->unfused) return B2B_ERROR_NOT_SUPPORTED;
     const bool any_mode = (p->flags & B2B_REMAP_MASK) == B2B_REMAP_AUTO;
@@ -570,7 +581,8 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
         const bool rt = p->tm >= 0 && d.tm == b2bk::TM_RUNTIME;   // run-time types serve any mixture
         if ((!rt && (d.dtype != p->dtype || d.tm != p->tm)) || d.nst != p->nst || d.f8 != p->f8) continue;
         if (p->f8) {
-            if (d.dtd == p->dtd && find_f8(p->dtype, p->dtd, p->dims)) cands.push_back(&d);
+            // only instances whose own bounds hold the plan's widths
+            if (f8_fits(d, p->dtype, p->dtd, p->dims)) cands.push_back(&d);
             continue;
         }
         if (d.rtw) {
@@ -587,7 +599,7 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
         cands.push_back(&d);
     }
     if (cands.empty()) return B2B_ERROR_NOT_SUPPORTED;
-    hipStream_t st = (hipStream_t)stream;
+    hipStream_t st = stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
         if (e0) (void)hipEventDestroy(e0);
@@ -769,7 +781,7 @@ b2b_status_t b2b_remap_compile(int32_t elems, const int32_t* src, const int32_t*
 }
 
 b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, const int32_t* q, const int32_t* r,
-                               const uint32_t* in, uint32_t* out, void* stream) {
+                               const uint32_t* in, uint32_t* out, hipStream_t stream) {
     if (elems < 1 || elems > b2bk::kExecMax || rounds != elems || !p || !q || !r || !in || !out)
         return B2B_ERROR_INVALID_VALUE;
     b2bk::ExecArgs a;
@@ -796,12 +808,12 @@ b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, 
             a.code[j][i] = (uint16_t)(p[k] | (give[i] << 6) | (r[k] << 10));
         }
     }
-    hipLaunchKernelGGL(b2bk::remap_exec_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, in, out, a);
+    hipLaunchKernelGGL(b2bk::remap_exec_kernel<>, dim3(1), dim3(64), 0, stream, in, out, a);
     return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
 }
 
 b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, const void* in, void* out,
-                             void* stream) {
+                             hipStream_t stream) {
     int dt;
     if (shape == B2B_SHAPE_F16_16X16X32) dt = B2B_DTYPE_F16;
     else if (shape == B2B_SHAPE_BF16_16X16X32) dt = B2B_DTYPE_BF16;
@@ -818,11 +830,11 @@ b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, con
     if (m == b2bk::MODE_BPERM && !make_sched(dt, orn != 0, a.sched[0])) return B2B_ERROR_NOT_SUPPORTED;
     for (const b2b::ProbeDesc& d : b2b::probe_registry())
         if (d.dtype == dt && d.mode == m && d.orn == orn)
-            return d.launch(in, out, a, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+            return d.launch(in, out, a, stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
     return B2B_ERROR_NOT_SUPPORTED;
 }
 
-b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream) {
+b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, hipStream_t stream) {
     int dt, s32 = 0;
     if (shape == B2B_SHAPE_F16_16X16X32) dt = B2B_DTYPE_F16;
     else if (shape == B2B_SHAPE_BF16_16X16X32) dt = B2B_DTYPE_BF16;
@@ -831,19 +843,19 @@ b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, voi
     else if (shape == B2B_SHAPE_F64_16X16X4) dt = B2B_DTYPE_F64;
     else if (shape == B2B_SHAPE_FP8_32X32X64) {
         if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
-        hipLaunchKernelGGL(b2bk::mfma_f8_probe_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, c);
+        hipLaunchKernelGGL(b2bk::mfma_f8_probe_kernel<>, dim3(1), dim3(64), 0, stream, a, b, c);
         return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
     } else return B2B_ERROR_NOT_SUPPORTED;
     if (!a || !b || !c) return B2B_ERROR_INVALID_VALUE;
     for (const b2b::MfmaProbeDesc& d : b2b::mfma_probe_registry())
         if (d.dtype == dt && d.shape32 == s32)
-            return d.launch(a, b, c, (hipStream_t)stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+            return d.launch(a, b, c, stream) == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
     return B2B_ERROR_NOT_SUPPORTED;
 }
 
-b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, void* stream) {
+b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, hipStream_t stream) {
     if (!x || !y) return B2B_ERROR_INVALID_VALUE;
-    hipLaunchKernelGGL(b2bk::cvt_f8_probe_kernel<>, dim3(1), dim3(64), 0, (hipStream_t)stream, x, (int*)y);
+    hipLaunchKernelGGL(b2bk::cvt_f8_probe_kernel<>, dim3(1), dim3(64), 0, stream, x, (int*)y);
     return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
 }
 

@@ -37,6 +37,7 @@
 #ifndef B2B_H_
 #define B2B_H_
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 #include <stddef.h>
 #include <stdint.h>
 
@@ -123,7 +124,9 @@ typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
  *                 0 for a B* broadcasts it
  *   flags         B2B_FLAG_* | B2B_REMAP_*
  * Returns INVALID_VALUE for non-positive sizes, ld below the row width, ld
- * not a multiple of 16 bytes, unknown flags, or more than 2^31 - 1 row tiles
+ * not a multiple of 16 bytes, a leading dimension whose span over 32 rows of
+ * A or D, or over all rows of a weight matrix, reaches 2^31 bytes (the
+ * kernels' buffer offsets are 32-bit), unknown flags, or more than 2^31 - 1 row tiles
  * (batch x ceil(M / rows a workgroup takes)); NOT_SUPPORTED for cascades no
  * kernel covers: widths that break the granules or bounds of the run-time-width
  * kernels (see B2B_FLAG_MFMA_32X32) and have no fixed-width kernel, or weights
@@ -135,14 +138,18 @@ b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch,
                              const int64_t* ld, const int64_t* batch_stride, uint32_t flags);
 
 /*
- * Enqueues the cascade on `stream` (a hipStream_t; NULL is the null stream).
+ * Executes a planned cascade (page 1: the rearrangement module of the
+ * apparatus, Fig. 5, i.e. the execution step of the method's flow in Fig. 1:
+ * the operators run fused, the first one's result rearranged on chip into
+ * the second one's operand by the relation the plan fixed).
+ * Enqueues the cascade on `stream` (NULL is the null stream).
  * A, B0, B1, B2, D are device pointers, 16-byte aligned; B2 must be NULL iff
  * N3 == 0; D must not alias any input.  Only enqueues; does not synchronise.
  * Plans of one GEMM or of more than three (b2b_chain_create) take
  * b2b_chain_run; here they return INVALID_VALUE.
  */
 b2b_status_t b2b_gemm_run(b2b_gemm_t plan, const void* A, const void* B0, const void* B1,
-                          const void* B2, void* D, void* stream);
+                          const void* B2, void* D, hipStream_t stream);
 
 /*
  * A cascade of any number of GEMMs (page 1 allows as many fused operators as
@@ -198,10 +205,12 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
                                     int32_t nst, const int64_t* widths, const int64_t* ld,
                                     const int64_t* batch_stride, uint32_t flags);
 
-/* Enqueues a cascade planned by either create call; B holds its nst weight
- * pointers (device, 16-byte aligned, none equal to D).  Same asynchrony and
- * errors as b2b_gemm_run. */
-b2b_status_t b2b_chain_run(b2b_gemm_t plan, const void* A, const void* const* B, void* D, void* stream);
+/* Executes a cascade planned by either create call (page 1: the
+ * rearrangement module of Fig. 5, the execution step of Fig. 1, for any
+ * number of fused operators); B holds its nst weight pointers (device,
+ * 16-byte aligned, none equal to D).  Same asynchrony and errors as
+ * b2b_gemm_run. */
+b2b_status_t b2b_chain_run(b2b_gemm_t plan, const void* A, const void* const* B, void* D, hipStream_t stream);
 
 /* Releases a plan (and its workspace, after the device is idle). NULL is a no-op. */
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);
@@ -226,7 +235,7 @@ const char* b2b_status_string(b2b_status_t s);
  * meanwhile.  reps: 1..10000.
  */
 b2b_status_t b2b_gemm_tune(b2b_gemm_t plan, int32_t nsets, const void* const* A, const void* const* B,
-                           void* const* D, void* stream, int32_t reps);
+                           void* const* D, hipStream_t stream, int32_t reps);
 
 /* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
    remap mode, tile, grid, LDS and workspace bytes, kernel launches per run)
@@ -301,7 +310,7 @@ b2b_status_t b2b_remap_compile(int32_t elems, const int32_t* src, const int32_t*
  * once and every lane fills each of its slots once.
  */
 b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, const int32_t* q, const int32_t* r,
-                               const uint32_t* in, uint32_t* out, void* stream);
+                               const uint32_t* in, uint32_t* out, hipStream_t stream);
 
 /*
  * Runs one device rearrangement executor on index payloads and writes what
@@ -315,7 +324,7 @@ b2b_status_t b2b_remap_execute(int32_t elems, int32_t rounds, const int32_t* p, 
  * 16x16x4 f64); orient_n requires BPERMUTE or LDS.
  */
 b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, const void* in,
-                             void* out, void* stream);
+                             void* out, hipStream_t stream);
 
 /*
  * Runs one matrix instruction of `shape` on raw operand registers and writes
@@ -327,7 +336,7 @@ b2b_status_t b2b_remap_probe(b2b_shape_t shape, int orient_n, uint32_t mode, con
  * Accumulators start at zero.  Shapes: 16x16x32 and 32x32x16 f16/bf16, 16x16x4
  * f64, 32x32x64 fp8 (E4M3 operands, unit scales).
  */
-b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, void* stream);
+b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, void* c, hipStream_t stream);
 
 /*
  * The kernels' fp32 -> fp8 E4M3 conversion (v_cvt_pk_fp8_f32, used to round
@@ -335,7 +344,7 @@ b2b_status_t b2b_mfma_probe(b2b_shape_t shape, const void* a, const void* b, voi
  * its rounding against the format's definition.
  *   x  device, 256 float32;  y  device, 256 bytes (the codes in order)
  */
-b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, void* stream);
+b2b_status_t b2b_fp8_convert_probe(const float* x, void* y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,12 @@ def _create(**kw):
     (dict(flags=4 | (1 << 4)), 2),                     # 32x32 path: no coordination rounds
     (dict(flags=4 | 2 | (3 << 4)), 2),                 # 32x32 path: orientation T only
     (dict(batch=2, bs=[0, 4096, 4096, 0, 8192]), 1),   # A broadcast over batches
+    # 32-bit buffer offsets: 32 rows of A (or D), or a whole weight matrix,
+    # must span less than 2^31 bytes
+    (dict(ld=[1 << 25, 64, 64, 0, 64]), 1),            # 32 rows x 2^25 x 2 bytes = 2^31
+    (dict(ld=[64, 64, 64, 0, 1 << 25]), 1),
+    (dict(ld=[64, 1 << 24, 64, 0, 64]), 1),            # 64 rows of B0 x 2^24 x 2 bytes = 2^31
+    (dict(dtype=2, ld=[1 << 23, 64, 64, 0, 64]), 1),   # fp64: 32 x 2^23 x 8 bytes
 ])
 def test_create_rejects(kw, status):
     st, h = _create(**kw)
@@ -416,3 +422,13 @@ def test_missing_library_fails_loudly(tmp_path):
     import sys
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.stdout.split() == ["ImportError", "True", "ImportError", "True"], r.stdout + r.stderr[-500:]
+
+
+def test_leading_dimension_spans_below_2_31_accepted():
+    """Just inside the 32-bit offsets: 32 rows of A at 2^24 - 8 elements, a
+    64-row weight at 2^23 elements (2^30 bytes) and fp64 D at 2^22."""
+    for kw in (dict(ld=[(1 << 24) - 8, 64, 64, 0, 64]), dict(ld=[64, 1 << 23, 64, 0, 64]),
+               dict(dtype=2, ld=[64, 64, 64, 0, 1 << 22])):
+        st, h = _create(**kw)
+        assert st == 0, kw
+        cf.lib().b2b_gemm_destroy(h)

@@ -51,6 +51,11 @@ def test_tune(cfg, M, batch, kw, expect):
 
 @pytest.mark.parametrize("types,widths", [(("f16", "bf16", "f16"), (128, 128, 128)),
                                           (("f16", "fp8", "f16"), (128, 128, 128)),
+                                          # wider than the 128-bound fp8 instances: only the
+                                          # 256-bound ones may compete (a narrower one would
+                                          # walk only part of K and of D's columns)
+                                          (("f16", "fp8", "f16"), (256, 128, 128)),
+                                          (("bf16", "fp8", "bf16"), (128, 128, 256)),
                                           # compiled masks and the run-time-typed instance compete
                                           (("f16", "bf16", "f16", "bf16"), (128, 128, 128, 64)),
                                           (("tf32", "tf32", "tf32"), (128, 128, 64))])
