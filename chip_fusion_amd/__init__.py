@@ -28,6 +28,8 @@ EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_cre
            "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_compile",
            "b2b_remap_execute", "b2b_remap_probe",
            "b2b_mfma_probe", "b2b_fp8_convert_probe")
+# measurement instruments (b2b_bench.h)
+BENCH_EXPORTS = ("b2b_bench_mfma", "b2b_bench_copy")
 
 
 class B2BError(RuntimeError):
@@ -69,7 +71,9 @@ def lib():
         L.b2b_remap_execute.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
         L.b2b_mfma_probe.argtypes = [i32, vp, vp, vp, vp]
         L.b2b_fp8_convert_probe.argtypes = [vp, vp, vp]
-        for n in EXPORTS:
+        L.b2b_bench_mfma.argtypes = [i32, i32, i64, vp, ctypes.POINTER(ctypes.c_double), vp]
+        L.b2b_bench_copy.argtypes = [vp, vp, i64, i32, vp]
+        for n in EXPORTS + BENCH_EXPORTS:
             if n not in ("b2b_status_string",):
                 getattr(L, n).restype = i32
         _lib = L
@@ -325,6 +329,25 @@ def fp8_convert_probe(x, stream=None):
     y = torch.empty(256, dtype=torch.uint8, device=x.device)
     _check(lib().b2b_fp8_convert_probe(_ptr(x), _ptr(y), _stream_ptr(stream)), "b2b_fp8_convert_probe")
     return y
+
+
+def bench_mfma(dtype, workgroups, iters, sink, stream=None):
+    """Enqueues the matrix-core-only loop (b2b_bench_mfma) on a float64
+    device tensor `sink` of workgroups * 256 values; returns its FLOP."""
+    if sink.dtype != torch.float64 or sink.numel() < workgroups * 256 or sink.device.type != "cuda":
+        raise ValueError("sink: a float64 device tensor of workgroups * 256 values is expected")
+    flop = ctypes.c_double()
+    _check(lib().b2b_bench_mfma(DTYPES[dtype], workgroups, iters, _ptr(sink), ctypes.byref(flop),
+                                _stream_ptr(stream)), "b2b_bench_mfma")
+    return flop.value
+
+
+def bench_copy(src, dst, workgroups, stream=None):
+    """Enqueues the HBM stream dst = src over all of src's bytes (b2b_bench_copy)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n or src.device.type != "cuda" or dst.device.type != "cuda":
+        raise ValueError("src and dst: device tensors, dst at least as large as src")
+    _check(lib().b2b_bench_copy(_ptr(src), _ptr(dst), n, workgroups, _stream_ptr(stream)), "b2b_bench_copy")
 
 
 def to_device(x, dtype, device="cuda"):

@@ -12,6 +12,7 @@
 #include <atomic>
 #include <climits>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -167,6 +168,24 @@ const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int t
             best = &d;
     }
     return best;
+}
+
+// Device allocation of an unfused plan's workspace.  B2B_FAULT_INJECT=alloc
+// (or alloc:N) makes the first (or N-th) such allocation of a create call
+// fail as if the device were out of memory: a test hook for the error path,
+// which must leave no plan and no allocation behind.
+hipError_t ws_alloc(void** p, size_t bytes, int* count) {
+    ++*count;
+    if (const char* fi = std::getenv("B2B_FAULT_INJECT")) {
+        if (std::strncmp(fi, "alloc", 5) == 0) {
+            const int n = fi[5] == ':' ? std::atoi(fi + 6) : 1;
+            if (n == *count) {
+                *p = nullptr;
+                return hipErrorOutOfMemory;
+            }
+        }
+    }
+    return hipMalloc(p, bytes);
 }
 
 // Coordination rounds in the packed per-lane form the kernels read.
@@ -352,6 +371,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     p->flags = flags;
     p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
     std::memset(p->sched, 0, sizeof p->sched);
+    int allocs = 0;   // workspace allocations of this call
 
     if (!p->unfused && f8) {
         p->fused = find_f8(dt, f8_dtd, dims);
@@ -395,7 +415,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         p->stage_k[1] = find_f8a(f8_dtd, d1);
         if (!p->stage_k[0] || !p->stage_k[1]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
         p->work_bytes[0] = batch * M * dims[1];      // one byte an element
-        if (hipMalloc(&p->work[0], (size_t)p->work_bytes[0]) != hipSuccess) {
+        if (ws_alloc(&p->work[0], (size_t)p->work_bytes[0], &allocs) != hipSuccess) {
             (void)hipGetLastError();
             delete p;
             return B2B_ERROR_OUT_OF_MEMORY;
@@ -415,7 +435,7 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         }
         for (int s = 0; s + 1 < nst; ++s) {
             p->work_bytes[s] = batch * M * dims[s + 1] * es;
-            if (hipMalloc(&p->work[s], (size_t)p->work_bytes[s]) != hipSuccess) {
+            if (ws_alloc(&p->work[s], (size_t)p->work_bytes[s], &allocs) != hipSuccess) {
                 (void)hipGetLastError();
                 for (int t = 0; t < s; ++t) (void)hipFree(p->work[t]);
                 delete p;
@@ -436,6 +456,13 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
         return B2B_ERROR_INVALID_VALUE;
     }
     *plan = p;
+    // B2B_LOG=1: the chosen plan on stderr (the grid is settled at the first run)
+    if (const char* lg = std::getenv("B2B_LOG")) {
+        if (lg[0] && std::strcmp(lg, "0") != 0) {
+            char buf[512];
+            if (b2b_gemm_get_info(p, buf, sizeof buf) == B2B_SUCCESS) std::fprintf(stderr, "[b2b] plan: %s\n", buf);
+        }
+    }
     return B2B_SUCCESS;
 }
 

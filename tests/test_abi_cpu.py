@@ -14,8 +14,8 @@ from oracle import remap as R
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    txt = open(os.path.join(ROOT, "include", "b2b.h")).read()
+def _declared(header="b2b.h"):
+    txt = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"\b(b2b_[a-z0-9_]+)\s*\(", txt)))
 
 
@@ -26,6 +26,24 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(cf.EXPORTS)
+    bench = _declared("b2b_bench.h")
+    for n in bench:
+        assert hasattr(L, n), n
+    assert set(bench) == set(cf.BENCH_EXPORTS)
+
+
+def test_bench_instruments_reject_bad_arguments():
+    """The measurement calls validate before launching (no GPU needed)."""
+    L = cf.lib()
+    flop = ctypes.c_double()
+    p = ctypes.c_void_p(0x1000)
+    assert L.b2b_bench_mfma(0, 0, 10, p, ctypes.byref(flop), None) == 1          # no workgroups
+    assert L.b2b_bench_mfma(0, 4, 0, p, ctypes.byref(flop), None) == 1           # no rounds
+    assert L.b2b_bench_mfma(0, 4, 10, None, ctypes.byref(flop), None) == 1       # no sink
+    assert L.b2b_bench_mfma(3, 4, 10, p, ctypes.byref(flop), None) == 2          # tf32: no loop
+    assert L.b2b_bench_copy(p, ctypes.c_void_p(0x100000), 100, 4, None) == 1     # not whole 64 bytes
+    assert L.b2b_bench_copy(p, ctypes.c_void_p(0x1040), 128, 4, None) == 1       # overlapping
+    assert L.b2b_bench_copy(ctypes.c_void_p(0x1008), ctypes.c_void_p(0x100000), 128, 4, None) == 1
 
 
 def _create(**kw):
@@ -432,3 +450,20 @@ def test_leading_dimension_spans_below_2_31_accepted():
         st, h = _create(**kw)
         assert st == 0, kw
         cf.lib().b2b_gemm_destroy(h)
+
+
+def test_plan_log_on_request():
+    """B2B_LOG=1 prints the chosen plan on stderr at creation; unset, nothing."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import chip_fusion_amd as cf\n"
+            "cf.Plan('f16', 2, 100, 64, 64, 64).close()\n") % ROOT
+    env = dict(os.environ, B2B_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stderr[-500:]
+    line = [x for x in r.stderr.splitlines() if x.startswith("[b2b] plan:")]
+    assert len(line) == 1 and "path=fused" in line[0] and "dims=64x64x64" in line[0] and "M=100" in line[0]
+    env.pop("B2B_LOG")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
+    assert "[b2b]" not in r.stderr

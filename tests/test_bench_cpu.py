@@ -60,3 +60,37 @@ def test_bad_type_options_refused(args):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2, r.stderr[-500:]
     assert r.stdout.strip() == ""
+
+
+def test_roofline_binding_roof():
+    # workload 5 is HBM-bound (212 FLOP/B against a ridge of 315), workload 4 fp64-MFMA-bound
+    f5, b5 = bench.workload_numbers(synth.WORKLOADS[5])
+    r = bench.roofline(f5, b5, 0.05, bench.PEAK["f16"])
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - b5 / 0.05e-3 / 1e9) < 1e-6 and abs(r["frac"] - r["achieved"] / 8000) < 1e-12
+    f4, b4 = bench.workload_numbers(synth.WORKLOADS[4])
+    r = bench.roofline(f4, b4, 0.04, bench.PEAK["f64"])
+    assert r["bound"] == "mfma" and abs(r["achieved"] - f4 / 0.04e-3 / 1e12) < 1e-9
+
+
+def test_repeats_cover_50_ms():
+    assert bench.repeats_for(20.0, 5) == 5
+    assert bench.repeats_for(4.2, 5) == 12        # 12 x 4.2 ms >= 50 ms
+    assert bench.repeats_for(0.0, 5) > 5
+
+
+def test_summarize_trace_keeps_the_last_launches(tmp_path):
+    """Median, min and max over the last N launches of each kernel, in start order."""
+    p = tmp_path / "kernel_trace.csv"
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    # kernel a: 10 warm-up launches of 100 ns, then 5 of 10..50 ns; kernel b: 2 launches
+    t = 0
+    for d in [100] * 10 + [10, 20, 30, 40, 50]:
+        rows.append(f'"a<1, 2>",{t},{t + d}')
+        t += 1000
+    rows += ['"b",5,12', '"b",7,10']
+    p.write_text("\n".join(rows) + "\n")
+    out = {e["kernel"]: e for e in bench.summarize_trace(str(p), 5)}
+    assert out["a<1, 2>"]["launches"] == 15 and out["a<1, 2>"]["timed"] == 5
+    assert out["a<1, 2>"]["median_ns"] == 30 and out["a<1, 2>"]["min_ns"] == 10 and out["a<1, 2>"]["max_ns"] == 50
+    assert out["b"]["median_ns"] == 5
