@@ -32,7 +32,9 @@ def test_unfused_workspace_allocation_failure(monkeypatch):
     print("\n[case] unfused workspace allocation failure", flush=True)
     st, h = _create_unfused()                       # the same plan allocates without the hook
     assert st == 0 and h.value
-    assert "workspace_bytes=134217728" in cf.Plan.info(type("P", (), {"_h": h})())
+    buf = ctypes.create_string_buffer(512)
+    assert cf.lib().b2b_gemm_get_info(h, buf, 512) == 0
+    assert "workspace_bytes=134217728" in buf.value.decode()
     assert cf.lib().b2b_gemm_destroy(h) == 0
     free0 = _free()
     for spec in ["alloc", "alloc:1"] + ["alloc:2"] * 10:
