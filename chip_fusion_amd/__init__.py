@@ -22,8 +22,9 @@ FLAG_UNFUSED, FLAG_ORIENT_N, FLAG_MFMA_32X32, FLAG_TF32_EXACT = 1, 2, 4, 8
 SHAPES = {"f16_16x16x32": 0, "bf16_16x16x32": 1, "f16_32x32x16": 2, "bf16_32x32x16": 3,
           "f16_16x16x16": 4, "f64_16x16x4": 5, "fp8_32x32x64": 6}
 STATUS = {0: "success", 1: "invalid value", 2: "not supported", 3: "HIP runtime error",
-          4: "out of memory"}
-EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_create_typed", "b2b_chain_run", "b2b_gemm_tune",
+          4: "out of memory", 5: "intermediates exceed the static workspace"}
+STATIC_WORKSPACE_BYTES = 32 << 20
+EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_create_typed", "b2b_chain_run", "b2b_chain_run_static", "b2b_gemm_tune",
            "b2b_gemm_destroy", "b2b_status_string",
            "b2b_gemm_get_info", "b2b_remap_relation", "b2b_remap_schedule", "b2b_remap_compile",
            "b2b_remap_execute", "b2b_remap_probe",
@@ -55,6 +56,8 @@ def lib():
         L.b2b_chain_create.argtypes = [ctypes.POINTER(vp), i32, i64, i64, ctypes.c_int32, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
         L.b2b_chain_run.argtypes = [vp, vp, ctypes.POINTER(vp), vp, vp]
+        L.b2b_chain_run_static.argtypes = [i32, i64, i64, ctypes.c_int32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                           ctypes.POINTER(i64), vp, ctypes.POINTER(vp), vp, vp]
         L.b2b_chain_create_typed.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), i64, i64, ctypes.c_int32,
                                              ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64), u32]
         L.b2b_chain_create_typed.restype = i32
@@ -246,6 +249,31 @@ class Chain(Plan):
         st = lib().b2b_chain_run(self._h, _ptr(A), ptrs, _ptr(D), _stream_ptr(stream))
         _check(st, "b2b_chain_run")
         return D
+
+
+def chain_run_static(dtype, batch, M, widths, A, Bs, D, ld=None, batch_stride=None, stream=None):
+    """The unfused cascade with the library's static workspace
+    (b2b_chain_run_static): nothing is allocated by the call."""
+    code = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    widths = list(widths)
+    nst = len(widths) - 1
+    if len(Bs) != nst:
+        raise ValueError(f"{nst} weight matrices expected, got {len(Bs)}")
+    rows, width, L, S = _dense(widths, batch, M, ld, batch_stride)
+    ops = [("A", A)] + [(f"B{i}", b) for i, b in enumerate(Bs)] + [("D", D)]
+    for i, (name, t) in enumerate(ops):
+        _check_operand(t, name, _torch_dtype(code), batch, rows[i], width[i], L[i], S[i])
+    for name, t in ops:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: a device (cuda) tensor is expected, got one on {t.device}")
+    arr = ctypes.c_int64 * (nst + 2)
+    w = (ctypes.c_int64 * (nst + 1))(*widths)
+    ptrs = (ctypes.c_void_p * nst)(*[b.data_ptr() for b in Bs])
+    st = lib().b2b_chain_run_static(code, batch, M, nst, w, arr(*ld) if ld is not None else None,
+                                    arr(*batch_stride) if batch_stride is not None else None, _ptr(A), ptrs,
+                                    _ptr(D), _stream_ptr(stream))
+    _check(st, "b2b_chain_run_static")
+    return D
 
 
 def remap_relation(shape, orient_n=False):

@@ -285,6 +285,7 @@ const char* b2b_status_string(b2b_status_t s) {
         case B2B_ERROR_NOT_SUPPORTED: return "not supported";
         case B2B_ERROR_HIP: return "HIP runtime error";
         case B2B_ERROR_OUT_OF_MEMORY: return "out of memory";
+        case B2B_ERROR_WORKSPACE_LIMIT: return "intermediates exceed the static workspace";
     }
     return "unknown status";
 }
@@ -300,11 +301,11 @@ namespace {
 // the type of bit 0; the cascade then runs on the 32x32x16 kernels.
 // f8_dtd >= 0: two GEMMs, the second in fp8 E4M3 (B1 one byte per element),
 // D in type f8_dtd.
-b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
-                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1,
-                         int f8_dtd = -1) {
-    if (!plan) return B2B_ERROR_INVALID_VALUE;
-    *plan = nullptr;
+// plan_fill validates and plans into *p (a fresh plan the caller owns): it
+// picks the kernels and, for the unfused path, sizes the workspace
+// (p->work_bytes) without allocating anything, on the host or the device.
+b2b_status_t plan_fill(b2b_gemm_plan* p, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
+                       const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm, int f8_dtd) {
     if (dt != B2B_DTYPE_F16 && dt != B2B_DTYPE_BF16 && dt != B2B_DTYPE_F64 && dt != B2B_DTYPE_TF32)
         return B2B_ERROR_NOT_SUPPORTED;
     if (nst < 1 || nst > kMaxSt || !d) return B2B_ERROR_INVALID_VALUE;
@@ -353,8 +354,6 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     }
     if (batch > 1 && (S[0] == 0 || S[n - 1] < M * L[n - 1])) return B2B_ERROR_INVALID_VALUE;
 
-    b2b_gemm_plan* p = new (std::nothrow) b2b_gemm_plan();
-    if (!p) return B2B_ERROR_OUT_OF_MEMORY;
     p->dtype = dt;
     p->tm = tm;
     p->passes = passes;
@@ -371,16 +370,15 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     p->flags = flags;
     p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
     std::memset(p->sched, 0, sizeof p->sched);
-    int allocs = 0;   // workspace allocations of this call
 
     if (!p->unfused && f8) {
         p->fused = find_f8(dt, f8_dtd, dims);
         p->mode = b2bk::MODE_RELABEL;
-        if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        if (!p->fused) return B2B_ERROR_NOT_SUPPORTED;
     } else if (!p->unfused) {
         if (s32 || nst > 3) {
             // the fixed-width kernels cover up to three GEMMs
-            if (orn) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+            if (orn) return B2B_ERROR_NOT_SUPPORTED;
             p->fused = find_gen(dt, nst, dims, mode32, tm, passes);
             // a mixture without a compiled mask: the types read at run time
             if (!p->fused && typed) p->fused = find_gen_rt(nst, dims);
@@ -401,27 +399,20 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
             p->fused = find_gen(dt, nst, dims, mode32);
             p->mode = mode32;
         }
-        if (!p->fused) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        if (!p->fused) return B2B_ERROR_NOT_SUPPORTED;
         if (p->mode == b2bk::MODE_BPERM) {
-            if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1])) {
-                delete p;
+            if (!make_sched(dt, orn != 0, p->sched[0]) || !make_sched(dt, false, p->sched[1]))
                 return B2B_ERROR_NOT_SUPPORTED;
-            }
         }
     } else if (f8) {
         // unfused: the first GEMM writes its result as fp8, the second reads it
         const int64_t d0[4] = {dims[0], dims[1], 0, 0}, d1[4] = {dims[1], dims[2], 0, 0};
         p->stage_k[0] = dims[1] % 64 ? nullptr : find_gen(dt, 1, d0, 0, -1, 0, 1);
         p->stage_k[1] = find_f8a(f8_dtd, d1);
-        if (!p->stage_k[0] || !p->stage_k[1]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+        if (!p->stage_k[0] || !p->stage_k[1]) return B2B_ERROR_NOT_SUPPORTED;
         p->work_bytes[0] = batch * M * dims[1];      // one byte an element
-        if (ws_alloc(&p->work[0], (size_t)p->work_bytes[0], &allocs) != hipSuccess) {
-            (void)hipGetLastError();
-            delete p;
-            return B2B_ERROR_OUT_OF_MEMORY;
-        }
     } else {
-        if (orn) { delete p; return B2B_ERROR_INVALID_VALUE; }
+        if (orn) return B2B_ERROR_INVALID_VALUE;
         for (int s = 0; s < nst; ++s) {
             const int64_t d2[4] = {dims[s], dims[s + 1], 0, 0};
             const int km0 = (s == 0 && dt == B2B_DTYPE_F64) ? b2bk::KM_PAIR64 : b2bk::KM_NAT;
@@ -431,17 +422,9 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
             const int stm = (sub == 1 || sub == 2) ? sub : -1;
             p->stage_k[s] = (s32 || stm >= 0) ? nullptr : find_kernel(sdt, 1, d2, 0, 0, km0);
             if (!p->stage_k[s]) p->stage_k[s] = find_gen(sdt, 1, d2, 0, stm, passes);
-            if (!p->stage_k[s]) { delete p; return B2B_ERROR_NOT_SUPPORTED; }
+            if (!p->stage_k[s]) return B2B_ERROR_NOT_SUPPORTED;
         }
-        for (int s = 0; s + 1 < nst; ++s) {
-            p->work_bytes[s] = batch * M * dims[s + 1] * es;
-            if (ws_alloc(&p->work[s], (size_t)p->work_bytes[s], &allocs) != hipSuccess) {
-                (void)hipGetLastError();
-                for (int t = 0; t < s; ++t) (void)hipFree(p->work[t]);
-                delete p;
-                return B2B_ERROR_OUT_OF_MEMORY;
-            }
-        }
+        for (int s = 0; s + 1 < nst; ++s) p->work_bytes[s] = batch * M * dims[s + 1] * es;
     }
     // the kernels count tiles (rows_wg rows of one batch) in 32 bits
     auto tiles_fit = [&](const KernelDesc* k) {
@@ -449,11 +432,33 @@ b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int
     };
     bool fit = tiles_fit(p->fused);
     for (const KernelDesc* k : p->stage_k) fit = fit && tiles_fit(k);
-    if (!fit) {
-        for (void* w : p->work)
-            if (w) (void)hipFree(w);
+    return fit ? B2B_SUCCESS : B2B_ERROR_INVALID_VALUE;
+}
+
+// A new plan (plan_fill) with its unfused workspace allocated.
+b2b_status_t create_impl(b2b_gemm_t* plan, int dt, int64_t batch, int64_t M, int nst, const int64_t* d,
+                         const int64_t* Lin, const int64_t* Sin, uint32_t flags, bool chain, int tm = -1,
+                         int f8_dtd = -1) {
+    if (!plan) return B2B_ERROR_INVALID_VALUE;
+    *plan = nullptr;
+    b2b_gemm_plan* p = new (std::nothrow) b2b_gemm_plan();
+    if (!p) return B2B_ERROR_OUT_OF_MEMORY;
+    const b2b_status_t st = plan_fill(p, dt, batch, M, nst, d, Lin, Sin, flags, chain, tm, f8_dtd);
+    if (st != B2B_SUCCESS) {
         delete p;
-        return B2B_ERROR_INVALID_VALUE;
+        return st;
+    }
+    int allocs = 0;   // workspace allocations of this call
+    for (int s = 0; s + 1 < kMaxSt; ++s) {
+        if (!p->work_bytes[s]) continue;
+        if (ws_alloc(&p->work[s], (size_t)p->work_bytes[s], &allocs) != hipSuccess) {
+            (void)hipGetLastError();
+            p->work[s] = nullptr;
+            for (void* w : p->work)
+                if (w) (void)hipFree(w);
+            delete p;
+            return B2B_ERROR_OUT_OF_MEMORY;
+        }
     }
     *plan = p;
     // B2B_LOG=1: the chosen plan on stderr (the grid is settled at the first run)
@@ -580,6 +585,72 @@ b2b_status_t b2b_gemm_run(b2b_gemm_t p, const void* A, const void* B0, const voi
 b2b_status_t b2b_chain_run(b2b_gemm_t p, const void* A, const void* const* B, void* D, hipStream_t stream) {
     if (!p || !B) return B2B_ERROR_INVALID_VALUE;
     return run_impl(p, A, B, D, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The unfused path without allocation (b2b_chain_run_static): the
+// intermediates go to `scratch`, a file-scope device array of
+// B2B_STATIC_WORKSPACE_BYTES that each GPU holds from the first call on it
+// until the process ends.  Host code never uses the array's name as an
+// address: its device address is asked for once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[B2B_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch`
+b2b_status_t scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return B2B_ERROR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return B2B_ERROR_NOT_SUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return B2B_ERROR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return B2B_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+b2b_status_t b2b_chain_run_static(b2b_dtype_t dtype, int64_t batch, int64_t M, int32_t nst, const int64_t* widths,
+                                  const int64_t* ld, const int64_t* batch_stride, const void* A,
+                                  const void* const* B, void* D, hipStream_t stream) {
+    if (!widths || !B) return B2B_ERROR_INVALID_VALUE;
+    // the plan lives on the stack: neither device nor host memory is allocated
+    b2b_gemm_plan plan;
+    b2b_status_t st = plan_fill(&plan, (int)dtype, batch, M, nst, widths, ld, batch_stride, B2B_FLAG_UNFUSED, true,
+                                -1, -1);
+    if (st != B2B_SUCCESS) return st;
+    // intermediate s in half s % 2 (stage s reads half (s - 1) % 2 and writes
+    // half s % 2; the stream orders the stages); one intermediate takes the
+    // whole array
+    int64_t half = 0;
+    for (int64_t w : plan.work_bytes) half = std::max(half, (w + 255) / 256 * 256);
+    const int64_t need = nst > 2 ? 2 * half : half;
+    if (need > (int64_t)B2B_STATIC_WORKSPACE_BYTES) return B2B_ERROR_WORKSPACE_LIMIT;
+    void* base = nullptr;
+    if (half) {
+        st = scratch_address(&base);
+        if (st != B2B_SUCCESS) return st;
+    }
+    for (int s = 0; s + 1 < nst; ++s) plan.work[s] = (char*)base + (s % 2) * half;
+    st = run_impl(&plan, A, B, D, stream);
+    for (void*& w : plan.work) w = nullptr;   // the array is not the plan's
+    return st;
 }
 
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t p) {

@@ -78,7 +78,9 @@ typedef enum {
     B2B_ERROR_INVALID_VALUE = 1,  /* bad dimension, leading dimension, pointer or alignment */
     B2B_ERROR_NOT_SUPPORTED = 2,  /* the cascade cannot be fused with this dtype/shape/mode */
     B2B_ERROR_HIP = 3,            /* a HIP runtime call failed */
-    B2B_ERROR_OUT_OF_MEMORY = 4   /* host or device allocation failed */
+    B2B_ERROR_OUT_OF_MEMORY = 4,  /* host or device allocation failed */
+    B2B_ERROR_WORKSPACE_LIMIT = 5 /* b2b_chain_run_static: the intermediates need more than
+                                     B2B_STATIC_WORKSPACE_BYTES */
 } b2b_status_t;
 
 /* Flags of b2b_gemm_create. */
@@ -211,6 +213,32 @@ b2b_status_t b2b_chain_create_typed(b2b_gemm_t* plan, const b2b_dtype_t* dtypes,
  * 16-byte aligned, none equal to D).  Same asynchrony and errors as
  * b2b_gemm_run. */
 b2b_status_t b2b_chain_run(b2b_gemm_t plan, const void* A, const void* const* B, void* D, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * unfused path of b2b_chain_create(..., B2B_FLAG_UNFUSED) followed by
+ * b2b_chain_run, in one call that allocates nothing -- no device memory, no
+ * host heap.  The same single-GEMM kernels run in the same order, so D equals
+ * that plan's D bit for bit.  The intermediates go to a workspace the library
+ * holds in a device array of B2B_STATIC_WORKSPACE_BYTES (one per GPU it runs
+ * on, in device memory from the first call on that GPU until the process
+ * ends): intermediate s in half s % 2 of it, or all of it when there is one.
+ *   dtype, batch, M, nst, widths, ld, batch_stride   as for b2b_chain_create
+ *   A, B, D, stream                                  as for b2b_chain_run
+ * Every call on a GPU shares that GPU's array and leaves its last
+ * intermediates in it: calls that overlap on one GPU (on different streams,
+ * or from several threads) race and must be serialised by the caller.
+ * Errors: as b2b_chain_create and b2b_chain_run (the plan is made and dropped
+ * inside the call); WORKSPACE_LIMIT when the intermediates need more than the
+ * array (the largest times two with three GEMMs or more, each rounded up to
+ * 256 bytes, or the only one with two GEMMs); HIP if the array's address
+ * cannot be obtained.  Nothing is written to D on an error.
+ */
+#define B2B_STATIC_WORKSPACE_BYTES (32u << 20)
+b2b_status_t b2b_chain_run_static(b2b_dtype_t dtype, int64_t batch, int64_t M, int32_t nst, const int64_t* widths,
+                                  const int64_t* ld, const int64_t* batch_stride, const void* A,
+                                  const void* const* B, void* D, hipStream_t stream);
 
 /* Releases a plan (and its workspace, after the device is idle). NULL is a no-op. */
 b2b_status_t b2b_gemm_destroy(b2b_gemm_t plan);

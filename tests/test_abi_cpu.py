@@ -144,7 +144,7 @@ def test_run_rejects_bad_pointers():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert cf.lib().b2b_status_string(s).decode() == cf.STATUS[s]
 
 
@@ -467,3 +467,27 @@ def test_plan_log_on_request():
     env.pop("B2B_LOG")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
     assert "[b2b]" not in r.stderr
+
+
+def test_static_run_checks_before_touching_the_device():
+    """b2b_chain_run_static plans and sizes its intermediates first: bad
+    arguments and intermediates beyond the static workspace are refused
+    before the device is touched."""
+    L = cf.lib()
+    p = ctypes.c_void_p(0x1000)
+    ptrs = (ctypes.c_void_p * 3)(0x1000, 0x1000, 0x1000)
+
+    def run(dtype, batch, M, widths):
+        w = (ctypes.c_int64 * len(widths))(*widths)
+        return L.b2b_chain_run_static(dtype, batch, M, len(widths) - 1, w, None, None, p, ptrs,
+                                      ctypes.c_void_p(0x2000000), None)
+    assert L.b2b_chain_run_static(0, 1, 64, 2, None, None, None, p, ptrs, ctypes.c_void_p(0x2000), None) == 1
+    assert run(0, 0, 64, [64, 64, 64]) == 1                      # no batches
+    # two GEMMs: one intermediate, the whole 32 MiB array
+    assert run(0, 1, 131072, [64, 128, 64]) != 5                 # exactly 32 MiB fits
+    assert run(0, 1, 131073, [64, 128, 64]) == 5                 # a row more does not
+    # three GEMMs: two halves of the largest intermediate (16 MiB each)
+    assert run(0, 1, 65536, [64, 128, 64, 64]) != 5
+    assert run(0, 1, 65537, [64, 128, 64, 64]) == 5
+    assert run(2, 8, 16384, [64, 64, 64]) == 5                   # fp64 workload 4: 64 MiB
+    assert cf.STATIC_WORKSPACE_BYTES == 32 << 20
