@@ -178,10 +178,12 @@ def measure_ceilings(cf, torch, stream, repeats):
         ms = time_blocks(lambda i: cf.bench_mfma(dt, wg, it, sink, stream=stream), 1, repeats + 1, stream, torch)[1:]
         mfma[dt] = flop / (float(np.median(ms)) * 1e-3) / 1e12
     out["mfma_tflops"] = mfma
-    nbytes = 64 << 20
+    # 128 MiB read + 128 MiB written per launch over four pairs, four
+    # workgroups a compute unit: the best of the sizes and grids measured
+    nbytes = 128 << 20
     pairs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
-              torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(8)]
-    cwg = 8 * cus
+              torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(4)]
+    cwg = 4 * cus
 
     def copy(i):
         s, d = pairs[i % len(pairs)]
