@@ -49,6 +49,7 @@ struct b2b_gemm_plan {
     int tm = -1;                                 // type per stage (bit s: bf16), or -1: dtype throughout
     int passes = 0;                              // tf32: bf16 passes per product (3 or 4)
     int f8 = 0, dtd = 0;                         // second GEMM in fp8 E4M3, D's type
+    int tail = 0;                                // fused on a kernel that takes any widths and leading dimensions
     int64_t batch = 0, M = 0, dims[kMaxSt + 1] = {};
     // leading dimensions and batch strides (elements): [0] A, [1 + s] B_s, [nst + 1] D
     int64_t ld[kMaxSt + 2] = {}, bs[kMaxSt + 2] = {};
@@ -88,16 +89,36 @@ const KernelDesc* find_kernel(int dt, int nst, const int64_t* dims, int mode, in
 // Run-time-width kernel for widths dims[0..nst] (32x32x16 for fp16/bf16,
 // 16x16x4 for fp64): the smallest width bound that holds them all, or null
 // when a granule, a bound or LDS rules the cascade out.
+// tail: an instance that takes any widths (each padded on chip to the
+// granule: 32 for fp16/bf16, 8 for fp64's K and 16 for its N) and any
+// leading dimensions; the bound and LDS then hold for the padded widths.
 bool gen_fits(const KernelDesc& d, int dt, int nst, const int64_t* dims, int tm = -1, int passes = 0,
-              int out8 = 0) {
-    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm || d.passes != passes || d.out8 != out8) return false;
+              int out8 = 0, int tail = 0) {
+    if (!d.rtw || d.dtype != dt || d.nst != nst || d.tm != tm || d.passes != passes || d.out8 != out8 ||
+        d.tail != tail)
+        return false;
     const bool f64 = dt == B2B_DTYPE_F64;
-    if (dims[0] % (f64 ? 8 : 32) || dims[0] > d.maxd) return false;
+    const int64_t gk = f64 ? 8 : 32, gn = f64 ? 16 : 32;
+    int64_t w[kMaxSt + 1];
+    for (int i = 0; i <= nst; ++i) {
+        const int64_t g = i == 0 ? gk : gn;
+        if (!tail && dims[i] % g) return false;
+        w[i] = (dims[i] + g - 1) / g * g;
+        if (w[i] > d.maxd) return false;
+    }
     int64_t lds = 0;
-    for (int i = 1; i <= nst; ++i)
-        if (dims[i] % (f64 ? 16 : 32) || dims[i] > d.maxd) return false;
-    for (int i = 0; i < nst; ++i) lds += dims[i] * dims[i + 1] * elt_size(dt);
+    for (int i = 0; i < nst; ++i) lds += w[i] * w[i + 1] * elt_size(dt);
     return lds <= 160 * 1024;
+}
+
+// whether widths d[0..nst] are whole granules of the kernels without tails
+// (fp16/bf16: multiples of 32; fp64: K of 8, N of 16)
+bool whole_granules(int dt, int nst, const int64_t* d) {
+    const bool f64 = dt == B2B_DTYPE_F64;
+    if (d[0] % (f64 ? 8 : 32)) return false;
+    for (int i = 1; i <= nst; ++i)
+        if (d[i] % (f64 ? 16 : 32)) return false;
+    return true;
 }
 
 // Two GEMMs, the second in fp8: first GEMM's type dt, D's type dtd; K a
@@ -159,10 +180,10 @@ const KernelDesc* find_gen_rt(int nst, const int64_t* dims) {
 // same bound, the four-wave one where two of its workgroups fit a CU's LDS
 // (twice the tiles in flight per CU, measured 3 % faster), else the eight-wave one.
 const KernelDesc* find_gen(int dt, int nst, const int64_t* dims, int mode, int tm = -1, int passes = 0,
-                           int out8 = 0) {
+                           int out8 = 0, int tail = 0) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
-        if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes, out8) || (nst > 1 && d.mode != mode)) continue;
+        if (d.f8 || !gen_fits(d, dt, nst, dims, tm, passes, out8, tail) || (nst > 1 && d.mode != mode)) continue;
         if (!best || d.maxd < best->maxd ||
             (d.maxd == best->maxd && wave_rank(d, dims, nst) < wave_rank(*best, dims, nst)))
             best = &d;
@@ -337,6 +358,7 @@ b2b_status_t plan_fill(b2b_gemm_plan* p, int dt, int64_t batch, int64_t M, int n
     const int n = nst + 2;
     int64_t L[kMaxSt + 2], S[kMaxSt + 2];
     const int es = elt_size(dt);
+    bool ld16 = true;
     for (int i = 0; i < n; ++i) {
         // operand i: A (rows M, width K), B_s (rows d[s], width d[s+1]), D (rows M, width d[nst])
         const int64_t rows = (i == 0 || i == n - 1) ? M : dims[i - 1];
@@ -344,15 +366,22 @@ b2b_status_t plan_fill(b2b_gemm_plan* p, int dt, int64_t batch, int64_t M, int n
         const int eo = (f8 && i == 2) ? 1 : es;    // the fp8 weights: one byte an element
         L[i] = Lin ? Lin[i] : width;
         if (L[i] < width) return B2B_ERROR_INVALID_VALUE;
-        if ((L[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
         S[i] = Sin ? Sin[i] : rows * L[i];
-        if (S[i] < 0 || (S[i] * eo) % 16) return B2B_ERROR_INVALID_VALUE;
+        if (S[i] < 0) return B2B_ERROR_INVALID_VALUE;
+        // rows and batches starting on 16-byte boundaries (else only the tail kernels)
+        if ((L[i] * eo) % 16 || (S[i] * eo) % 16) ld16 = false;
         // the kernels address a wave's rows of A or D (at most 32) and a whole
         // weight matrix through one buffer resource, with 32-bit signed offsets
         const int64_t span_rows = (i == 0 || i == n - 1) ? std::min<int64_t>(M, 32) : rows;
         if (span_rows * L[i] * eo > (int64_t)INT32_MAX) return B2B_ERROR_INVALID_VALUE;
     }
     if (batch > 1 && (S[0] == 0 || S[n - 1] < M * L[n - 1])) return B2B_ERROR_INVALID_VALUE;
+    // Widths off the granule, or rows / batches not on 16-byte boundaries:
+    // the tail kernels (one type, fp16 / bf16 / fp64, relabelled).
+    const bool tail = !(ld16 && whole_granules(dt, nst, dims));
+    const bool tail_ok = (dt == B2B_DTYPE_F16 || dt == B2B_DTYPE_BF16 || dt == B2B_DTYPE_F64) && !typed && !f8 &&
+                         !orn && mode == b2bk::MODE_RELABEL;
+    if (tail && !tail_ok) return ld16 ? B2B_ERROR_NOT_SUPPORTED : B2B_ERROR_INVALID_VALUE;
 
     p->dtype = dt;
     p->tm = tm;
@@ -371,7 +400,12 @@ b2b_status_t plan_fill(b2b_gemm_plan* p, int dt, int64_t batch, int64_t M, int n
     p->unfused = (flags & B2B_FLAG_UNFUSED) != 0;
     std::memset(p->sched, 0, sizeof p->sched);
 
-    if (!p->unfused && f8) {
+    if (!p->unfused && tail) {
+        p->fused = find_gen(dt, nst, dims, b2bk::MODE_RELABEL, -1, 0, 0, 1);
+        p->mode = b2bk::MODE_RELABEL;
+        p->tail = 1;
+        if (!p->fused) return B2B_ERROR_NOT_SUPPORTED;
+    } else if (!p->unfused && f8) {
         p->fused = find_f8(dt, f8_dtd, dims);
         p->mode = b2bk::MODE_RELABEL;
         if (!p->fused) return B2B_ERROR_NOT_SUPPORTED;
@@ -420,6 +454,19 @@ b2b_status_t plan_fill(b2b_gemm_plan* p, int dt, int64_t batch, int64_t M, int n
             const int sub = typed ? (tm >> s) & 3 : 0;
             const int sdt = typed ? ((sub & 1) ? B2B_DTYPE_BF16 : B2B_DTYPE_F16) : dt;
             const int stm = (sub == 1 || sub == 2) ? sub : -1;
+            // this GEMM's operands: A or the previous intermediate (dense), B_s,
+            // and D or its own intermediate (dense)
+            const bool last = s + 1 == nst;
+            const int64_t lx = s == 0 ? L[0] : dims[s], sx = s == 0 ? S[0] : M * dims[s];
+            const int64_t ly = last ? L[n - 1] : dims[s + 1], sy = last ? S[n - 1] : M * dims[s + 1];
+            const bool al16 = (lx * es) % 16 == 0 && (sx * es) % 16 == 0 && (L[1 + s] * es) % 16 == 0 &&
+                              (S[1 + s] * es) % 16 == 0 && (ly * es) % 16 == 0 && (sy * es) % 16 == 0;
+            if (!al16 || !whole_granules(sdt, 1, d2)) {
+                if (!tail_ok) return B2B_ERROR_NOT_SUPPORTED;
+                p->stage_k[s] = find_gen(sdt, 1, d2, 0, -1, 0, 0, 1);
+                if (!p->stage_k[s]) return B2B_ERROR_NOT_SUPPORTED;
+                continue;
+            }
             p->stage_k[s] = (s32 || stm >= 0) ? nullptr : find_kernel(sdt, 1, d2, 0, 0, km0);
             if (!p->stage_k[s]) p->stage_k[s] = find_gen(sdt, 1, d2, 0, stm, passes);
             if (!p->stage_k[s]) return B2B_ERROR_NOT_SUPPORTED;
@@ -684,9 +731,9 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t p, int32_t nsets, const void* const* A, co
             continue;
         }
         if (d.rtw) {
-            if (p->orn || !gen_fits(d, d.dtype, p->nst, p->dims, d.tm, p->passes)) continue;
+            if (p->orn || !gen_fits(d, d.dtype, p->nst, p->dims, d.tm, p->passes, 0, p->tail)) continue;
         } else {
-            if (s32 || d.orn != p->orn) continue;
+            if (s32 || d.orn != p->orn || p->tail) continue;
             bool ok = true;
             for (int i = 0; i <= p->nst; ++i) ok = ok && d.dims[i] == p->dims[i];
             if (!ok) continue;
@@ -811,12 +858,12 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     for (int i = 1; i <= p->nst; ++i) dims += "x" + std::to_string(p->dims[i]);
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
-                  "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d",
+                  "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d tail=%d",
                   p->unfused ? "unfused" : "fused", dts_s.c_str(), (long long)p->batch,
                   (long long)p->M, dims.c_str(), mfma,
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, lds_bytes, p->grid[0],
-                  (long long)work, p->unfused ? p->nst : 1);
+                  (long long)work, p->unfused ? p->nst : 1, k->tail);
     return B2B_SUCCESS;
 }
 

@@ -32,6 +32,7 @@ template <int DT0_, int DTD_, int MAXD_, int PF_, int WAVES_ = 8>
 struct F8Cfg {
     static constexpr int DT = DT0_, DTD = DTD_, NST = 2, MAXD = MAXD_, MODE = MODE_RELABEL, PF = PF_;
     static constexpr bool RTM = false;   // types fixed at compile time
+    static constexpr bool TAIL = false;  // widths whole granules
     static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32, MKS8 = MAXD / 64;
     static constexpr int LDS_MAX = 160 * 1024;
@@ -193,6 +194,7 @@ template <int DTD_, int MAXD_>
 struct F8ACfg {
     static constexpr int DT = DT_F16, DTD = DTD_, NST = 1, MAXD = MAXD_, MODE = MODE_RELABEL, PF = 1;
     static constexpr bool RTM = false;   // types fixed at compile time
+    static constexpr bool TAIL = false;  // widths whole granules
     static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32, MKS8 = MAXD / 64;
     static constexpr int LDS_MAX = 160 * 1024;

@@ -66,10 +66,17 @@ template <> struct Ty32<DT_BF16> {
 // cascade whose second GEMM is fp8), else in the last stage's 16-bit type.
 constexpr int TM_RUNTIME = -2;
 
-template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8, bool OUT8_ = false>
+// TAIL_: any widths (the K and N tails of widths that are not multiples of
+// 32) and any leading dimensions and batch strides (rows at any element
+// alignment): every width is padded to the next multiple of 32 on chip --
+// weights zero-filled in LDS, A's columns past K read as zero, D's columns
+// past N never written -- so the instructions see a cascade of whole
+// granules whose padded rows and columns are exactly zero.
+template <int DT_, int NST_, int MAXD_, int MODE_, int PF_, int TM_ = -1, int WAVES_ = 8, bool OUT8_ = false,
+          bool TAIL_ = false>
 struct GenCfg {
     static constexpr int DT = DT_, NST = NST_, MAXD = MAXD_, MODE = MODE_, PF = PF_, TM = TM_;
-    static constexpr bool OUT8 = OUT8_;
+    static constexpr bool OUT8 = OUT8_, TAIL = TAIL_;
     static constexpr int DE = OUT8 ? 1 : 2;   // bytes of a D element
     static constexpr bool RTM = TM_ == TM_RUNTIME;
     static constexpr int stype(int s) { return TM < 0 ? DT : (((TM >> s) & 1) ? DT_BF16 : DT_F16); }
@@ -81,7 +88,14 @@ struct GenCfg {
     static_assert(MODE == MODE_RELABEL || MODE == MODE_PERMLANE, "rearrangement");
     static_assert(TM == -1 || TM == TM_RUNTIME || (TM >= 0 && TM < (2 << NST) && stype(0) == DT), "type mask");
     static_assert(!RTM || MODE == MODE_RELABEL, "run-time types are relabelled");
+    static_assert(!TAIL || (TM == -1 && !OUT8 && MODE == MODE_RELABEL), "tails: one type, relabelled");
 };
+
+// the widths a kernel lays out: each padded to a multiple of 32 where the
+// kernel takes tails, else as given
+__host__ __device__ inline void gen_pad(const int32_t* d, int nst, bool tail, int32_t* out) {
+    for (int i = 0; i <= nst; ++i) out[i] = tail ? (d[i] + 31) / 32 * 32 : d[i];
+}
 
 // One weight matrix in LDS: `rows` x `n` 16-bit values in blocks of 32
 // columns, each block `rows` x 64 bytes (row r of block t at t*rows*64 + r*64).
@@ -143,6 +157,65 @@ __device__ __forceinline__ u4_t gen_wfrag(const unsigned char* lds, const GenFra
     return out;
 }
 
+// A 16-byte chunk of 8 16-bit elements of which `valid` lie inside the
+// matrix row (a K or N tail): a whole chunk is one 16-byte load, at any
+// element alignment of the row; a partial one is loaded element by element,
+// the rest reading as zero, so no access reaches past the row's last element.
+__device__ __forceinline__ u4_t ld_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t off, int valid) {
+    if (valid >= 8) return ld128(rs, off);
+    u4_t v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 7; ++e)
+        if (e < valid) {
+            const unsigned h = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)(off + 2 * e), 0, 0);
+            v[e >> 1] |= h << (16 * (e & 1));
+        }
+    return v;
+}
+// the store counterpart: only the chunk's first `valid` elements are written
+__device__ __forceinline__ void st_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
+    if (valid >= 8) {
+        st128(rs, off, v);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 7; ++e)
+        if (e < valid)
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), rs,
+                                                  (int)(off + 2 * e), 0, kStreamPolicy);
+}
+
+// weights of batch b -> LDS, each matrix padded with zeros to the whole
+// 32-row, 32-column blocks the kernel lays out (dt: the true widths)
+template <class C>
+__device__ inline void gen_stage_weights_tail(unsigned char* lds, const GenMat (&mat)[C::NST], const int* dt,
+                                              const KArgs& args, int b) {
+#pragma unroll
+    for (int s = 0; s < C::NST; ++s) {
+        const GenMat& m = mat[s];
+        const int rows_t = dt[s], cols_t = dt[s + 1];
+        const auto rs = make_rsrc((const char*)args.B[s] + (int64_t)b * args.sB[s] * 2,
+                                  (uint32_t)(rows_t * args.ldb[s] * 2));
+        const int cpr = m.n / 8, total = m.rows * cpr;
+        for (int i0 = 0; i0 < total; i0 += 8 * C::THREADS) {
+            u4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 8;
+                const int valid = (i < total && r < rows_t) ? cols_t - c : 0;
+                v[k] = ld_chunk16(rs, (uint32_t)((r * args.ldb[s] + c) * 2), valid);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 8;
+                if (i < total) *(u4_t*)(lds + m.pos(r, c)) = v[k];
+            }
+        }
+    }
+}
+
 // weights of batch b -> LDS (16-byte loads, eight in flight per thread).
 // Every thread issues the same loads (past the end: an offset beyond the
 // resource, which reads zero), so the compiler's counts of loads in flight
@@ -192,6 +265,21 @@ __device__ __forceinline__ void gen_load_a(u4_t (&a)[C::MKS], __amdgpu_buffer_rs
         const auto src = 2 * p < ks ? rs : none;
         a[2 * p] = ld128(src, (uint32_t)((r * lda + 32 * p + 8 * g) * 2));
         a[2 * p + 1] = ld128(src, (uint32_t)(((16 + r) * lda + 32 * p + 8 * g) * 2));
+    }
+}
+
+// gen_load_a with a K tail (K: the true width): chunks straddling K are
+// loaded element by element, columns past K read as zero
+template <class C>
+__device__ __forceinline__ void gen_load_a_tail(u4_t (&a)[C::MKS], __amdgpu_buffer_rsrc_t rs, int64_t lda, int ks,
+                                                int K, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < C::MKS / 2; ++p) {
+        const int c0 = 32 * p + 8 * g;
+        const int valid = 2 * p < ks ? K - c0 : 0;
+        a[2 * p] = ld_chunk16(rs, (uint32_t)((r * lda + c0) * 2), valid);
+        a[2 * p + 1] = ld_chunk16(rs, (uint32_t)(((16 + r) * lda + c0) * 2), valid);
     }
 }
 
@@ -259,10 +347,12 @@ __device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t&
 // chunks XOR-swizzled by row), read back so that each store writes 8 rows x
 // 128 contiguous bytes.  Without a staging region (stg < 0) the 16-byte
 // pieces go straight to memory.
+// ncols: D's true width, where the kernel takes tails (columns past it are
+// not written; chunks straddling it are stored element by element).
 template <class C>
 __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, const f16x_t& acc0, const f16x_t& acc1,
                                                bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane,
-                                               bool bf = false) {
+                                               bool bf = false, int ncols = 0) {
     const int m = lane & 31, h = lane >> 5;
     u4_t c[4];
     gen_regroup_d<C>(acc0, c[0], c[1], bf);
@@ -271,7 +361,11 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
         // chunk q of this lane sits at column n0 + 16 q + 8 h
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (q < 2 || two) st128(rs, (uint32_t)((m * ldd + n0 + 16 * q + 8 * h) * 2), c[q]);
+            if (q < 2 || two) {
+                const int col = n0 + 16 * q + 8 * h;
+                if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((m * ldd + col) * 2), c[q], ncols - col);
+                else st128(rs, (uint32_t)((m * ldd + col) * 2), c[q]);
+            }
         return;
     }
     unsigned char* st = lds + stg;
@@ -288,7 +382,11 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
     for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + (lane >> 3);
         const u4_t v = *(const u4_t*)(st + r * 128 + ((ch ^ (r & 7)) << 4));
-        if (ch < nch) st128(rs, (uint32_t)((r * ldd + n0 + 8 * ch) * 2), v);
+        if (ch < nch) {
+            const int col = n0 + 8 * ch;
+            if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((r * ldd + col) * 2), v, ncols - col);
+            else st128(rs, (uint32_t)((r * ldd + col) * 2), v);
+        }
     }
     asm volatile("" ::: "memory");
 }
@@ -430,9 +528,14 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int d[C::NST + 1];
+    // d: the widths the kernel lays out (padded to whole granules where it
+    // takes tails); dt: the true widths
+    int d[C::NST + 1], dt[C::NST + 1];
 #pragma unroll
-    for (int i = 0; i <= C::NST; ++i) d[i] = args.dims[i];
+    for (int i = 0; i <= C::NST; ++i) {
+        dt[i] = args.dims[i];
+        d[i] = C::TAIL ? (dt[i] + 31) / 32 * 32 : dt[i];
+    }
     GenMat mat[C::NST];
     int off = 0;
 #pragma unroll
@@ -463,7 +566,7 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         auto bf_at = [&](int s) { return C::RTM && ((args.tmask >> s) & 1); };
         auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
             if constexpr (C::OUT8) gen_store_pair_f8(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
-            else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane, bf_at(C::NST));
+            else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane, bf_at(C::NST), dt[C::NST]);
         };
         // GEMM S on operand x with the sink: its compiled type, or a uniform
         // branch to the type the run-time mask gives
@@ -515,21 +618,26 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         const int b = t / tr.TB;
         tr.segment(t);
         __syncthreads();   // the previous segment's weight reads are over
-        gen_stage_weights<C>(lds, mat, args, b);
+        if constexpr (C::TAIL) gen_stage_weights_tail<C>(lds, mat, dt, args, b);
+        else gen_stage_weights<C>(lds, mat, args, b);
         __syncthreads();
+        auto load = [&](u4_t (&a)[C::MKS], int tt) __attribute__((always_inline)) {
+            if constexpr (C::TAIL) gen_load_a_tail<C>(a, a_rsrc(tt), args.lda, ks0, dt[0], lane);
+            else gen_load_a<C>(a, a_rsrc(tt), no_rsrc, args.lda, ks0, lane);
+        };
         if constexpr (C::PF == 0) {
             for (; t < tr.t_end; ++t) {
-                gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+                load(ring[0], t);
                 process(t, ring[0]);
             }
         } else {
             // two register sets: the next tile's A is in flight while this one is computed
-            gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+            load(ring[0], t);
             for (;;) {
-                gen_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                load(ring[1], t + 1);
                 process(t, ring[0]);
                 if (++t >= tr.t_end) break;
-                gen_load_a<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                load(ring[0], t + 1);
                 process(t, ring[1]);
                 if (++t >= tr.t_end) break;
             }

@@ -26,9 +26,14 @@ namespace b2bk {
 
 // NST_: GEMMs (1..6); MAXD_: bound on every width; PF_: A tiles fetched ahead;
 // GRP_: output tiles computed together.
-template <int NST_, int MAXD_, int PF_, int GRP_>
+// TAIL_: any widths and any leading dimensions and batch strides: K is
+// padded to a multiple of 8 and every N to a multiple of 16 on chip (weights
+// zero-filled in LDS, A's columns past K read as zero, D's columns past N not
+// written).
+template <int NST_, int MAXD_, int PF_, int GRP_, bool TAIL_ = false>
 struct Gen64Cfg {
     static constexpr int DT = DT_F64, NST = NST_, MAXD = MAXD_, PF = PF_, GRP = GRP_;
+    static constexpr bool TAIL = TAIL_;
     static constexpr int MODE = MODE_RELABEL;                 // the layouts coincide
     static constexpr int WAVES = 8, THREADS = 64 * WAVES, ROWS_WAVE = 16, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 4, MNT = MAXD / 16;     // K-steps, 16-column tiles
@@ -36,6 +41,12 @@ struct Gen64Cfg {
     static_assert(MAXD % 16 == 0 && NST >= 1 && NST <= kMaxStages && (PF == 0 || PF == 1), "config");
     static_assert(GRP == 2 || GRP == 4, "tile group");
 };
+
+// the widths a kernel lays out: K to a multiple of 8 and every N to one of
+// 16 where the kernel takes tails, else as given
+__host__ __device__ inline void gen64_pad(const int32_t* d, int nst, bool tail, int32_t* out) {
+    for (int i = 0; i <= nst; ++i) out[i] = !tail ? d[i] : i == 0 ? (d[i] + 7) / 8 * 8 : (d[i] + 15) / 16 * 16;
+}
 
 __host__ __device__ inline int64_t gen64_weight_bytes(const int32_t* d, int nst) {
     int64_t b = 0;
@@ -99,6 +110,67 @@ __device__ inline void gen64_stage_weights(unsigned char* lds, const int (&d)[C:
     }
 }
 
+// A 16-byte piece of two fp64 elements of which `valid` lie inside the row:
+// whole, one 16-byte access at any 8-byte alignment; half, one 8-byte
+// access; none, nothing (zeros)
+__device__ __forceinline__ u4_t ld_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t off, int valid) {
+    if (valid >= 2) return ld128(rs, off);
+    if (valid == 1) {
+        const u2_t x = ld64(rs, off);
+        return u4_t{x[0], x[1], 0u, 0u};
+    }
+    return u4_t{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ void st_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
+    if (valid >= 2) st128(rs, off, v);
+    else if (valid == 1) __builtin_amdgcn_raw_buffer_store_b64(u2_t{v[0], v[1]}, rs, (int)off, 0, kStreamPolicy);
+}
+
+// weights of batch b -> LDS, zero-padded to the laid-out widths d (dt: true)
+template <class C>
+__device__ inline void gen64_stage_weights_tail(unsigned char* lds, const int (&d)[C::NST + 1],
+                                                const int (&dt)[C::NST + 1], const KArgs& args, int b) {
+    int off = 0;
+#pragma unroll
+    for (int s = 0; s < C::NST; ++s) {
+        const int rows = d[s], n = d[s + 1], cpr = n / 2, total = rows * cpr;   // 16-byte pieces
+        const int rows_t = dt[s], cols_t = dt[s + 1];
+        const auto rs = make_rsrc((const char*)args.B[s] + (int64_t)b * args.sB[s] * 8,
+                                  (uint32_t)(rows_t * args.ldb[s] * 8));
+        for (int i0 = 0; i0 < total; i0 += 8 * C::THREADS) {
+            u4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 2;
+                const int valid = (i < total && r < rows_t) ? cols_t - c : 0;
+                v[k] = ld_pair64(rs, (uint32_t)((r * args.ldb[s] + c) * 8), valid);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * C::THREADS + (int)threadIdx.x;
+                const int r = i / cpr, c = (i % cpr) * 2;
+                if (i < total) *(u4_t*)(lds + off + (c >> 4) * rows * 128 + r * 128 + (c & 15) * 8) = v[k];
+            }
+        }
+        off += rows * n * 8;
+    }
+}
+
+// gen64_load_a with a K tail (K: the true width)
+template <class C>
+__device__ __forceinline__ void gen64_load_a_tail(double (&a)[C::MKS], __amdgpu_buffer_rsrc_t rs, int64_t lda, int ks,
+                                                  int K, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < C::MKS / 2; ++p) {
+        const int c0 = 8 * p + 2 * g;
+        const u4_t v = ld_pair64(rs, (uint32_t)((m * lda + c0) * 8), 2 * p < ks ? K - c0 : 0);
+        a[2 * p] = djoin(u2_t{v[0], v[1]});
+        a[2 * p + 1] = djoin(u2_t{v[2], v[3]});
+    }
+}
+
 // A of one wave's 16 rows: load p brings k = 8p + 2g, 8p + 2g + 1 of row l%16,
 // the operands of K-steps 2p and 2p+1 (past K: an empty resource, zeros)
 template <class C>
@@ -117,9 +189,12 @@ __device__ __forceinline__ void gen64_load_a(double (&a)[C::MKS], __amdgpu_buffe
 // Lane (m, g) holds row m, columns 16i + g + 4v of tile i.  Staged: written
 // into the wave's region (16 rows x 512 bytes, 16-byte chunks XOR-swizzled by
 // row), read back as 2 rows x 512 bytes per store.
+// ncols: D's true width, where the kernel takes tails (columns past it are
+// not written).
 template <class C>
 __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, const d4_t (&acc)[C::GRP], int cnt,
-                                                  __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane) {
+                                                  __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane,
+                                                  int ncols = 0) {
     const int m = lane & 15, g = lane >> 4;
     if (stg < 0) {
 #pragma unroll
@@ -127,9 +202,10 @@ __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, c
             if (i < cnt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
+                    const int col = n0 + 16 * i + g + 4 * v;
                     const u2_t x = dsplit(acc[i][v]);
-                    __builtin_amdgcn_raw_buffer_store_b64(x, rs, (int)((m * ldd + n0 + 16 * i + g + 4 * v) * 8), 0,
-                                                          kStreamPolicy);
+                    if (!C::TAIL || col < ncols)
+                        __builtin_amdgcn_raw_buffer_store_b64(x, rs, (int)((m * ldd + col) * 8), 0, kStreamPolicy);
                 }
         return;
     }
@@ -147,7 +223,11 @@ __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, c
     for (int k = 0; k < 8; ++k) {
         const int r = 2 * k + (lane >> 5);
         const u4_t x = *(const u4_t*)(st + r * 512 + ((q ^ r) << 4));
-        if (q < nq) st128(rs, (uint32_t)((r * ldd + n0 + 2 * q) * 8), x);
+        if (q < nq) {
+            const int col = n0 + 2 * q;
+            if constexpr (C::TAIL) st_pair64(rs, (uint32_t)((r * ldd + col) * 8), x, ncols - col);
+            else st128(rs, (uint32_t)((r * ldd + col) * 8), x);
+        }
     }
     asm volatile("" ::: "memory");
 }
@@ -192,9 +272,13 @@ __device__ __forceinline__ void gen64_body(const KArgs& args) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int d[C::NST + 1];
+    // d: the widths the kernel lays out (padded where it takes tails); dt: true
+    int d[C::NST + 1], dt[C::NST + 1];
 #pragma unroll
-    for (int i = 0; i <= C::NST; ++i) d[i] = args.dims[i];
+    for (int i = 0; i <= C::NST; ++i) {
+        dt[i] = args.dims[i];
+        d[i] = !C::TAIL ? dt[i] : i == 0 ? (dt[i] + 7) / 8 * 8 : (dt[i] + 15) / 16 * 16;
+    }
     Gen64Frag fr[C::NST];
     int off = 0;
 #pragma unroll
@@ -233,7 +317,7 @@ __device__ __forceinline__ void gen64_body(const KArgs& args) {
         const auto d_rs = make_rsrc((char*)args.D + ((int64_t)(t / TB) * args.sD + (rows ? row0 : 0) * args.ldd) * 8,
                                     (uint32_t)(rows * args.ldd * 8));
         auto to_d = [&](int tt, const d4_t (&acc)[C::GRP], int cnt) __attribute__((always_inline)) {
-            gen64_store_group<C>(lds, stg, acc, cnt, d_rs, args.ldd, 16 * tt, lane);
+            gen64_store_group<C>(lds, stg, acc, cnt, d_rs, args.ldd, 16 * tt, lane, dt[C::NST]);
         };
         if constexpr (C::NST == 1) {
             gen64_gemm<C, true>(lds, fr[0], a, ks0, dn / 16, to_d);
@@ -269,20 +353,25 @@ __device__ __forceinline__ void gen64_body(const KArgs& args) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         __syncthreads();   // the previous segment's weight reads are over
-        gen64_stage_weights<C>(lds, d, args, b);
+        if constexpr (C::TAIL) gen64_stage_weights_tail<C>(lds, d, dt, args, b);
+        else gen64_stage_weights<C>(lds, d, args, b);
         __syncthreads();
+        auto load = [&](double (&a)[C::MKS], int tt) __attribute__((always_inline)) {
+            if constexpr (C::TAIL) gen64_load_a_tail<C>(a, a_rsrc(tt), args.lda, ks0, dt[0], lane);
+            else gen64_load_a<C>(a, a_rsrc(tt), no_rsrc, args.lda, ks0, lane);
+        };
         if constexpr (C::PF == 0) {
             for (; t < t_end; ++t) {
-                gen64_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+                load(ring[0], t);
                 process(t, ring[0]);
             }
         } else {
-            gen64_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+            load(ring[0], t);
             for (;;) {
-                gen64_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                load(ring[1], t + 1);
                 process(t, ring[0]);
                 if (++t >= t_end) break;
-                gen64_load_a<C>(ring[0], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                load(ring[0], t + 1);
                 process(t, ring[1]);
                 if (++t >= t_end) break;
             }

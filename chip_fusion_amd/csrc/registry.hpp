@@ -24,6 +24,7 @@ struct KernelDesc {
     int f8 = 0;       // 1: two GEMMs, the second on the fp8 instruction; 2: one fp8 GEMM (dtd: D's type)
     int dtd = -1;
     int out8 = 0;     // 1: D written as fp8 E4M3 bytes
+    int tail = 0;     // 1: any widths, leading dimensions and batch strides (padded on chip)
     const void* fn;   // the __global__ function, for occupancy queries
     // dynamic LDS bytes for the widths d[0..nst] (run-time-width kernels), else 0
     int64_t (*dyn_lds)(const int32_t* d) = nullptr;
@@ -105,14 +106,22 @@ KernelDesc describe_gen() {
     d.maxd = C::MAXD;
     d.tm = C::TM;
     d.out8 = C::OUT8 ? 1 : 0;
+    d.tail = C::TAIL ? 1 : 0;
     d.fn = (const void*)&b2bk::gen_kernel<C>;
-    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen_lds_bytes(w, C::NST, C::WAVES); };
+    // LDS for the widths the kernel lays out (padded where it takes tails)
+    d.dyn_lds = [](const int32_t* w) -> int64_t {
+        int32_t p[b2bk::kMaxStages + 1];
+        b2bk::gen_pad(w, C::NST, C::TAIL, p);
+        return b2bk::gen_lds_bytes(p, C::NST, C::WAVES);
+    };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
         // dynamic LDS up to the whole 160 KB of a CU
         static const hipError_t attr = hipFuncSetAttribute(
             (const void*)&b2bk::gen_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
         if (attr != hipSuccess) return attr;
-        const size_t shm = (size_t)b2bk::gen_lds_bytes(a.dims, C::NST, C::WAVES);
+        int32_t p[b2bk::kMaxStages + 1];
+        b2bk::gen_pad(a.dims, C::NST, C::TAIL, p);
+        const size_t shm = (size_t)b2bk::gen_lds_bytes(p, C::NST, C::WAVES);
         hipLaunchKernelGGL(b2bk::gen_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };
@@ -234,13 +243,20 @@ KernelDesc describe_gen64() {
     d.lds_bytes = 0;
     d.rtw = 1;
     d.maxd = C::MAXD;
+    d.tail = C::TAIL ? 1 : 0;
     d.fn = (const void*)&b2bk::gen64_kernel<C>;
-    d.dyn_lds = [](const int32_t* w) -> int64_t { return b2bk::gen64_lds_bytes(w, C::NST); };
+    d.dyn_lds = [](const int32_t* w) -> int64_t {
+        int32_t p[b2bk::kMaxStages + 1];
+        b2bk::gen64_pad(w, C::NST, C::TAIL, p);
+        return b2bk::gen64_lds_bytes(p, C::NST);
+    };
     d.launch = [](const b2bk::KArgs& a, int grid, hipStream_t s) -> hipError_t {
         static const hipError_t attr = hipFuncSetAttribute(
             (const void*)&b2bk::gen64_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_MAX);
         if (attr != hipSuccess) return attr;
-        const size_t shm = (size_t)b2bk::gen64_lds_bytes(a.dims, C::NST);
+        int32_t p[b2bk::kMaxStages + 1];
+        b2bk::gen64_pad(a.dims, C::NST, C::TAIL, p);
+        const size_t shm = (size_t)b2bk::gen64_lds_bytes(p, C::NST);
         hipLaunchKernelGGL(b2bk::gen64_kernel<C>, dim3(grid), dim3(C::THREADS), shm, s, a);
         return hipGetLastError();
     };

@@ -125,15 +125,30 @@ typedef struct b2b_gemm_plan* b2b_gemm_t;   /* opaque, owned by the library */
  *   batch_stride  batch strides in elements: {A, B0, B1, B2, D}; NULL means dense;
  *                 0 for a B* broadcasts it
  *   flags         B2B_FLAG_* | B2B_REMAP_*
+ * Widths and layouts: K, N1, N2 (, N3) may be any positive values and the
+ * leading dimensions and batch strides any values at least the row width
+ * (page 1 derives the relation for whatever operators are adjacent; nothing
+ * ties it to a size granule).  Cascades whose widths are whole granules of
+ * the instructions (fp16/bf16: multiples of 32; fp64: K of 8, N of 16) and
+ * whose rows and batches start on 16-byte boundaries run on the kernels
+ * described with the flags; the others -- one type throughout (fp16, bf16
+ * or fp64), rearrangement AUTO or RELABEL -- run on kernels that pad every
+ * width to the granule on chip (zero weights in LDS, zero columns of A past
+ * K, D's columns past N not written), fused when the padded widths stay
+ * within the run-time-width bounds (fp16/bf16: 256 and the weights within
+ * LDS, one to three GEMMs; fp64: 64 for two or three GEMMs), unfused
+ * otherwise (one GEMM a kernel, fp16/bf16 to 256, fp64 to 128).
  * Returns INVALID_VALUE for non-positive sizes, ld below the row width, ld
- * not a multiple of 16 bytes, a leading dimension whose span over 32 rows of
+ * or a batch stride off a 16-byte multiple on a cascade the padding kernels
+ * do not take (a type per stage, tf32, fp8, orientation N, a rearrangement
+ * other than RELABEL), a leading dimension whose span over 32 rows of
  * A or D, or over all rows of a weight matrix, reaches 2^31 bytes (the
  * kernels' buffer offsets are 32-bit), unknown flags, or more than 2^31 - 1 row tiles
  * (batch x ceil(M / rows a workgroup takes)); NOT_SUPPORTED for cascades no
- * kernel covers: widths that break the granules or bounds of the run-time-width
- * kernels (see B2B_FLAG_MFMA_32X32) and have no fixed-width kernel, or weights
- * beyond LDS (then the caller may retry with B2B_FLAG_UNFUSED, whose per-GEMM
- * kernels need only one matrix in LDS).
+ * kernel covers: padded widths beyond the bounds above, a tail on a cascade
+ * the padding kernels do not take, or weights beyond LDS (then the caller may
+ * retry with B2B_FLAG_UNFUSED, whose per-GEMM kernels need only one matrix in
+ * LDS).
  */
 b2b_status_t b2b_gemm_create(b2b_gemm_t* plan, b2b_dtype_t dtype, int64_t batch, int64_t M,
                              int64_t K, int64_t N1, int64_t N2, int64_t N3,

@@ -62,15 +62,16 @@ def _create(**kw):
     (dict(M=0), 1), (dict(K=0), 1), (dict(N1=-1), 1), (dict(batch=0), 1), (dict(N3=-2), 1),
     (dict(dtype=7), 2),
     (dict(ld=[60, 64, 64, 0, 64]), 1),        # lda below K
-    (dict(ld=[68, 64, 64, 0, 64]), 1),        # lda not a multiple of 16 bytes
+    (dict(ld=[68, 64, 64, 0, 64], flags=1 << 4), 1),   # rows off 16-byte boundaries: only the
+                                                        # tail kernels take them, and they relabel
     (dict(flags=1 << 12), 1),                 # unknown flag
     (dict(flags=(7 << 4)), 1),                # unknown remap mode
     (dict(flags=2 | (2 << 4)), 1),            # orientation N with permlane
-    (dict(K=96, N1=80, N2=96), 2),            # N1 off the 32-column granule
-    (dict(K=80, N1=64, N2=64), 2),            # K off the 32-column granule
+    (dict(K=96, N1=80, N2=96, flags=2 | (1 << 4)), 2),  # a tail with orientation N
+    (dict(K=80, N1=64, N2=64, flags=3 << 4), 2),        # a tail with the LDS rearrangement
     (dict(K=96, N1=96, N2=288), 2),           # a width above 256
     (dict(dtype=2, K=96, N1=96, N2=160), 2),  # fp64: widths above 128
-    (dict(dtype=2, K=92, N1=96, N2=96), 2),   # fp64: K off the 8-column granule
+    (dict(dtype=2, K=92, N1=96, N2=96), 2),   # fp64 tails fuse up to 64 wide (96 pads to 96)
     (dict(K=256, N1=256, N2=256, flags=4), 2),         # 32x32 path: 256 KB of weights
     (dict(dtype=2, flags=4), 2),                       # 32x32 path: 16-bit types only
     (dict(flags=4 | (1 << 4)), 2),                     # 32x32 path: no coordination rounds
@@ -491,3 +492,35 @@ def test_static_run_checks_before_touching_the_device():
     assert run(0, 1, 65537, [64, 128, 64, 64]) == 5
     assert run(2, 8, 16384, [64, 64, 64]) == 5                   # fp64 workload 4: 64 MiB
     assert cf.STATIC_WORKSPACE_BYTES == 32 << 20
+
+
+@pytest.mark.parametrize("kw,tail,mfma", [
+    # widths off the granule: the tail kernels (32x32x16 for 16-bit, 16x16x4 for fp64)
+    (dict(K=100, N1=72, N2=50), 1, "32x32x16"),
+    (dict(dtype=1, K=100, N1=72, N2=50, N3=40), 1, "32x32x16"),
+    (dict(K=1, N1=1, N2=1), 1, "32x32x16"),
+    (dict(K=96, N1=80, N2=96), 1, "32x32x16"),
+    (dict(dtype=2, K=10, N1=20, N2=36), 1, "f64_16x16x4"),
+    (dict(dtype=2, K=10, N1=20, N2=36, N3=12), 1, "f64_16x16x4"),
+    # whole granules, rows off 16-byte boundaries (dense or padded)
+    (dict(ld=[68, 64, 64, 0, 64]), 1, "32x32x16"),
+    (dict(dtype=2, ld=[65, 64, 64, 0, 64]), 1, "f64_16x16x4"),
+    (dict(batch=2, bs=[128 * 64 + 4, 4096, 4096, 0, 128 * 64]), 1, "32x32x16"),
+    # whole granules on 16-byte rows: the kernels without tails
+    (dict(), 0, "16x16x32"),
+    (dict(ld=[72, 64, 64, 0, 64]), 0, "16x16x32"),
+])
+def test_tail_plan_selection(kw, tail, mfma):
+    """K and N tails, and rows at any element alignment, plan onto the tail
+    kernels; whole granules on 16-byte rows keep the kernels without tails."""
+    info = _info(**kw)
+    assert info["tail"] == str(tail) and info["mfma"] == mfma and info["path"] == "fused", info
+
+
+def test_tail_bounds():
+    """Tails fuse within the padded bounds: 16-bit to 256 with all weights in
+    LDS, fp64 to 64 for two or three GEMMs."""
+    assert _create(K=250, N1=150, N2=130)[0] == 0
+    assert _create(K=250, N1=250, N2=250)[0] == 2          # 2 x 256 x 256 x 2 bytes of weights
+    assert _create(dtype=2, K=60, N1=60, N2=60)[0] == 0
+    assert _create(dtype=2, K=60, N1=70, N2=60)[0] == 2    # 70 pads to 80 > 64
