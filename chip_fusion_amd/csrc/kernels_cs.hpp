@@ -73,8 +73,15 @@ struct CsCfg {
     // (conflict-free fragment reads of 16 consecutive rows)
     __device__ static inline int apos(int row, int chunk) { return row * ROW_A + ((chunk ^ (row & 15)) << 4); }
     __device__ static inline int cpos(int row, int chunk) { return row * N1 * ELT + ((chunk ^ (row & 15)) << 4); }
-    // D slice: 32 rows x 128 B, chunk swizzled so 16 consecutive rows cover all banks
-    __device__ static inline int dpos(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+    // D slice: 32 rows x 128 B, chunk swizzled so that the rows one 16-byte
+    // store touches -- 8 or 16 consecutive rows, one chunk each, however
+    // many lanes the LDS serves a cycle -- and the two rows one read covers
+    // fall on distinct banks (the pairing (row >> 1) of an earlier layout
+    // put rows 2j and 2j + 1 of a store on one bank: 12 % of LDS-active
+    // cycles were conflicts)
+    __device__ static inline int dpos(int row, int chunk) {
+        return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+    }
 };
 
 template <class C>
