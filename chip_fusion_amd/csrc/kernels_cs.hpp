@@ -138,7 +138,12 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         const int nseg = t_end - t;
-        barrier_lds();   // the previous segment's LDS reads are over
+        // The previous segment's LDS reads are over, and its A loads past the
+        // segment's end have landed: with an empty resource they still write
+        // (zeros) into ring slots that this segment's weight chunks, copied by
+        // other waves, are about to fill.
+        if (first) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier_lds();
         // A prefetch depth ramps up: tiles 0..last(-1) before the first step,
         // then up to two more per step until PF tiles are ahead.  Issuing all
         // PF tiles at once delays tile 0 (every workgroup asks for its whole
