@@ -30,7 +30,7 @@ EXPORTS = ("b2b_gemm_create", "b2b_gemm_run", "b2b_chain_create", "b2b_chain_cre
            "b2b_remap_execute", "b2b_remap_probe",
            "b2b_mfma_probe", "b2b_fp8_convert_probe")
 # measurement instruments (b2b_bench.h)
-BENCH_EXPORTS = ("b2b_bench_mfma", "b2b_bench_copy")
+BENCH_EXPORTS = ("b2b_bench_mfma", "b2b_bench_copy", "b2b_bench_stream")
 
 
 class B2BError(RuntimeError):
@@ -76,6 +76,7 @@ def lib():
         L.b2b_fp8_convert_probe.argtypes = [vp, vp, vp]
         L.b2b_bench_mfma.argtypes = [i32, i32, i64, vp, ctypes.POINTER(ctypes.c_double), vp]
         L.b2b_bench_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.b2b_bench_stream.argtypes = [vp, i64, vp, i64, i32, vp]
         for n in EXPORTS + BENCH_EXPORTS:
             if n not in ("b2b_status_string",):
                 getattr(L, n).restype = i32
@@ -370,12 +371,30 @@ def bench_mfma(dtype, workgroups, iters, sink, stream=None):
     return flop.value
 
 
+def _stream_operands(src, dst):
+    for name, x in (("src", src), ("dst", dst)):
+        if x.device.type != "cuda" or not x.is_contiguous():
+            raise ValueError(f"{name}: a contiguous device tensor is expected")
+    return src.numel() * src.element_size(), dst.numel() * dst.element_size()
+
+
 def bench_copy(src, dst, workgroups, stream=None):
     """Enqueues the HBM stream dst = src over all of src's bytes (b2b_bench_copy)."""
-    n = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < n or src.device.type != "cuda" or dst.device.type != "cuda":
-        raise ValueError("src and dst: device tensors, dst at least as large as src")
+    n, m = _stream_operands(src, dst)
+    if m < n:
+        raise ValueError("dst must be at least as large as src")
     _check(lib().b2b_bench_copy(_ptr(src), _ptr(dst), n, workgroups, _stream_ptr(stream)), "b2b_bench_copy")
+
+
+def bench_stream(src, dst, workgroups, stream=None):
+    """Enqueues the mixed stream (b2b_bench_stream): all of src's bytes read as
+    R back-to-back streams, XOR-folded into all of dst's bytes, R = src bytes /
+    dst bytes (an integer, 1 to 4)."""
+    n, m = _stream_operands(src, dst)
+    if m < 64 or n % m or not 1 <= n // m <= 4:
+        raise ValueError("src must hold 1 to 4 times dst's bytes, dst at least 64 bytes")
+    _check(lib().b2b_bench_stream(_ptr(src), n, _ptr(dst), m, workgroups, _stream_ptr(stream)),
+           "b2b_bench_stream")
 
 
 def to_device(x, dtype, device="cuda"):

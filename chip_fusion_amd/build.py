@@ -32,18 +32,19 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-# host-only sources: planning, validation and launch code, no device code
-HOST_SOURCES = ("api.hip", "plan.cpp", "plan.hpp")
+# sources with no cascade kernel in them: planning, validation and launch
+# code, and the measurement instruments (matrix-core loop, copy and stream)
+NON_CASCADE_SOURCES = ("api.hip", "plan.cpp", "plan.hpp", "microbench.hip")
 
 
 def source_digest():
-    """sha256 over the code (comments and layout aside) of the device sources
-    the library is built from (kernel headers and instance lists), used to
-    tell whether stored profiler counters still describe the current kernels."""
+    """sha256 over the code (comments and layout aside) of the sources the
+    cascade kernels are built from (kernel headers and instance lists), used
+    to tell whether stored profiler counters still describe those kernels."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if f.endswith((".hip", ".hpp")) and os.path.basename(f) not in HOST_SOURCES:
+        if f.endswith((".hip", ".hpp")) and os.path.basename(f) not in NON_CASCADE_SOURCES:
             h.update(os.path.basename(f).encode())
             h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]

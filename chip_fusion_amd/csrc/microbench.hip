@@ -85,6 +85,38 @@ __global__ __launch_bounds__(256) void copy_kernel(const u4_t* __restrict__ src,
     for (; i < n16; i += stride) __builtin_nontemporal_store(src[i], &dst[i]);
 }
 
+// dst[i] = src[i] ^ src[i + n] ^ ... ^ src[i + (R - 1) n]: R read streams of
+// n 16-byte pieces for one written stream, two outputs per thread and round
+// (2R loads in flight), grid stride, non-temporal stores
+template <int R>
+__global__ __launch_bounds__(256) void stream_kernel(const u4_t* __restrict__ src, u4_t* __restrict__ dst,
+                                                     int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + stride < n16; i += 2 * stride) {
+        u4_t v[2][R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            v[0][k] = src[i + k * n16];
+            v[1][k] = src[i + stride + k * n16];
+        }
+        u4_t x = v[0][0], y = v[1][0];
+#pragma unroll
+        for (int k = 1; k < R; ++k) {
+            x ^= v[0][k];
+            y ^= v[1][k];
+        }
+        __builtin_nontemporal_store(x, &dst[i]);
+        __builtin_nontemporal_store(y, &dst[i + stride]);
+    }
+    for (; i < n16; i += stride) {
+        u4_t x = src[i];
+#pragma unroll
+        for (int k = 1; k < R; ++k) x ^= src[i + k * n16];
+        __builtin_nontemporal_store(x, &dst[i]);
+    }
+}
+
 }  // namespace b2bk
 
 extern "C" {
@@ -126,6 +158,26 @@ b2b_status_t b2b_bench_copy(const void* src, void* dst, int64_t bytes, int32_t w
     if (s < d + bytes && d < s + bytes) return B2B_ERROR_INVALID_VALUE;
     hipLaunchKernelGGL(b2bk::copy_kernel, dim3(workgroups), dim3(256), 0, stream, (const b2bk::u4_t*)src,
                        (b2bk::u4_t*)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
+}
+
+b2b_status_t b2b_bench_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                              int32_t workgroups, hipStream_t stream) {
+    if (!src || !dst || write_bytes < 64 || write_bytes % 64 || read_bytes < write_bytes ||
+        read_bytes % write_bytes || read_bytes / write_bytes > 4 || (uintptr_t)src % 16 || (uintptr_t)dst % 16 ||
+        workgroups < 1 || workgroups > 65536)
+        return B2B_ERROR_INVALID_VALUE;
+    const char *s = (const char*)src, *d = (const char*)dst;
+    if (s < d + write_bytes && d < s + read_bytes) return B2B_ERROR_INVALID_VALUE;
+    const int64_t n16 = write_bytes / 16;
+    const auto* in = (const b2bk::u4_t*)src;
+    auto* out = (b2bk::u4_t*)dst;
+    switch (read_bytes / write_bytes) {
+        case 1: hipLaunchKernelGGL(b2bk::copy_kernel, dim3(workgroups), dim3(256), 0, stream, in, out, n16); break;
+        case 2: hipLaunchKernelGGL(b2bk::stream_kernel<2>, dim3(workgroups), dim3(256), 0, stream, in, out, n16); break;
+        case 3: hipLaunchKernelGGL(b2bk::stream_kernel<3>, dim3(workgroups), dim3(256), 0, stream, in, out, n16); break;
+        default: hipLaunchKernelGGL(b2bk::stream_kernel<4>, dim3(workgroups), dim3(256), 0, stream, in, out, n16); break;
+    }
     return hipGetLastError() == hipSuccess ? B2B_SUCCESS : B2B_ERROR_HIP;
 }
 

@@ -47,6 +47,22 @@ b2b_status_t b2b_bench_mfma(b2b_dtype_t dtype, int32_t workgroups, int64_t iters
  */
 b2b_status_t b2b_bench_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups, hipStream_t stream);
 
+/*
+ * HBM stream with a read:write mix: dst[i] = src[i] ^ src[i + n] ^ ... over
+ * 16-byte pieces, R = read_bytes / write_bytes read streams of n pieces each
+ * (src holds them back to back) for the one written stream of n pieces.  Fed
+ * a cascade's own A (read) and D (written) buffers, it moves exactly the
+ * bytes the cascade must move to and from HBM, at the rate the memory system
+ * gives a pure stream of that mix -- the cascade's practical memory roofline.
+ * R = 1 is the copy above.
+ *   src, dst     device pointers, 16-byte aligned, not overlapping
+ *   read_bytes   R * write_bytes, 1 <= R <= 4
+ *   write_bytes  a multiple of 64
+ *   workgroups   1..65536 workgroups of 256 threads, grid stride
+ */
+b2b_status_t b2b_bench_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                              int32_t workgroups, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,14 @@ def test_bench_instruments_reject_bad_arguments():
     assert L.b2b_bench_copy(p, ctypes.c_void_p(0x100000), 100, 4, None) == 1     # not whole 64 bytes
     assert L.b2b_bench_copy(p, ctypes.c_void_p(0x1040), 128, 4, None) == 1       # overlapping
     assert L.b2b_bench_copy(ctypes.c_void_p(0x1008), ctypes.c_void_p(0x100000), 128, 4, None) == 1
+    q = ctypes.c_void_p(0x100000)
+    assert L.b2b_bench_stream(p, 256, q, 100, 4, None) == 1                      # not whole 64 bytes
+    assert L.b2b_bench_stream(p, 192, q, 128, 4, None) == 1                      # not a whole ratio
+    assert L.b2b_bench_stream(p, 640, q, 128, 4, None) == 1                      # ratio above 4
+    assert L.b2b_bench_stream(p, 64, q, 128, 4, None) == 1                       # fewer bytes read than written
+    assert L.b2b_bench_stream(p, 512, ctypes.c_void_p(0x1100), 128, 4, None) == 1   # dst inside src
+    assert L.b2b_bench_stream(p, 256, q, 128, 0, None) == 1                      # no workgroups
+    assert L.b2b_bench_stream(ctypes.c_void_p(0x1008), 256, q, 128, 4, None) == 1   # misaligned
 
 
 def _create(**kw):
