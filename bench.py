@@ -15,8 +15,9 @@ median block gives ms_per_step, min and max are reported beside it.
 Prints one JSON line: TFLOP/s of the whole job, the dominant kernel's
 roofline figures (algorithmic bytes or FLOP over its measured duration), the
 fractions of the measured matrix-core and HBM ceilings (kernels of the same
-library that run only matrix instructions, or only a copy stream), and the
-CPU oracle timed on a bounded sample of the same workload.
+library that run only matrix instructions, only a copy stream, or a stream of
+the workload's own A and D bytes over its own buffers), and the CPU oracle
+timed on a bounded sample of the same workload.
 
 --summarize-trace FILE reads a rocprofv3 kernel trace (CSV) and prints, per
 kernel, the median, min and max duration of the last N launches (the timed
