@@ -121,10 +121,9 @@ bool whole_granules(int dt, int nst, const int64_t* d) {
     return true;
 }
 
-// Two GEMMs, the second in fp8: first GEMM's type dt, D's type dtd; K a
-// multiple of 32, N1 of 64, N2 of 32, each within the bound, weights in LDS.
-// Four-wave instances rank first where two of their workgroups fit a CU's
-// LDS, then eight-wave ones, then four-wave ones alone on a CU.
+// Rank among fitting instances of one width bound: four-wave instances
+// first where two of their workgroups fit a CU's LDS, then eight-wave ones,
+// then four-wave ones alone on a CU.
 int wave_rank(const KernelDesc& d, const int64_t* dims, int nst) {
     int32_t d32[kMaxSt + 1] = {};
     for (int i = 0; i <= nst; ++i) d32[i] = (int32_t)dims[i];
@@ -153,6 +152,8 @@ bool f8_fits(const KernelDesc& d, int dt, int dtd, const int64_t* dims) {
     return dims[0] * dims[1] * 2 + dims[1] * dims[2] <= 160 * 1024;
 }
 
+// Two GEMMs, the second in fp8: the fitting instance with the smallest
+// width bound, ranked by waves among equal bounds.
 const KernelDesc* find_f8(int dt, int dtd, const int64_t* dims) {
     const KernelDesc* best = nullptr;
     for (const KernelDesc& d : b2b::registry()) {
