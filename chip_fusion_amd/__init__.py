@@ -277,6 +277,15 @@ def chain_run_static(dtype, batch, M, widths, A, Bs, D, ld=None, batch_stride=No
     return D
 
 
+def _need(t, nbytes, name):
+    """ValueError unless t is a contiguous device tensor of at least nbytes:
+    the probe kernels read and write fixed sizes, whatever the tensor holds."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{name}: a contiguous device tensor is expected")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {nbytes} bytes expected, the tensor holds {t.numel() * t.element_size()}")
+
+
 def remap_relation(shape, orient_n=False):
     """Relation table of one remap unit and elements per lane (b2b_remap_relation)."""
     sh = SHAPES[shape] if isinstance(shape, str) else shape
@@ -323,6 +332,11 @@ def remap_execute(p, q, r, payload, stream=None):
     """Runs compiled rounds on a device int32/uint32 tensor [64 * E] (b2b_remap_execute)."""
     p, q, r = (np.ascontiguousarray(x, np.int32).reshape(-1) for x in (p, q, r))
     E = p.size // 64
+    if p.size % 64 or q.size != p.size or r.size != p.size:
+        raise ValueError("p, q, r: [E, 64] each")
+    if payload.dtype not in (torch.int32, torch.uint32) or payload.numel() != 64 * E:
+        raise ValueError(f"payload: 64 * E = {64 * E} 32-bit values expected")
+    _need(payload, 256 * E, "payload")
     out = torch.empty_like(payload)
     _check(lib().b2b_remap_execute(E, E, p.ctypes.data, q.ctypes.data, r.ctypes.data, _ptr(payload), _ptr(out),
                                    _stream_ptr(stream)), "b2b_remap_execute")
@@ -332,6 +346,7 @@ def remap_execute(p, q, r, payload, stream=None):
 def remap_probe(shape, mode, inp, orient_n=False, stream=None):
     """Runs the device rearrangement executor `mode` on payload tensor `inp`."""
     sh = SHAPES[shape] if isinstance(shape, str) else shape
+    _need(inp, 2048 if sh == SHAPES["f64_16x16x4"] else 1024, "inp")   # 4 doubles or 8 16-bit values a lane
     out = torch.empty_like(inp)
     st = lib().b2b_remap_probe(sh, int(orient_n), REMAP[mode] << 4, _ptr(inp), _ptr(out),
                                _stream_ptr(stream))
@@ -345,6 +360,9 @@ def mfma_probe(shape, a, b, stream=None):
     sh = SHAPES[shape] if isinstance(shape, str) else shape
     acc_dtype = torch.float64 if a.dtype == torch.float64 else torch.float32
     nacc = 16 if sh in (SHAPES["f16_32x32x16"], SHAPES["bf16_32x32x16"], SHAPES["fp8_32x32x64"]) else 4
+    per_lane = 8 if sh == SHAPES["f64_16x16x4"] else (32 if sh == SHAPES["fp8_32x32x64"] else 16)
+    _need(a, 64 * per_lane, "a")
+    _need(b, 64 * per_lane, "b")
     c = torch.empty((64, nacc), dtype=acc_dtype, device=a.device)
     _check(lib().b2b_mfma_probe(sh, _ptr(a), _ptr(b), _ptr(c), _stream_ptr(stream)), "b2b_mfma_probe")
     return c

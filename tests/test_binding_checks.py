@@ -60,3 +60,19 @@ def test_chain_types_and_tune_sets():
     with pytest.raises(ValueError, match="D: the plan addresses"):
         q.tune([(Af, [Bf, Bf], torch.zeros((1, 63, 64), dtype=torch.float64))])
     q.close()
+
+
+def test_probe_bindings_refuse_host_and_short_tensors():
+    """The layout, rearrangement and round-executor probes read fixed sizes
+    (16 bytes a lane, 8 for fp64, 32 for fp8; 64 * E words); tensors in host
+    memory, or ones that do not hold those sizes, are refused first."""
+    with pytest.raises(ValueError, match="device"):
+        cf.mfma_probe("f16_16x16x32", _t((64, 8)), _t((64, 8)))
+    with pytest.raises(ValueError, match="device"):
+        cf.remap_probe("f16_16x16x32", "relabel", _t((512,), torch.int16))
+    with pytest.raises(ValueError, match="device"):
+        cf.remap_execute([[0] * 64], [[0] * 64], [[0] * 64], torch.zeros(64, dtype=torch.int32))
+    with pytest.raises(ValueError, match="64 \\* E"):
+        cf.remap_execute([[0] * 64], [[0] * 64], [[0] * 64], torch.zeros(32, dtype=torch.int32))
+    with pytest.raises(ValueError, match=r"\[E, 64\]"):
+        cf.remap_execute([[0] * 64], [[0] * 63], [[0] * 64], torch.zeros(64, dtype=torch.int32))
