@@ -122,14 +122,24 @@ __device__ inline u4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline u2_t ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
-// Cache policy of D's stores: D is written once, so it goes non-temporal (nt)
-// and does not displace the weights from the caches.  A's loads keep the
+// Cache policy of D's stores: D is written once, so stores that write whole
+// 128-byte row segments go non-temporal (nt) and do not displace the weights
+// from the caches.  Stores that write parts of a line (D straight from the
+// accumulator layout, the last chunk of a ragged row) keep the default
+// policy, so that the L2 merges a line's pieces before writing it back: sent
+// non-temporal, a line's pieces reached HBM separately (28 % more bytes
+// written than D holds, on the tf32 three-GEMM kernel).  A's loads keep the
 // default policy: non-temporal A loads measured no better on the two-GEMM
 // fp16 workload and 1-3 % slower on the three-GEMM and fp64 ones.
 constexpr int kStreamPolicy = 2;
 
+// whole row segments of D
 __device__ inline void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, u4_t v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamPolicy);
+}
+// a piece of a line of D
+__device__ inline void st128_part(__amdgpu_buffer_rsrc_t r, uint32_t off, u4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 __device__ inline void st64(__amdgpu_buffer_rsrc_t r, uint32_t off, u2_t v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);

@@ -173,16 +173,20 @@ __device__ __forceinline__ u4_t ld_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t o
     return v;
 }
 // the store counterpart: only the chunk's first `valid` elements are written
+// (a whole chunk with the policy of its caller's stores: `part` for a piece
+// of a line; the elements of a partial chunk always as pieces)
+template <bool PART = false>
 __device__ __forceinline__ void st_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
     if (valid >= 8) {
-        st128(rs, off, v);
+        if constexpr (PART) st128_part(rs, off, v);
+        else st128(rs, off, v);
         return;
     }
 #pragma unroll
     for (int e = 0; e < 7; ++e)
         if (e < valid)
             __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), rs,
-                                                  (int)(off + 2 * e), 0, kStreamPolicy);
+                                                  (int)(off + 2 * e), 0, 0);
 }
 
 // weights of batch b -> LDS, each matrix padded with zeros to the whole
@@ -363,8 +367,8 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
         for (int q = 0; q < 4; ++q)
             if (q < 2 || two) {
                 const int col = n0 + 16 * q + 8 * h;
-                if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((m * ldd + col) * 2), c[q], ncols - col);
-                else st128(rs, (uint32_t)((m * ldd + col) * 2), c[q]);
+                if constexpr (C::TAIL) st_chunk16<true>(rs, (uint32_t)((m * ldd + col) * 2), c[q], ncols - col);
+                else st128_part(rs, (uint32_t)((m * ldd + col) * 2), c[q]);
             }
         return;
     }
@@ -417,7 +421,7 @@ __device__ __forceinline__ void gen_store_pair_f8(unsigned char* lds, int stg, c
             for (int a = 0; a < 4; ++a)
                 if (q == 0 || two)
                     __builtin_amdgcn_raw_buffer_store_b32(w[q][a], rs, (int)(m * ldd + n0 + 32 * q + 8 * a + 4 * h), 0,
-                                                          kStreamPolicy);
+                                                          0);
         return;
     }
     unsigned char* st = lds + stg;
@@ -431,7 +435,7 @@ __device__ __forceinline__ void gen_store_pair_f8(unsigned char* lds, int stg, c
     for (int i = 0; i < 2; ++i) {
         const int r = 16 * i + (lane >> 2);
         const u4_t v = *(const u4_t*)(st + r * 64 + 16 * ch);
-        if (ch < nch) st128(rs, (uint32_t)(r * ldd + n0 + 16 * ch), v);
+        if (ch < nch) st128_part(rs, (uint32_t)(r * ldd + n0 + 16 * ch), v);   // 64 bytes of a line
     }
     asm volatile("" ::: "memory");
 }

@@ -123,7 +123,7 @@ __device__ __forceinline__ u4_t ld_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t of
 }
 __device__ __forceinline__ void st_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
     if (valid >= 2) st128(rs, off, v);
-    else if (valid == 1) __builtin_amdgcn_raw_buffer_store_b64(u2_t{v[0], v[1]}, rs, (int)off, 0, kStreamPolicy);
+    else if (valid == 1) __builtin_amdgcn_raw_buffer_store_b64(u2_t{v[0], v[1]}, rs, (int)off, 0, 0);
 }
 
 // weights of batch b -> LDS, zero-padded to the laid-out widths d (dt: true)
@@ -205,7 +205,7 @@ __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, c
                     const int col = n0 + 16 * i + g + 4 * v;
                     const u2_t x = dsplit(acc[i][v]);
                     if (!C::TAIL || col < ncols)
-                        __builtin_amdgcn_raw_buffer_store_b64(x, rs, (int)((m * ldd + col) * 8), 0, kStreamPolicy);
+                        __builtin_amdgcn_raw_buffer_store_b64(x, rs, (int)((m * ldd + col) * 8), 0, 0);
                 }
         return;
     }

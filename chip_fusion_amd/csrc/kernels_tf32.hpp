@@ -247,7 +247,7 @@ __device__ __forceinline__ void tf32_store_tile(unsigned char* lds, int stg, con
                     __float_as_uint(acc[4 * a + 3])};
     if (stg < 0) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) st128(rs, (uint32_t)((m * ldd + n0 + 8 * a + 4 * h) * 4), c[a]);
+        for (int a = 0; a < 4; ++a) st128_part(rs, (uint32_t)((m * ldd + n0 + 8 * a + 4 * h) * 4), c[a]);
         return;
     }
     unsigned char* st = lds + stg;
