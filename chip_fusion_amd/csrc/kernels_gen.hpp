@@ -173,12 +173,12 @@ __device__ __forceinline__ u4_t ld_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t o
     return v;
 }
 // the store counterpart: only the chunk's first `valid` elements are written
-// (a whole chunk with the policy of its caller's stores: `part` for a piece
-// of a line; the elements of a partial chunk always as pieces)
-template <bool PART = false>
-__device__ __forceinline__ void st_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
+// (a whole chunk non-temporal unless `part`, i.e. it comes straight from the
+// accumulator layout, unstaged; the elements of a partial chunk always with
+// the default policy: sent non-temporal, 2-byte stores each went to HBM)
+__device__ __forceinline__ void st_chunk16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid, bool part) {
     if (valid >= 8) {
-        if constexpr (PART) st128_part(rs, off, v);
+        if (part) st128_part(rs, off, v);
         else st128(rs, off, v);
         return;
     }
@@ -367,7 +367,7 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
         for (int q = 0; q < 4; ++q)
             if (q < 2 || two) {
                 const int col = n0 + 16 * q + 8 * h;
-                if constexpr (C::TAIL) st_chunk16<true>(rs, (uint32_t)((m * ldd + col) * 2), c[q], ncols - col);
+                if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((m * ldd + col) * 2), c[q], ncols - col, true);
                 else st128_part(rs, (uint32_t)((m * ldd + col) * 2), c[q]);
             }
         return;
@@ -388,7 +388,7 @@ __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, cons
         const u4_t v = *(const u4_t*)(st + r * 128 + ((ch ^ (r & 7)) << 4));
         if (ch < nch) {
             const int col = n0 + 8 * ch;
-            if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((r * ldd + col) * 2), v, ncols - col);
+            if constexpr (C::TAIL) st_chunk16(rs, (uint32_t)((r * ldd + col) * 2), v, ncols - col, false);
             else st128(rs, (uint32_t)((r * ldd + col) * 2), v);
         }
     }
@@ -435,7 +435,7 @@ __device__ __forceinline__ void gen_store_pair_f8(unsigned char* lds, int stg, c
     for (int i = 0; i < 2; ++i) {
         const int r = 16 * i + (lane >> 2);
         const u4_t v = *(const u4_t*)(st + r * 64 + 16 * ch);
-        if (ch < nch) st128_part(rs, (uint32_t)(r * ldd + n0 + 16 * ch), v);   // 64 bytes of a line
+        if (ch < nch) st128(rs, (uint32_t)(r * ldd + n0 + 16 * ch), v);
     }
     asm volatile("" ::: "memory");
 }

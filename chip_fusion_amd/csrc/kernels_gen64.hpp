@@ -121,8 +121,9 @@ __device__ __forceinline__ u4_t ld_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t of
     }
     return u4_t{0u, 0u, 0u, 0u};
 }
-__device__ __forceinline__ void st_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid) {
-    if (valid >= 2) st128(rs, off, v);
+__device__ __forceinline__ void st_pair64(__amdgpu_buffer_rsrc_t rs, uint32_t off, u4_t v, int valid, bool part) {
+    if (valid >= 2 && part) st128_part(rs, off, v);
+    else if (valid >= 2) st128(rs, off, v);
     else if (valid == 1) __builtin_amdgcn_raw_buffer_store_b64(u2_t{v[0], v[1]}, rs, (int)off, 0, 0);
 }
 
@@ -225,7 +226,7 @@ __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, c
         const u4_t x = *(const u4_t*)(st + r * 512 + ((q ^ r) << 4));
         if (q < nq) {
             const int col = n0 + 2 * q;
-            if constexpr (C::TAIL) st_pair64(rs, (uint32_t)((r * ldd + col) * 8), x, ncols - col);
+            if constexpr (C::TAIL) st_pair64(rs, (uint32_t)((r * ldd + col) * 8), x, ncols - col, false);
             else st128(rs, (uint32_t)((r * ldd + col) * 8), x);
         }
     }
