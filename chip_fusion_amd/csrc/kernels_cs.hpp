@@ -24,8 +24,8 @@
 //
 // The weights reach the registers through LDS at the start of each batch
 // segment: 64-row chunks of B0 and B1 are copied row-major into LDS (buffer
-// loads that write LDS, three chunks in flight, in the space the A ring and
-// the C0 buffers use later), and each wave picks its fragments out of them
+// loads that write LDS, four chunks in flight, in the space the A ring, the
+// C0 buffers and the D slices use later), and each wave picks its fragments out of them
 // with transposing LDS reads (ds_read_b64_tr_b16: a 4 x 16 block of 16-bit
 // values comes back one column per lane), so the MFMA operand's K-contiguous
 // layout needs no separate re-layout pass over the weights.
@@ -47,7 +47,6 @@ struct CsCfg {
     static constexpr int KS0 = K / 32, KS1 = N1 / 32;            // K-steps of each GEMM
     static constexpr int ABYTES = R * K * ELT, CBYTES = R * N1 * ELT, DSLICE = R * N2W * ELT;
     static constexpr int OFF_C = NA * ABYTES, OFF_D = OFF_C + 2 * CBYTES;
-    static constexpr int LDS_BYTES = OFF_D + YW * DSLICE;
     static constexpr int A_LOADS = ABYTES / (16 * 64 * XW);      // 1 KB loads per first-GEMM wave per tile
     static constexpr int ROW_A = K * ELT, CPR_A = ROW_A / 16;    // bytes, 16-byte chunks per row of A
     static constexpr int ROWS_LOAD = 1024 / ROW_A;               // rows of A per 1 KB load
@@ -56,17 +55,20 @@ struct CsCfg {
     static_assert(ABYTES % (16 * 64 * XW) == 0 && 1024 % ROW_A == 0 && CPR_A >= 16,
                   "A tile must split into whole 1 KB loads of whole rows");
     static_assert(DCH == 8, "D slices are written as 128-byte row segments");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(PF <= 5 && A_LOADS == 4, "wait counts");
     // weight staging: chunks of 64 rows (32 KB) of B0 then B1, row-major, 16-byte
     // chunks swizzled so the transposing fragment reads are conflict-free
     static constexpr int WROWS = 64, WCH = WROWS * N1 * ELT;      // rows and bytes per chunk
     static constexpr int NCH0 = K / WROWS, NCH = NCH0 + N1 / WROWS;
     static constexpr int W_LOADS = WCH / (16 * 64 * WAVES);       // 1 KB loads per wave per chunk
+    static constexpr int NWB = 4;                                 // staging buffers = chunks in flight
+    // the fourth staging buffer starts at the D slices and runs past them
+    static constexpr int LDS_BYTES = (OFF_D + YW * DSLICE > OFF_D + WCH) ? OFF_D + YW * DSLICE : OFF_D + WCH;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(N1 * ELT == 512 && N2 * ELT == 512 && K % WROWS == 0 && N1 % WROWS == 0,
                   "weight staging is written for rows of 512 bytes");
     static_assert(NCH0 == 4 && NCH == 8 && W_LOADS == 4 && NA >= 6,
-                  "staging buffers: ring slots 2-3, 4-5 and the C0 buffers");
+                  "staging buffers: ring slots 2-3, 4-5, the C0 buffers and the D slices");
     __device__ static inline int wswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 3) << 2)); }
     __device__ static inline int wpos(int r, int chunk) { return r * 512 + ((chunk ^ wswz(r)) << 4); }
     // row-major A and C0 tiles, 16-byte chunks XOR-swizzled by row
@@ -133,17 +135,53 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
         }
     };
 
+    // Weights: chunk c (64 rows of B0 for c < 4, of B1 after) goes to staging
+    // buffer c % 4 -- ring slots 2-3, ring slots 4-5, the C0 buffers, the D
+    // slices -- while ring slots 0-1 receive A tiles 0 and 1.  Order of
+    // issue: chunks 0-3, A tiles 0-1 (first-GEMM waves), then chunk c+4 once
+    // chunk c has been read.
+    auto buf = [&](int c) -> unsigned char* {
+        const int i = c % C::NWB;
+        return lds + (i == 0 ? 2 * C::ABYTES : i == 1 ? 4 * C::ABYTES : i == 2 ? C::OFF_C : C::OFF_D);
+    };
+    auto load_chunk = [&](int b, int c) {
+        const int mat = c < C::NCH0 ? 0 : 1, c4 = mat ? c - C::NCH0 : c;
+        const int64_t rows = mat ? C::N1 : C::K;
+        const auto rs = make_rsrc((const char*)args.B[mat] + (int64_t)b * args.sB[mat] * C::ELT,
+                                  (uint32_t)(rows * args.ldb[mat] * C::ELT));
+        unsigned char* dst = buf(c);
+#pragma unroll
+        for (int i = 0; i < C::W_LOADS; ++i) {
+            const int q = wave * C::W_LOADS + i;                 // 1 KB piece: rows 2q, 2q+1 of the chunk
+            const int r = 2 * q + lane / 32, pos = lane % 32;
+            const int chunk = pos ^ C::wswz(r);                  // lands at wpos(r, chunk)
+            lds_dma16<false>(rs, dst + q * 1024, (int)((C::WROWS * c4 + r) * args.ldb[mat] * C::ELT) + chunk * 16);
+        }
+    };
+
+    // The first segment's first chunks go out before anything else: the
+    // compiler computes the addresses the rest of the kernel needs at entry
+    // (~400 instructions a wave, ~1 us), which would otherwise delay them.
     int t = t0;
+    bool issued = true;
+#pragma unroll
+    for (int c = 0; c < C::NWB; ++c) load_chunk(t0 / TB, c);
+    __builtin_amdgcn_sched_barrier(0);
     while (t < t1) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
         const int nseg = t_end - t;
-        // The previous segment's LDS reads are over, and its A loads past the
-        // segment's end have landed: with an empty resource they still write
-        // (zeros) into ring slots that this segment's weight chunks, copied by
-        // other waves, are about to fill.
-        if (first) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        barrier_lds();
+        if (!issued) {
+            // The previous segment's LDS reads are over, and its A loads past
+            // the segment's end have landed: with an empty resource they still
+            // write (zeros) into ring slots that this segment's weight chunks,
+            // copied by other waves, are about to fill.
+            if (first) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            barrier_lds();
+#pragma unroll
+            for (int c = 0; c < C::NWB; ++c) load_chunk(b, c);
+        }
+        issued = false;
         // A prefetch depth ramps up: tiles 0..last(-1) before the first step,
         // then up to two more per step until PF tiles are ahead.  Issuing all
         // PF tiles at once delays tile 0 (every workgroup asks for its whole
@@ -152,29 +190,6 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
         // as the weights are in.
         auto last = [&](int s) { return s < 0 ? 1 : (2 * s + 3 < s + C::PF ? 2 * s + 3 : s + C::PF); };
 
-        // Weights: chunk c (64 rows of B0 for c < 4, of B1 after) goes to
-        // staging buffer c % 3 -- ring slots 2-3, ring slots 4-5, the C0
-        // buffers -- while ring slots 0-1 receive A tiles 0 and 1.  Order of
-        // issue: chunks 0-2, A tiles 0-1 (first-GEMM waves), then chunk c+3
-        // once chunk c has been read.
-        auto buf = [&](int c) -> unsigned char* {
-            const int i = c % 3;
-            return lds + (i == 0 ? 2 * C::ABYTES : i == 1 ? 4 * C::ABYTES : C::OFF_C);
-        };
-        auto load_chunk = [&](int c) {
-            const int mat = c < C::NCH0 ? 0 : 1, c4 = mat ? c - C::NCH0 : c;
-            const int64_t rows = mat ? C::N1 : C::K;
-            const auto rs = make_rsrc((const char*)args.B[mat] + (int64_t)b * args.sB[mat] * C::ELT,
-                                      (uint32_t)(rows * args.ldb[mat] * C::ELT));
-            unsigned char* dst = buf(c);
-#pragma unroll
-            for (int i = 0; i < C::W_LOADS; ++i) {
-                const int q = wave * C::W_LOADS + i;                 // 1 KB piece: rows 2q, 2q+1 of the chunk
-                const int r = 2 * q + lane / 32, pos = lane % 32;
-                const int chunk = pos ^ C::wswz(r);                  // lands at wpos(r, chunk)
-                lds_dma16<false>(rs, dst + q * 1024, (int)((C::WROWS * c4 + r) * args.ldb[mat] * C::ELT) + chunk * 16);
-            }
-        };
         // fragment (16-column tile at n0, 32 rows from k0 of the chunk) of this
         // wave: two transposing reads, rows k0+8g+0..3 and k0+8g+4..7
         auto frag = [&](unsigned char* src, int n0, int k0) {
@@ -192,22 +207,22 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
             }
             return out;
         };
-        load_chunk(0);
-        load_chunk(1);
-        load_chunk(2);
         if (first)
             for (int k = 0; k <= last(-1); ++k) load_tile(t + k, k);
 #pragma unroll
         for (int c = 0; c < C::NCH; ++c) {
-            // wait for chunk c: chunks min(2, 7 - c) later, and (first-GEMM
-            // waves, c <= 2) the two A tiles issued after chunk 2, stay in flight
+            // wait for chunk c: chunks min(3, 7 - c) later, and (first-GEMM
+            // waves, c <= 3) the two A tiles issued after chunk 3, stay in flight
+            static_assert(C::NWB == 4 && C::NCH == 8, "wait counts");
             if (first) {
-                if (c <= 2) barrier_vm<2 * C::W_LOADS + 2 * C::A_LOADS>();
-                else if (c <= 5) barrier_vm<2 * C::W_LOADS>();
+                if (c <= 3) barrier_vm<3 * C::W_LOADS + 2 * C::A_LOADS>();
+                else if (c == 4) barrier_vm<3 * C::W_LOADS>();
+                else if (c == 5) barrier_vm<2 * C::W_LOADS>();
                 else if (c == 6) barrier_vm<C::W_LOADS>();
                 else barrier_vm<0>();
             } else {
-                if (c <= 5) barrier_vm<2 * C::W_LOADS>();
+                if (c <= 4) barrier_vm<3 * C::W_LOADS>();
+                else if (c == 5) barrier_vm<2 * C::W_LOADS>();
                 else if (c == 6) barrier_vm<C::W_LOADS>();
                 else barrier_vm<0>();
             }
@@ -220,7 +235,7 @@ __device__ __forceinline__ void cs_body(const KArgs& args) {
                         w[n][(C::WROWS / 32) * c4 + kl] = frag(buf(c), C::N1W * sw + 16 * n, 32 * kl);
             }
             barrier_lds();   // chunk c has been read: its buffer is free
-            if (c + 3 < C::NCH) load_chunk(c + 3);
+            if (c + C::NWB < C::NCH) load_chunk(b, c + C::NWB);
         }
         // here the weights are in registers and A tiles 0 and 1 are in LDS
         for (int s = 0; s <= nseg; ++s) {
