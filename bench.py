@@ -225,16 +225,20 @@ def measure_stream(cf, torch, stream, sets, steps, repeats):
             "reads_per_write": rb // wb, "workgroups": wg}
 
 
+DTYPE_NAMES = {"f16": "fp16", "bf16": "bf16", "f64": "fp64", "tf32": "tf32"}
+
+
 def measure(cfg_id, args, cf, torch, synth, oracle, cpu_seconds, ceilings=None, log=True):
     """One workload: build the plan and rotating buffer sets, warm up, time
     the blocks, check sampled rows against the oracle, time the oracle."""
     c = dict(synth.WORKLOADS[cfg_id])
     if args.dtype and args.dtype != c["dtype"]:
-        c["name"] = c["name"].replace(c["dtype"], args.dtype, 1)
+        # the name leads with the type ("fp16 b16 ..."): the new type's name replaces it
+        c["name"] = DTYPE_NAMES[args.dtype] + " " + c["name"].split(" ", 1)[1]
         c["dtype"] = args.dtype
     if args.dims:
         c["dims"] = [int(x) for x in args.dims.split(",")]
-        c["name"] = (f"{c['dtype']} b{c['batch']} {c['M']}x{c['dims'][0]} . "
+        c["name"] = (f"{DTYPE_NAMES[c['dtype']]} b{c['batch']} {c['M']}x{c['dims'][0]} . "
                      + " . ".join(f"{c['dims'][s]}x{c['dims'][s + 1]}" for s in range(len(c["dims"]) - 1)))
     dt = c["dtype"]
     types = args.types.split(",") if args.types else None

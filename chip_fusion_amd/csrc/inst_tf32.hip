@@ -5,7 +5,7 @@
 // (stages, max width, passes[, waves per workgroup])
 B2B_TF32_INSTANCE(1, 128, 3);
 B2B_TF32_INSTANCE(2, 128, 3);
-B2B_TF32_INSTANCE(3, 128, 3, 4);
+B2B_TF32_INSTANCE(3, 128, 3);
 B2B_TF32_INSTANCE(1, 128, 4);
 B2B_TF32_INSTANCE(2, 128, 4);
-B2B_TF32_INSTANCE(3, 128, 4, 4);
+B2B_TF32_INSTANCE(3, 128, 4);

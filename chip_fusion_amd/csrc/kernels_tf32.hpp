@@ -30,8 +30,7 @@ namespace b2bk {
 
 // NST_: GEMMs (1 for the unfused path); MAXD_: bound on every width;
 // PASSES_: 3 or 4; WAVES_: 8 (two waves per SIMD, up to 256 registers
-// each) or 4 (one wave per SIMD with up to 512, for the three-GEMM cascade,
-// whose middle GEMM holds its input and output operands).
+// each) or 4 (one wave per SIMD with up to 512).
 template <int NST_, int MAXD_, int PASSES_, int WAVES_ = 8>
 struct Tf32Cfg {
     static constexpr int DT = DT_TF32, NST = NST_, MAXD = MAXD_, PASSES = PASSES_;
@@ -238,7 +237,13 @@ __device__ __forceinline__ void tf32_to_operand(const f16x_t& acc, u4_t& h0, u4_
 // XOR-swizzled by row) each store writes 8 rows x 128 bytes; without one
 // the chunks go straight to memory.
 __device__ __forceinline__ void tf32_store_tile(unsigned char* lds, int stg, const f16x_t& acc,
-                                                __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane) {
+                                                __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane_) {
+    // the lane index passes through an empty asm statement so that the
+    // compiler computes the store offsets here, per tile, instead of keeping
+    // every tile's offsets in registers for the whole kernel (at two waves
+    // per SIMD the three-GEMM cascade would spill them)
+    int lane = lane_;
+    asm volatile("" : "+v"(lane));
     const int m = lane & 31, h = lane >> 5;
     u4_t c[4];
 #pragma unroll
@@ -314,13 +319,16 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
             for (int j = 0; j < C::MKS; ++j) tf32_operand(a[2 * j], a[2 * j + 1], xh[j], xl[j]);
             // this tile's A is consumed: the next one's loads go out -- all
             // at once where the registers allow (a single GEMM, or one wave
-            // per SIMD), else a quarter now and the rest before the last
-            // GEMM, when the split operands of the first are no longer live
+            // per SIMD), else before the last GEMM, when the split operands
+            // of the first are no longer live: a quarter now and the rest
+            // then for two GEMMs, all of it then for three (whose middle
+            // GEMM holds its input and output operands)
             constexpr bool EARLY = C::NST == 1 || C::WAVES == 4;
+            constexpr int Q = (EARLY || C::NST < 3) ? C::MKS / 4 : 0;   // K-steps loaded now
             auto issue_next = [&]() __attribute__((always_inline)) {
-                tf32_load_a<C, C::MKS / 4, C::MKS>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+                tf32_load_a<C, Q, C::MKS>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
             };
-            tf32_load_a<C, 0, C::MKS / 4>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
+            tf32_load_a<C, 0, Q>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
             if constexpr (EARLY) issue_next();
 
             const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, 4, t);

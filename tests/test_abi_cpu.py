@@ -310,7 +310,7 @@ def test_typed_rejects(dtypes, widths, flags, status):
     (dict(dtype=3, widths=(128, 128, 128)), dict(dtype="tf32", mfma="bf16x3_32x32x16", waves="8",
                                                  lds_bytes=str(128 * 128 * 2 * 4 + 8 * 4096))),
     (dict(dtype=3, widths=(128, 128, 128), flags=8), dict(mfma="bf16x4_32x32x16")),
-    (dict(dtype=3, widths=(128, 128, 128, 64)), dict(mfma="bf16x3_32x32x16", waves="4", rows_per_wg="128",
+    (dict(dtype=3, widths=(128, 128, 128, 64)), dict(mfma="bf16x3_32x32x16", waves="8", rows_per_wg="256",
                                                      lds_bytes=str(160 * 1024))),
     (dict(dtype=3, widths=(96, 64)), dict(dims="96x64", launches="1")),
 ])
