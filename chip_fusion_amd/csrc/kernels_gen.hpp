@@ -250,6 +250,28 @@ __device__ inline void gen_stage_weights(unsigned char* lds, const GenMat (&mat)
     }
 }
 
+// The same copy by buffer loads that write LDS (no registers, nothing to wait
+// for before the next instruction): one instruction moves 16 rows x 64 bytes
+// of one 32-column block -- lane l takes 16-byte chunk l%4 of row 16i + l/4 --
+// which is 1 KB of contiguous LDS in the GenMat layout.  Widths are whole
+// blocks here (the tail kernels stage through registers).
+template <class C>
+__device__ inline void gen_copy_weights(unsigned char* lds, const GenMat (&mat)[C::NST], const KArgs& args, int b,
+                                        int wave, int lane) {
+#pragma unroll
+    for (int s = 0; s < C::NST; ++s) {
+        const GenMat& m = mat[s];
+        const auto rs = make_rsrc((const char*)args.B[s] + (int64_t)b * args.sB[s] * 2,
+                                  (uint32_t)(m.rows * args.ldb[s] * 2));
+        const int rg = m.rows / 16, nq = rg * (m.n / 32);
+        for (int q = wave; q < nq; q += C::WAVES) {
+            const int blk = q / rg, i = q % rg, r = 16 * i + (lane >> 2);
+            lds_dma16<false>(rs, lds + m.off + blk * m.tstride + 1024 * i,
+                             (int)((r * args.ldb[s] + 32 * blk + 8 * (lane & 3)) * 2));
+        }
+    }
+}
+
 // A fragments of one wave's 32 rows: K-step j holds row l%32, k = 16j + 8*(l/32) + 0..7.
 // Two K-steps (64 bytes of a row) come from two loads of 16 rows x 64 bytes
 // each -- X: rows 0-15, Y: rows 16-31, lane group g holding 16-byte chunk g
@@ -550,13 +572,19 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
     const int ks0 = d[0] / 16, dn = d[C::NST];
     // the wave's D staging region follows the weights, where LDS allows
     const int stg = gen_stage_d(d, C::NST, C::WAVES) ? off + wave * 4096 : -1;
+
+    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
+    if (!tr.init(args, wave)) return;
+    // the first segment's weight copies go out before anything else: the
+    // compiler computes the addresses the rest of the kernel needs at entry
+    // (several hundred instructions a wave), which would otherwise delay them
+    if constexpr (!C::TAIL) gen_copy_weights<C>(lds, mat, args, tr.t0 / tr.TB, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
     constexpr bool REL = C::MODE == MODE_RELABEL;
     GenFrag fr[C::NST];
 #pragma unroll
     for (int s = 0; s < C::NST; ++s) fr[s].init(mat[s], REL && s > 0, lane);
 
-    TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
-    if (!tr.init(args, wave)) return;
     auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 2, t); };
 
     auto process = [&](int t, const u4_t (&a_in)[C::MKS]) __attribute__((always_inline)) {
@@ -618,25 +646,40 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
     const auto no_rsrc = make_rsrc(args.A, 0u);
     u4_t ring[C::PF + 1][C::MKS];
     int t = tr.t0;
+    bool issued = !C::TAIL;   // the first segment's weights are on their way
     while (t < tr.t1) {
         const int b = t / tr.TB;
         tr.segment(t);
-        __syncthreads();   // the previous segment's weight reads are over
-        if constexpr (C::TAIL) gen_stage_weights_tail<C>(lds, mat, dt, args, b);
-        else gen_stage_weights<C>(lds, mat, args, b);
-        __syncthreads();
         auto load = [&](u4_t (&a)[C::MKS], int tt) __attribute__((always_inline)) {
             if constexpr (C::TAIL) gen_load_a_tail<C>(a, a_rsrc(tt), args.lda, ks0, dt[0], lane);
             else gen_load_a<C>(a, a_rsrc(tt), no_rsrc, args.lda, ks0, lane);
         };
+        if constexpr (C::TAIL) {
+            __syncthreads();   // the previous segment's weight reads are over
+            gen_stage_weights_tail<C>(lds, mat, dt, args, b);
+            __syncthreads();
+            load(ring[0], t);
+        } else {
+            if (!issued) {
+                __syncthreads();   // the previous segment's weight reads are over
+                gen_copy_weights<C>(lds, mat, args, b, wave, lane);
+            }
+            issued = false;
+            // the segment's first A tile goes out behind the weights, and
+            // both are waited for here (the copies are not the compiler's to
+            // wait for)
+            load(ring[0], t);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
         if constexpr (C::PF == 0) {
-            for (; t < tr.t_end; ++t) {
-                load(ring[0], t);
+            for (;;) {
                 process(t, ring[0]);
+                if (++t >= tr.t_end) break;
+                load(ring[0], t);
             }
         } else {
             // two register sets: the next tile's A is in flight while this one is computed
-            load(ring[0], t);
             for (;;) {
                 load(ring[1], t + 1);
                 process(t, ring[0]);
