@@ -312,6 +312,15 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, const unsigned char*
 }
 #pragma clang diagnostic pop
 
+// This lane's index, computed where it is called: the compiler can neither
+// keep it (and the addresses derived from it) in a register across the
+// kernel nor fold it into an earlier computation.
+__device__ inline int lane_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 __device__ inline void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -40,7 +40,7 @@ struct F8Cfg {
     static_assert(DT != DT_F64 && DTD != DT_F64 && MAXD % 64 == 0 && (PF == 0 || PF == 1), "config");
     // the 16-bit weights (B0 alone) for gen_stage_weights
     struct Stage0 {
-        static constexpr int NST = 1, THREADS = 64 * WAVES_;
+        static constexpr int NST = 1, WAVES = WAVES_, THREADS = 64 * WAVES_;
     };
 };
 
@@ -119,6 +119,14 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
 
     TileRange<C::ROWS_WG, C::ROWS_WAVE> tr;
     if (!tr.init(args, wave)) return;
+    // Up to 128 wide the first segment's B0 copies go out before the entry
+    // arithmetic and the first A tile before B1's gather.  At 256 a tile of A
+    // is 128 KB a CU: ahead of the gather's byte loads in the memory pipeline
+    // it slows the gather more than the overlap gains (2-3 %), so there B0 is
+    // staged through registers and A follows the weights.
+    constexpr bool EARLY = C::MAXD <= 128;
+    if constexpr (EARLY) gen_copy_weights<typename C::Stage0>(lds, m0, args, tr.t0 / tr.TB, wave);
+    __builtin_amdgcn_sched_barrier(0);
     auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 2, t); };
 
     auto process = [&](int t, const u4_t (&a_in)[C::MKS]) __attribute__((always_inline)) {
@@ -154,20 +162,37 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
     const auto no_rsrc = make_rsrc(args.A, 0u);
     u4_t ring[C::PF + 1][C::MKS];
     int t = tr.t0;
+    bool issued = EARLY;   // the first segment's B0 is on its way
     while (t < tr.t1) {
         const int b = t / tr.TB;
         tr.segment(t);
-        __syncthreads();   // the previous segment's weight reads are over
-        gen_stage_weights<typename C::Stage0>(lds, m0, args, b);
-        f8_stage_b1<C>(lds, off1, args, b, d1, d2);
-        __syncthreads();
+        if constexpr (EARLY) {
+            if (!issued) {
+                __syncthreads();   // the previous segment's weight reads are over
+                gen_copy_weights<typename C::Stage0>(lds, m0, args, b, wave);
+            }
+            issued = false;
+            // the first A tile, then B1's gather (its LDS writes wait for its
+            // loads, and so, in order, for everything before them); then all
+            // of it, the copies included, before the barrier
+            gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+            f8_stage_b1<C>(lds, off1, args, b, d1, d2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        } else {
+            __syncthreads();   // the previous segment's weight reads are over
+            gen_stage_weights<typename C::Stage0>(lds, m0, args, b);
+            f8_stage_b1<C>(lds, off1, args, b, d1, d2);
+            __syncthreads();
+            gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+        }
         if constexpr (C::PF == 0) {
-            for (; t < tr.t_end; ++t) {
-                gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
+            for (;;) {
                 process(t, ring[0]);
+                if (++t >= tr.t_end) break;
+                gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
             }
         } else {
-            gen_load_a<C>(ring[0], a_rsrc(t), no_rsrc, args.lda, ks0, lane);
             for (;;) {
                 gen_load_a<C>(ring[1], a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
                 process(t, ring[0]);

@@ -257,7 +257,8 @@ __device__ inline void gen_stage_weights(unsigned char* lds, const GenMat (&mat)
 // blocks here (the tail kernels stage through registers).
 template <class C>
 __device__ inline void gen_copy_weights(unsigned char* lds, const GenMat (&mat)[C::NST], const KArgs& args, int b,
-                                        int wave, int lane) {
+                                        int wave) {
+    const int lane = lane_here();
 #pragma unroll
     for (int s = 0; s < C::NST; ++s) {
         const GenMat& m = mat[s];
@@ -578,7 +579,7 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
     // the first segment's weight copies go out before anything else: the
     // compiler computes the addresses the rest of the kernel needs at entry
     // (several hundred instructions a wave), which would otherwise delay them
-    if constexpr (!C::TAIL) gen_copy_weights<C>(lds, mat, args, tr.t0 / tr.TB, wave, lane);
+    if constexpr (!C::TAIL) gen_copy_weights<C>(lds, mat, args, tr.t0 / tr.TB, wave);
     __builtin_amdgcn_sched_barrier(0);
     constexpr bool REL = C::MODE == MODE_RELABEL;
     GenFrag fr[C::NST];
@@ -662,7 +663,7 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         } else {
             if (!issued) {
                 __syncthreads();   // the previous segment's weight reads are over
-                gen_copy_weights<C>(lds, mat, args, b, wave, lane);
+                gen_copy_weights<C>(lds, mat, args, b, wave);
             }
             issued = false;
             // the segment's first A tile goes out behind the weights, and

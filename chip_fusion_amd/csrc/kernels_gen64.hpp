@@ -80,6 +80,30 @@ __device__ __forceinline__ double gen64_wfrag(const unsigned char* lds, const Ge
     return *(const double*)(lds + fr.base + t * fr.tstride + 128 * kj);
 }
 
+// The same copy by buffer loads that write LDS: one instruction moves 8 rows
+// x 128 bytes of one 16-column block -- lane l takes 16-byte piece l%8 of row
+// 8i + l/8 -- which is 1 KB of contiguous LDS.  Widths are whole blocks here
+// (the tail kernels stage through registers).
+template <class C>
+__device__ inline void gen64_copy_weights(unsigned char* lds, const int (&d)[C::NST + 1], const KArgs& args, int b,
+                                          int wave) {
+    const int lane = lane_here();
+    int off = 0;
+#pragma unroll
+    for (int s = 0; s < C::NST; ++s) {
+        const int rows = d[s], n = d[s + 1];
+        const auto rs = make_rsrc((const char*)args.B[s] + (int64_t)b * args.sB[s] * 8,
+                                  (uint32_t)(rows * args.ldb[s] * 8));
+        const int rg = rows / 8, nq = rg * (n / 16);
+        for (int q = wave; q < nq; q += C::THREADS / 64) {
+            const int blk = q / rg, i = q % rg, r = 8 * i + (lane >> 3);
+            lds_dma16<false>(rs, lds + off + blk * rows * 128 + 1024 * i,
+                             (int)((r * args.ldb[s] + 16 * blk + 2 * (lane & 7)) * 8));
+        }
+        off += rows * n * 8;
+    }
+}
+
 // weights of batch b -> LDS, 16 columns per block (16-byte loads, eight in
 // flight per thread, every thread issuing the same loads)
 template <class C>
@@ -297,6 +321,9 @@ __device__ __forceinline__ void gen64_body(const KArgs& args) {
     const int t1 = t0 + per + (lid < extra ? 1 : 0);
     if (t0 >= t1) return;
     const int TB = args.tiles_per_batch;
+    // the first segment's weight copies go out before the entry arithmetic
+    if constexpr (!C::TAIL) gen64_copy_weights<C>(lds, d, args, t0 / TB, wave);
+    __builtin_amdgcn_sched_barrier(0);
 
     int t_end = t1;
     auto rows_of = [&](int t) {
@@ -350,24 +377,38 @@ __device__ __forceinline__ void gen64_body(const KArgs& args) {
     const auto no_rsrc = make_rsrc(args.A, 0u);
     double ring[C::PF + 1][C::MKS];
     int t = t0;
+    bool issued = !C::TAIL;   // the first segment's weights are on their way
     while (t < t1) {
         const int b = t / TB;
         t_end = (b + 1) * TB < t1 ? (b + 1) * TB : t1;
-        __syncthreads();   // the previous segment's weight reads are over
-        if constexpr (C::TAIL) gen64_stage_weights_tail<C>(lds, d, dt, args, b);
-        else gen64_stage_weights<C>(lds, d, args, b);
-        __syncthreads();
         auto load = [&](double (&a)[C::MKS], int tt) __attribute__((always_inline)) {
             if constexpr (C::TAIL) gen64_load_a_tail<C>(a, a_rsrc(tt), args.lda, ks0, dt[0], lane);
             else gen64_load_a<C>(a, a_rsrc(tt), no_rsrc, args.lda, ks0, lane);
         };
+        if constexpr (C::TAIL) {
+            __syncthreads();   // the previous segment's weight reads are over
+            gen64_stage_weights_tail<C>(lds, d, dt, args, b);
+            __syncthreads();
+            load(ring[0], t);
+        } else {
+            if (!issued) {
+                __syncthreads();   // the previous segment's weight reads are over
+                gen64_copy_weights<C>(lds, d, args, b, wave);
+            }
+            issued = false;
+            // the segment's first A tile goes out behind the weights; both
+            // are waited for here (the copies are not the compiler's to wait for)
+            load(ring[0], t);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
         if constexpr (C::PF == 0) {
-            for (; t < t_end; ++t) {
-                load(ring[0], t);
+            for (;;) {
                 process(t, ring[0]);
+                if (++t >= t_end) break;
+                load(ring[0], t);
             }
         } else {
-            load(ring[0], t);
             for (;;) {
                 load(ring[1], t + 1);
                 process(t, ring[0]);
