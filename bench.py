@@ -450,7 +450,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the cascade shards by rows with no exchange; see the design notes)", file=sys.stderr)
+              "(the cascade would shard by rows of A and D, each GPU holding every weight, with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     if args.tf32_exact and args.dtype != "tf32":
