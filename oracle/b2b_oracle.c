@@ -19,7 +19,7 @@
  * cascade so that the intermediate never leaves the chip; the value of the
  * cascade itself is the plain matrix product written out here.
  *
- * Readings where the pages are silent (they are listed in the design notes):
+ * Readings where the pages are silent:
  *   - accumulation: float32 for fp16/bf16 inputs, float64 for fp64 inputs;
  *     every output element sums its K products in ascending k order from +0;
  *   - rnd: round-to-nearest-even to the input type between stages and for D;
