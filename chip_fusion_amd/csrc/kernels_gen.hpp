@@ -378,8 +378,16 @@ __device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t&
 // not written; chunks straddling it are stored element by element).
 template <class C>
 __device__ __forceinline__ void gen_store_pair(unsigned char* lds, int stg, const f16x_t& acc0, const f16x_t& acc1,
-                                               bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane,
+                                               bool two, __amdgpu_buffer_rsrc_t rs, int64_t ldd, int n0, int lane_,
                                                bool bf = false, int ncols = 0) {
+    // From four GEMMs on the lane index passes through an empty asm statement,
+    // so that the store offsets are computed here, per tile pair, instead of
+    // being held in registers for the whole kernel: the longer chains need
+    // those registers (the run-time-typed ones spilled without this; the
+    // one-type five-GEMM chain runs 5 % faster).  Shorter cascades keep their
+    // offsets (recomputing them cost the three-GEMM run-time-typed instance 7 %).
+    int lane = lane_;
+    if constexpr (C::NST >= 4) asm volatile("" : "+v"(lane));
     const int m = lane & 31, h = lane >> 5;
     u4_t c[4];
     gen_regroup_d<C>(acc0, c[0], c[1], bf);

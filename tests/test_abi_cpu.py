@@ -280,6 +280,10 @@ def _typed(dtypes, widths, flags=0, batch=1, M=128):
     ((0, 1, 0, 1), (256, 64, 256, 64), dict(dtype="f16/bf16/f16/bf16", path="fused")),
     ((1, 0, 0, 1, 1, 0, 1, 0, 1), (64, 64, 128, 64, 96, 32, 128, 64, 96), dict(path="fused", launches="1")),
     ((0, 1, 0, 1, 1), (64, 32, 32, 32, 64), dict(dtype="f16/bf16/f16/bf16/bf16", path="fused")),
+    # four and five typed GEMMs past 128 wide
+    ((0, 1, 0, 1, 0), (256, 128, 128, 128, 64), dict(dtype="f16/bf16/f16/bf16/f16", path="fused",
+                                                     mfma="32x32x16", launches="1")),
+    ((1, 0, 1, 0, 1, 0), (256, 64, 192, 64, 128, 64), dict(dtype="bf16/f16/bf16/f16/bf16/f16", path="fused")),
     # one type throughout: the plan of b2b_chain_create
     ((1, 1, 1), (128, 128, 128), dict(dtype="bf16", mfma="16x16x32")),
     ((2, 2, 2), (64, 64, 64), dict(dtype="f64", mfma="f64_16x16x4")),
@@ -298,7 +302,7 @@ def test_typed_plan_selection(dtypes, widths, expect):
     ((0, 2, 0), (64, 64, 64), 0, 2),                              # fp64 mixed with a 16-bit type
     ((0, 1, 0, 1, 0, 1, 0, 1), (128,) * 8, 0, 2),                 # 224 KB of weights
     ((0, 1, 0, 1, 0, 1, 0, 1, 0, 1), (64,) * 10, 0, 1),           # nine GEMMs
-    ((0, 1, 0, 1, 0), (256, 128, 128, 128, 64), 0, 2),            # four or more typed GEMMs: widths up to 128
+    ((0, 1, 0, 1, 0, 1, 0), (256, 64, 64, 64, 64, 64, 64), 0, 2),    # six or more typed GEMMs: widths up to 128
     ((0, 5, 0), (128, 128, 128), 0, 2),                           # unknown type
 ])
 def test_typed_rejects(dtypes, widths, flags, status):

@@ -52,12 +52,15 @@ FUSED = [
     (("f16", "bf16", "f16", "bf16"), 2, 333, (128, 96, 128, 64)),
     (("bf16", "f16", "f16", "f16"), 1, 257, (64, 128, 32, 128)),
     (("f16", "f16", "f16", "bf16"), 2, 100, (128, 128, 128, 64)),
-    # mixtures read at run time: three GEMMs past 128 wide, four to six GEMMs
+    # mixtures read at run time: three to five GEMMs past 128 wide, four to seven GEMMs
     (("f16", "bf16", "f16", "bf16"), 2, 300, (256, 64, 256, 64)),
     (("f16", "bf16", "bf16", "f16", "f16"), 2, 333, (128, 128, 128, 128, 64)),
     (("bf16", "f16", "bf16", "f16", "bf16", "f16"), 1, 513, (64, 96, 128, 32, 128, 64)),
     (("bf16", "f16", "bf16", "f16", "bf16", "f16", "bf16"), 2, 257, (64, 96, 128, 32, 128, 64, 128)),
     (("f16", "f16", "bf16", "f16", "bf16", "bf16", "f16", "bf16"), 2, 300, (64, 96, 64, 128, 32, 64, 96, 64)),
+    # four and five GEMMs past 128 wide
+    (("f16", "bf16", "f16", "bf16", "f16"), 2, 300, (256, 128, 128, 128, 64)),
+    (("bf16", "f16", "bf16", "f16", "bf16", "f16"), 3, 257, (256, 64, 192, 64, 128, 64)),
     (("bf16", "f16", "f16", "bf16", "bf16", "f16", "bf16", "f16", "bf16"), 1, 513, (64, 64, 128, 64, 96, 32, 128, 64, 96)),
 ]
 
