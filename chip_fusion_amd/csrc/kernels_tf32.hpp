@@ -30,10 +30,15 @@ namespace b2bk {
 
 // NST_: GEMMs (1 for the unfused path); MAXD_: bound on every width;
 // PASSES_: 3 or 4; WAVES_: 8 (two waves per SIMD, up to 256 registers
-// each) or 4 (one wave per SIMD with up to 512).
-template <int NST_, int MAXD_, int PASSES_, int WAVES_ = 8>
+// each) or 4 (one wave per SIMD with up to 512).  F0_..F3_: widths fixed at
+// compile time (K, N1, ...; all zero: read at run time).  With the widths
+// known the K-step and tile loops lose their branches and the weight
+// fragment addresses become immediates.
+template <int NST_, int MAXD_, int PASSES_, int WAVES_ = 8, int F0_ = 0, int F1_ = 0, int F2_ = 0, int F3_ = 0>
 struct Tf32Cfg {
     static constexpr int DT = DT_TF32, NST = NST_, MAXD = MAXD_, PASSES = PASSES_;
+    static constexpr bool FIXED = F0_ > 0;
+    static constexpr int F(int i) { return i == 0 ? F0_ : i == 1 ? F1_ : i == 2 ? F2_ : F3_; }
     static constexpr int MODE = MODE_RELABEL;
     static constexpr int WAVES = WAVES_, THREADS = 64 * WAVES, ROWS_WAVE = 32, ROWS_WG = ROWS_WAVE * WAVES;
     static constexpr int MKS = MAXD / 16, MNT = MAXD / 32;
@@ -41,6 +46,10 @@ struct Tf32Cfg {
     static_assert(MAXD % 32 == 0 && NST >= 1 && NST <= kMaxStages, "config");
     static_assert(PASSES == 3 || PASSES == 4, "passes");
     static_assert(WAVES == 4 || WAVES == 8, "waves");
+    static_assert(!FIXED || (F(0) % 32 == 0 && F(0) <= MAXD && F(NST) % 32 == 0 && F(NST) <= MAXD &&
+                             (NST < 2 || (F(1) % 32 == 0 && F(1) <= MAXD)) &&
+                             (NST < 3 || (F(2) % 32 == 0 && F(2) <= MAXD))),
+                  "fixed widths: multiples of 32 within the bound");
 };
 
 // LDS bytes: every weight matrix as hi and lo parts (2 x 2 bytes per
@@ -281,7 +290,7 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int d[C::NST + 1];
 #pragma unroll
-    for (int i = 0; i <= C::NST; ++i) d[i] = args.dims[i];
+    for (int i = 0; i <= C::NST; ++i) d[i] = C::FIXED ? C::F(i) : args.dims[i];
     GenMat mh[C::NST], ml[C::NST];
     int off = 0;
 #pragma unroll

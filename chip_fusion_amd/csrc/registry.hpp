@@ -17,7 +17,7 @@ struct KernelDesc {
     int dtype, nst, dims[4], mode, orn, km0;
     int mt, waves, threads, rows_wg, lds_bytes;
     int shape32 = 0;  // 1: 32x32x16 instruction
-    int rtw = 0;      // 1: widths read at run time, up to maxd (dims are 0)
+    int rtw = 0;      // 1: widths read at run time, up to maxd (dims are 0), or fixed (dims)
     int maxd = 0;
     int tm = -1;      // type per stage (bit s: bf16 operands of GEMM s, bit nst: D), or -1: all dtype
     int passes = 0;   // tf32: bf16 matrix-instruction passes per product (3 or 4)
@@ -128,13 +128,15 @@ KernelDesc describe_gen() {
     return d;
 }
 
-// tf32 instances (bf16 passes on the 32x32x16 instruction), run-time widths.
+// tf32 instances (bf16 passes on the 32x32x16 instruction), widths read at
+// run time or, for the instances that fix them, compiled in (dims: those
+// widths, which a plan must match exactly).
 template <class C>
 KernelDesc describe_tf32() {
     KernelDesc d;
     d.dtype = C::DT;
     d.nst = C::NST;
-    for (int& x : d.dims) x = 0;   // never matched by width
+    for (int i = 0; i < 4; ++i) d.dims[i] = C::FIXED && i <= C::NST ? C::F(i) : 0;
     d.mode = C::NST > 1 ? C::MODE : 0;
     d.orn = 0;
     d.km0 = b2bk::KM_NAT;
@@ -333,7 +335,7 @@ ProbeDesc describe_probe() {
     B2B_GEN_INSTANCE(((B2B_FIRST(__VA_ARGS__)) & 1) ? ::b2bk::DT_BF16 : ::b2bk::DT_F16, NST, MAXD, \
                      ::b2bk::MODE_RELABEL, PF, __VA_ARGS__)
 #define B2B_FIRST(a, ...) a
-// B2B_TF32_INSTANCE(stages, max width, passes)
+// B2B_TF32_INSTANCE(stages, max width, passes[, waves[, fixed widths K, N1, ...]])
 #define B2B_TF32_INSTANCE(...)                                                         \
     static ::b2b::Registrar B2B_CAT(b2b_tf32_reg_, __LINE__)(                          \
         ::b2b::describe_tf32<::b2bk::Tf32Cfg<__VA_ARGS__>>())

@@ -312,11 +312,17 @@ def test_typed_rejects(dtypes, widths, flags, status):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(dtype=3, widths=(128, 128, 128)), dict(dtype="tf32", mfma="bf16x3_32x32x16", waves="8",
-                                                 lds_bytes=str(128 * 128 * 2 * 4 + 8 * 4096))),
-    (dict(dtype=3, widths=(128, 128, 128), flags=8), dict(mfma="bf16x4_32x32x16")),
+                                                 lds_bytes=str(128 * 128 * 2 * 4 + 8 * 4096), widths="compiled")),
+    (dict(dtype=3, widths=(128, 128, 128), flags=8), dict(mfma="bf16x4_32x32x16", widths="compiled")),
     (dict(dtype=3, widths=(128, 128, 128, 64)), dict(mfma="bf16x3_32x32x16", waves="8", rows_per_wg="256",
-                                                     lds_bytes=str(160 * 1024))),
-    (dict(dtype=3, widths=(96, 64)), dict(dims="96x64", launches="1")),
+                                                     lds_bytes=str(160 * 1024), widths="compiled")),
+    (dict(dtype=3, widths=(128, 128, 128, 64), flags=8), dict(mfma="bf16x4_32x32x16", widths="compiled")),
+    # other widths: the same kernels reading the widths at run time
+    (dict(dtype=3, widths=(128, 96, 128)), dict(waves="8", widths="runtime")),
+    (dict(dtype=3, widths=(128, 128, 128, 32)), dict(rows_per_wg="256", widths="runtime")),
+    (dict(dtype=3, widths=(96, 64)), dict(dims="96x64", launches="1", widths="runtime")),
+    # the fixed-width 16-bit kernels have their widths compiled in
+    (dict(dtype=0, widths=(128, 128, 128)), dict(widths="compiled")),
 ])
 def test_tf32_plan_selection(kw, expect):
     info = _chain_info(**kw)
