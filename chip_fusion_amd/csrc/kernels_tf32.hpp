@@ -328,12 +328,16 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
             for (int j = 0; j < C::MKS; ++j) tf32_operand(a[2 * j], a[2 * j + 1], xh[j], xl[j]);
             // this tile's A is consumed: the next one's loads go out -- all
             // at once where the registers allow (a single GEMM, or one wave
-            // per SIMD), else before the last GEMM, when the split operands
-            // of the first are no longer live: a quarter now and the rest
-            // then for two GEMMs, all of it then for three (whose middle
-            // GEMM holds its input and output operands)
+            // per SIMD), else in two parts, the second once the split
+            // operands of the first GEMM are no longer live.  Run-time
+            // widths: a quarter now and the rest before the last GEMM for two
+            // GEMMs, all of it before the last GEMM for three (whose middle
+            // GEMM holds its input and output operands).  Widths compiled in
+            // (fewer registers for addresses and loop state): half now, the
+            // rest before the last GEMM, or after the first of three.
             constexpr bool EARLY = C::NST == 1 || C::WAVES == 4;
-            constexpr int Q = (EARLY || C::NST < 3) ? C::MKS / 4 : 0;   // K-steps loaded now
+            constexpr bool MID = C::FIXED && C::NST == 3 && !EARLY;
+            constexpr int Q = C::FIXED ? C::MKS / 2 : (EARLY || C::NST < 3) ? C::MKS / 4 : 0;   // K-steps loaded now
             auto issue_next = [&]() __attribute__((always_inline)) {
                 tf32_load_a<C, Q, C::MKS>(a, a_rsrc(t + 1), no_rsrc, args.lda, ks0, lane);
             };
@@ -360,6 +364,7 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
                                };
                 };
                 tf32_gemm<C>(lds, fh[0], fl[0], xh, xl, ks0, d[1] / 32, to_ops(oAh, oAl));
+                if constexpr (MID) issue_next();
                 gen_static_for<1, C::NST - 1>([&](auto sc) __attribute__((always_inline)) {
                     constexpr int S = decltype(sc)::value;
                     if constexpr (S % 2 == 1)
@@ -368,7 +373,7 @@ __device__ __forceinline__ void tf32_body(const KArgs& args) {
                         tf32_gemm_kouter<C>(lds, fh[S], fl[S], oBh, oBl, d[S] / 16, d[S + 1] / 32, to_ops(oAh, oAl));
                 });
                 constexpr int L = C::NST - 1;
-                if constexpr (!EARLY) issue_next();
+                if constexpr (!EARLY && !MID) issue_next();
                 if constexpr (L % 2 == 1) tf32_gemm<C>(lds, fh[L], fl[L], oAh, oAl, d[L] / 16, dn / 32, to_d);
                 else tf32_gemm<C>(lds, fh[L], fl[L], oBh, oBl, d[L] / 16, dn / 32, to_d);
             }
