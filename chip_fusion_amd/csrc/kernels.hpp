@@ -312,6 +312,16 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, const unsigned char*
 }
 #pragma clang diagnostic pop
 
+// A wave-uniform count, made opaque where it is passed: the loops bounded by
+// it then compare and branch on scalars at each step.  Otherwise the compiler
+// evaluates every step's condition once, early, and keeps each result as a
+// 64-bit lane mask in scalar registers, which run out and spill to vector
+// lanes in the run-time-width kernels.
+__device__ __forceinline__ int uniform_here(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // This lane's index, computed where it is called: the compiler can neither
 // keep it (and the addresses derived from it) in a register across the
 // kernel nor fold it into an earlier computation.

@@ -142,17 +142,18 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
                                x8[tt / 2] = f8_operand(a0, a1);
                            });
         // second GEMM on the fp8 instruction, output tiles in pairs
+        const int nt2u = uniform_here(nt2), ks8u = uniform_here(ks8);
 #pragma unroll
         for (int t2 = 0; t2 < C::MNT; t2 += 2) {
-            if (t2 < nt2) {
-                const bool two = t2 + 1 < nt2;
+            if (t2 < nt2u) {
+                const bool two = t2 + 1 < nt2u;
                 const int t2b = two ? t2 + 1 : t2;
                 f16x_t acc0 = {}, acc1 = {};
 #pragma unroll
                 for (int j = 0; j < C::MKS8; ++j)
-                    if (j < ks8) {
-                        acc0 = f8_mma(f8_wfrag(lds, off1, ks8, t2, j, lane), x8[j], acc0);
-                        acc1 = f8_mma(f8_wfrag(lds, off1, ks8, t2b, j, lane), x8[j], acc1);
+                    if (j < ks8u) {
+                        acc0 = f8_mma(f8_wfrag(lds, off1, ks8u, t2, j, lane), x8[j], acc0);
+                        acc1 = f8_mma(f8_wfrag(lds, off1, ks8u, t2b, j, lane), x8[j], acc1);
                     }
                 gen_store_pair<C>(lds, stg, acc0, acc1, two, d_rs, args.ldd, 32 * t2, lane);
             }
@@ -261,17 +262,18 @@ __device__ __forceinline__ void f8a_body(const KArgs& args) {
     auto a_rsrc = [&](int t) { return tr.a_rsrc(args.A, args.lda, args.sA, 1, t); };
     auto process = [&](int t, const i8v_t (&x)[C::MKS8]) __attribute__((always_inline)) {
         const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, 2, t);
+        const int ntu = uniform_here(nt), ks8u = uniform_here(ks8);
 #pragma unroll
         for (int t2 = 0; t2 < C::MNT; t2 += 2) {
-            if (t2 < nt) {
-                const bool two = t2 + 1 < nt;
+            if (t2 < ntu) {
+                const bool two = t2 + 1 < ntu;
                 const int t2b = two ? t2 + 1 : t2;
                 f16x_t acc0 = {}, acc1 = {};
 #pragma unroll
                 for (int j = 0; j < C::MKS8; ++j)
-                    if (j < ks8) {
-                        acc0 = f8_mma(f8_wfrag(lds, 0, ks8, t2, j, lane), x[j], acc0);
-                        acc1 = f8_mma(f8_wfrag(lds, 0, ks8, t2b, j, lane), x[j], acc1);
+                    if (j < ks8u) {
+                        acc0 = f8_mma(f8_wfrag(lds, 0, ks8u, t2, j, lane), x[j], acc0);
+                        acc1 = f8_mma(f8_wfrag(lds, 0, ks8u, t2b, j, lane), x[j], acc1);
                     }
                 gen_store_pair<C>(lds, stg, acc0, acc1, two, d_rs, args.ldd, 32 * t2, lane);
             }

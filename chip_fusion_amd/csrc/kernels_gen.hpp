@@ -481,6 +481,8 @@ __device__ __forceinline__ void gen_store_pair_f8(unsigned char* lds, int stg, c
 template <class C, int SDT, class Sink>
 __device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag& fr, const u4_t (&x)[C::MKS],
                                          int ks, int nt, Sink&& sink) {
+    ks = uniform_here(ks);
+    nt = uniform_here(nt);
 #pragma unroll
     for (int t = 0; t < C::MNT; t += 2) {
         if (t < nt) {

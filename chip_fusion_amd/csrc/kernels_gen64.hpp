@@ -263,6 +263,8 @@ __device__ __forceinline__ void gen64_store_group(unsigned char* lds, int stg, c
 template <class C, bool FIRST, class Sink>
 __device__ __forceinline__ void gen64_gemm(const unsigned char* lds, const Gen64Frag& fr, const double (&x)[C::MKS],
                                            int ks, int nt, Sink&& sink) {
+    ks = uniform_here(ks);
+    nt = uniform_here(nt);
 #pragma unroll
     for (int t = 0; t < C::MNT; t += C::GRP) {
         if (t < nt) {

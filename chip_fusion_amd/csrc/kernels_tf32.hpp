@@ -170,6 +170,10 @@ template <class C, class Sink>
 __device__ __forceinline__ void tf32_gemm(const unsigned char* lds, const GenFrag& fh, const GenFrag& fl,
                                           const u4_t (&xh)[C::MKS], const u4_t (&xl)[C::MKS], int ks, int nt,
                                           Sink&& sink) {
+    if constexpr (!C::FIXED) {
+        ks = uniform_here(ks);
+        nt = uniform_here(nt);
+    }
 #pragma unroll
     for (int t = 0; t < C::MNT; t += 2) {
         if (t < nt) {
@@ -205,6 +209,10 @@ template <class C, class Sink>
 __device__ __forceinline__ void tf32_gemm_kouter(const unsigned char* lds, const GenFrag& fh, const GenFrag& fl,
                                                  const u4_t (&xh)[C::MKS], const u4_t (&xl)[C::MKS], int ks,
                                                  int nt, Sink&& sink) {
+    if constexpr (!C::FIXED) {
+        ks = uniform_here(ks);
+        nt = uniform_here(nt);
+    }
     f16x_t acc[C::MNT];
 #pragma unroll
     for (int t = 0; t < C::MNT; ++t) acc[t] = f16x_t{};
