@@ -148,9 +148,11 @@ __device__ __forceinline__ void f8_body(const KArgs& args) {
             if (t2 < nt2u) {
                 const bool two = t2 + 1 < nt2u;
                 const int t2b = two ? t2 + 1 : t2;
-                f16x_t acc0 = {}, acc1 = {};
+                // K-step 0 always exists: its products start from zero
+                f16x_t acc0 = f8_mma(f8_wfrag(lds, off1, ks8u, t2, 0, lane), x8[0], f16x_t{});
+                f16x_t acc1 = f8_mma(f8_wfrag(lds, off1, ks8u, t2b, 0, lane), x8[0], f16x_t{});
 #pragma unroll
-                for (int j = 0; j < C::MKS8; ++j)
+                for (int j = 1; j < C::MKS8; ++j)
                     if (j < ks8u) {
                         acc0 = f8_mma(f8_wfrag(lds, off1, ks8u, t2, j, lane), x8[j], acc0);
                         acc1 = f8_mma(f8_wfrag(lds, off1, ks8u, t2b, j, lane), x8[j], acc1);
@@ -268,9 +270,11 @@ __device__ __forceinline__ void f8a_body(const KArgs& args) {
             if (t2 < ntu) {
                 const bool two = t2 + 1 < ntu;
                 const int t2b = two ? t2 + 1 : t2;
-                f16x_t acc0 = {}, acc1 = {};
+                // K-step 0 always exists: its products start from zero
+                f16x_t acc0 = f8_mma(f8_wfrag(lds, 0, ks8u, t2, 0, lane), x[0], f16x_t{});
+                f16x_t acc1 = f8_mma(f8_wfrag(lds, 0, ks8u, t2b, 0, lane), x[0], f16x_t{});
 #pragma unroll
-                for (int j = 0; j < C::MKS8; ++j)
+                for (int j = 1; j < C::MKS8; ++j)
                     if (j < ks8u) {
                         acc0 = f8_mma(f8_wfrag(lds, 0, ks8u, t2, j, lane), x[j], acc0);
                         acc1 = f8_mma(f8_wfrag(lds, 0, ks8u, t2b, j, lane), x[j], acc1);

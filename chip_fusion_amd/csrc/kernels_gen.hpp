@@ -488,9 +488,12 @@ __device__ __forceinline__ void gen_gemm(const unsigned char* lds, const GenFrag
         if (t < nt) {
             const bool two = t + 1 < nt;
             const int t1 = two ? t + 1 : t;
-            f16x_t acc0 = {}, acc1 = {};
+            // K-step 0 always exists (every width is at least 32): its
+            // products start from zero, with no accumulator to clear
+            f16x_t acc0 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t, 0), x[0], f16x_t{});
+            f16x_t acc1 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t1, 0), x[0], f16x_t{});
 #pragma unroll
-            for (int j = 0; j < C::MKS; ++j)
+            for (int j = 1; j < C::MKS; ++j)
                 if (j < ks) {
                     acc0 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t, j), x[j], acc0);
                     acc1 = Ty32<SDT>::mma(gen_wfrag(lds, fr, t1, j), x[j], acc1);

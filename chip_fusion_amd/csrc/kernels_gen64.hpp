@@ -271,12 +271,14 @@ __device__ __forceinline__ void gen64_gemm(const unsigned char* lds, const Gen64
             d4_t acc[C::GRP];
             int ti[C::GRP];
 #pragma unroll
-            for (int i = 0; i < C::GRP; ++i) {
-                acc[i] = d4_t{0.0, 0.0, 0.0, 0.0};
-                ti[i] = t + i < nt ? t + i : nt - 1;
-            }
+            for (int i = 0; i < C::GRP; ++i) ti[i] = t + i < nt ? t + i : nt - 1;
+            // K-step 0 always exists: its products start from zero, with no
+            // accumulator to clear
 #pragma unroll
-            for (int j = 0; j < C::MKS; ++j)
+            for (int i = 0; i < C::GRP; ++i)
+                acc[i] = Ty<DT_F64>::mma(gen64_wfrag<FIRST>(lds, fr, ti[i], 0), x[0], d4_t{0.0, 0.0, 0.0, 0.0});
+#pragma unroll
+            for (int j = 1; j < C::MKS; ++j)
                 if (j < ks)
 #pragma unroll
                     for (int i = 0; i < C::GRP; ++i)

@@ -179,24 +179,29 @@ __device__ __forceinline__ void tf32_gemm(const unsigned char* lds, const GenFra
         if (t < nt) {
             const bool two = t + 1 < nt;
             const int t1 = two ? t + 1 : t;
-            f16x_t acc0 = {}, acc1 = {};
-#pragma unroll
-            for (int j = 0; j < C::MKS; ++j)
-                if (j < ks) {
-                    const u4_t wh0 = gen_wfrag(lds, fh, t, j), wl0 = gen_wfrag(lds, fl, t, j);
-                    const u4_t wh1 = gen_wfrag(lds, fh, t1, j), wl1 = gen_wfrag(lds, fl, t1, j);
-                    // the small terms first
-                    if constexpr (C::PASSES == 4) {
-                        acc0 = tf32_mma(wl0, xl[j], acc0);
-                        acc1 = tf32_mma(wl1, xl[j], acc1);
-                    }
-                    acc0 = tf32_mma(wl0, xh[j], acc0);
-                    acc1 = tf32_mma(wl1, xh[j], acc1);
-                    acc0 = tf32_mma(wh0, xl[j], acc0);
-                    acc1 = tf32_mma(wh1, xl[j], acc1);
-                    acc0 = tf32_mma(wh0, xh[j], acc0);
-                    acc1 = tf32_mma(wh1, xh[j], acc1);
+            // one K-step of both chains; K-step 0 always exists (every
+            // width is at least 32) and starts them from zero, with no
+            // accumulator to clear
+            auto kstep = [&](int j, f16x_t c0, f16x_t c1, f16x_t& o0, f16x_t& o1) __attribute__((always_inline)) {
+                const u4_t wh0 = gen_wfrag(lds, fh, t, j), wl0 = gen_wfrag(lds, fl, t, j);
+                const u4_t wh1 = gen_wfrag(lds, fh, t1, j), wl1 = gen_wfrag(lds, fl, t1, j);
+                // the small terms first
+                if constexpr (C::PASSES == 4) {
+                    c0 = tf32_mma(wl0, xl[j], c0);
+                    c1 = tf32_mma(wl1, xl[j], c1);
                 }
+                c0 = tf32_mma(wl0, xh[j], c0);
+                c1 = tf32_mma(wl1, xh[j], c1);
+                c0 = tf32_mma(wh0, xl[j], c0);
+                c1 = tf32_mma(wh1, xl[j], c1);
+                o0 = tf32_mma(wh0, xh[j], c0);
+                o1 = tf32_mma(wh1, xh[j], c1);
+            };
+            f16x_t acc0, acc1;
+            kstep(0, f16x_t{}, f16x_t{}, acc0, acc1);
+#pragma unroll
+            for (int j = 1; j < C::MKS; ++j)
+                if (j < ks) kstep(j, acc0, acc1, acc0, acc1);
             sink(t, acc0, acc1, two);
         }
     }
@@ -213,20 +218,21 @@ __device__ __forceinline__ void tf32_gemm_kouter(const unsigned char* lds, const
         ks = uniform_here(ks);
         nt = uniform_here(nt);
     }
+    // K-step 0 always exists: its products start every tile's chain from
+    // zero (tiles past nt are never computed and never read)
     f16x_t acc[C::MNT];
 #pragma unroll
-    for (int t = 0; t < C::MNT; ++t) acc[t] = f16x_t{};
-#pragma unroll
     for (int j = 0; j < C::MKS; ++j)
-        if (j < ks) {
+        if (j == 0 || j < ks) {
 #pragma unroll
             for (int t = 0; t < C::MNT; ++t)
                 if (t < nt) {
                     const u4_t wh = gen_wfrag(lds, fh, t, j), wl = gen_wfrag(lds, fl, t, j);
-                    if constexpr (C::PASSES == 4) acc[t] = tf32_mma(wl, xl[j], acc[t]);
-                    acc[t] = tf32_mma(wl, xh[j], acc[t]);
-                    acc[t] = tf32_mma(wh, xl[j], acc[t]);
-                    acc[t] = tf32_mma(wh, xh[j], acc[t]);
+                    f16x_t c = j == 0 ? f16x_t{} : acc[t];
+                    if constexpr (C::PASSES == 4) c = tf32_mma(wl, xl[j], c);
+                    c = tf32_mma(wl, xh[j], c);
+                    c = tf32_mma(wh, xl[j], c);
+                    acc[t] = tf32_mma(wh, xh[j], c);
                 }
         }
 #pragma unroll
