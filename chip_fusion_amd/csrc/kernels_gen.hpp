@@ -325,20 +325,29 @@ __device__ __forceinline__ void gen_arrange_a(u4_t (&a)[C::MKS]) {
         }
 }
 
-// a pair of fp32 values rounded to the 16-bit type NDT, or (NDT < 0) to the
-// type `bf` picks at run time
+// 16 fp32 values, in pairs, rounded to the 16-bit type NDT, or (NDT < 0) to
+// the type `bf` picks at run time: one uniform branch for all of them (a
+// select per pair became a branch per pair), on a flag recomputed here
+// rather than held as a lane mask
 template <int NDT>
-__device__ __forceinline__ unsigned gen_pack(float x, float y, bool bf) {
-    if constexpr (NDT >= 0) return Ty<NDT>::pack(x, y);
-    else return bf ? Ty<DT_BF16>::pack(x, y) : Ty<DT_F16>::pack(x, y);
+__device__ __forceinline__ void gen_pack16(const f16x_t& acc, unsigned (&p)[8], bool bf) {
+    if constexpr (NDT >= 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = Ty<NDT>::pack(acc[2 * i], acc[2 * i + 1]);
+    } else if (uniform_here(bf ? 1 : 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = Ty<DT_BF16>::pack(acc[2 * i], acc[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = Ty<DT_F16>::pack(acc[2 * i], acc[2 * i + 1]);
+    }
 }
 
 // Result tile -> two K-steps of the next GEMM's operand (rounded to its type NDT).
 template <class C, int NDT>
 __device__ __forceinline__ void gen_to_operand(const f16x_t& acc, u4_t& o0, u4_t& o1, bool bf = false) {
     unsigned p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = gen_pack<NDT>(acc[2 * i], acc[2 * i + 1], bf);
+    gen_pack16<NDT>(acc, p, bf);
     // K-step s: result registers 8s..8s+7 (packed p[4s..4s+3])
     if constexpr (C::MODE == MODE_PERMLANE) {
         // natural K order: half 0 keeps registers 8s..8s+3 and takes the
@@ -359,8 +368,7 @@ template <class C>
 __device__ __forceinline__ void gen_regroup_d(const f16x_t& acc, u4_t& lo, u4_t& hi, bool bf = false) {
     constexpr int DDT = C::RTM ? -1 : C::stype(C::NST);
     unsigned p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = gen_pack<DDT>(acc[2 * i], acc[2 * i + 1], bf);
+    gen_pack16<DDT>(acc, p, bf);
     swap32(p[0], p[2]);
     swap32(p[1], p[3]);
     swap32(p[4], p[6]);
@@ -609,7 +617,7 @@ __device__ __forceinline__ void gen_body(const KArgs& args) {
         const auto d_rs = tr.rsrc(args.D, args.ldd, args.sD, C::DE, t);
         // run-time types: bit s of args.tmask (uniform) picks GEMM s's instruction and
         // the type its result is rounded into for GEMM s+1 (bit NST: D)
-        auto bf_at = [&](int s) { return C::RTM && ((args.tmask >> s) & 1); };
+        auto bf_at = [&](int s) { return C::RTM && ((uniform_here(args.tmask) >> s) & 1); };
         auto to_d = [&](int tt, const f16x_t& a0, const f16x_t& a1, bool two) __attribute__((always_inline)) {
             if constexpr (C::OUT8) gen_store_pair_f8(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane);
             else gen_store_pair<C>(lds, stg, a0, a1, two, d_rs, args.ldd, 32 * tt, lane, bf_at(C::NST), dt[C::NST]);
