@@ -110,18 +110,21 @@ def test_tf32_unfused(passes):
 
 
 @pytest.mark.parametrize("passes", [3, 4])
-@pytest.mark.parametrize("widths", [(128, 128, 64), (64, 96, 128, 32)])
+@pytest.mark.parametrize("widths", [(128, 128, 64), (64, 96, 128, 32), (128, 128, 128), (128, 128, 128, 64)])
 def test_tf32_integers_exact(widths, passes):
     """A: integers up to 2047 (exact in tf32, low parts nonzero); weights
     ternary (exact in bf16, so no dropped term); the intermediates pass 2^11
-    and are rounded to tf32; every partial sum is an integer below 2^24."""
+    and are rounded to tf32; every partial sum is an integer below 2^24.
+    The last two width sets run the instances with their widths compiled in."""
     _flush(f"tf32 exact x{passes} widths={widths}")
     rng = np.random.default_rng(41)
     A = rng.integers(-2047, 2048, (2, 300, widths[0])).astype(np.float32)
     Bs = [rng.integers(-1, 2, (2, widths[s], widths[s + 1])).astype(np.float32) for s in range(len(widths) - 1)]
     _assert_exact_sums(A, Bs)
     ref = oracle.cascade("tf32", A, Bs)
-    got, _ = _run(A, Bs, tf32_exact=passes == 4)
+    got, info = _run(A, Bs, tf32_exact=passes == 4)
+    compiled = widths in ((128, 128, 128), (128, 128, 128, 64))
+    assert ("widths=compiled" in info) == compiled, info
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
 
 
