@@ -7,6 +7,8 @@ B2B_GEN_TYPED(1, 128, 1, 1);
 B2B_GEN_TYPED(1, 128, 1, 2);
 B2B_GEN_TYPED(1, 256, 0, 1);
 B2B_GEN_TYPED(1, 256, 0, 2);
+B2B_GEN_TYPED(1, 192, 1, 1);
+B2B_GEN_TYPED(1, 192, 1, 2);
 B2B_GEN_TYPED(2, 128, 1, 1);
 B2B_GEN_TYPED(2, 128, 1, 2);
 B2B_GEN_TYPED(2, 128, 1, 3);
@@ -19,6 +21,12 @@ B2B_GEN_TYPED(2, 256, 0, 3);
 B2B_GEN_TYPED(2, 256, 0, 4);
 B2B_GEN_TYPED(2, 256, 0, 5);
 B2B_GEN_TYPED(2, 256, 0, 6);
+B2B_GEN_TYPED(2, 192, 1, 1);
+B2B_GEN_TYPED(2, 192, 1, 2);
+B2B_GEN_TYPED(2, 192, 1, 3);
+B2B_GEN_TYPED(2, 192, 1, 4);
+B2B_GEN_TYPED(2, 192, 1, 5);
+B2B_GEN_TYPED(2, 192, 1, 6);
 // four waves (128-row tiles): two workgroups a CU when the weights take at most 64 KB
 B2B_GEN_TYPED(2, 128, 1, 1, 4);
 B2B_GEN_TYPED(2, 128, 1, 2, 4);
