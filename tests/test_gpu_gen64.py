@@ -52,6 +52,7 @@ CASES = [
     (2, 333, (64, 48, 64, 32, 64)),      # four
     (1, 400, (32, 64, 16, 64, 48, 32)),  # five
     (2, 129, (40, 16)),                  # one GEMM
+    (2, 300, (96, 80, 96)),              # the instance bounded at 96 (one A tile ahead)
 ]
 
 
@@ -65,7 +66,7 @@ def test_f64_runtime_widths(case):
     assert_close("f64", got, oracle.cascade("f64", A, Bs), f"gen64 {widths}")
 
 
-@pytest.mark.parametrize("widths", [(96, 48, 112), (64, 48, 64, 32, 64)])
+@pytest.mark.parametrize("widths", [(96, 48, 112), (64, 48, 64, 32, 64), (96, 96, 48)])
 def test_f64_ternary_exact(widths):
     _flush(f"gen64 ternary widths={widths}")
     A, Bs = _inputs(2, 300, widths, dist="ternary", seed=0x5EED0301)

@@ -35,6 +35,9 @@ FAMILIES = [
      (128, 128, 128, 128, 128, 64), {}),
     ("fp64 run-time widths", "f64", (48, 48, 48), {}),
     ("fp64 run-time widths, four GEMMs", "f64", (64, 64, 64, 64, 64), {}),
+    ("fp64 run-time widths up to 96", "f64", (96, 80, 96), {}),
+    ("32x32x16 fp16 up to 192", "f16", (192, 160, 192), {}),
+    ("32x32x16 bf16 chain up to 192", "bf16", (192, 64, 192, 64, 192), {}),
     ("tf32, two GEMMs", "tf32", (128, 128, 128), {}),
     ("tf32, three GEMMs", "tf32", (128, 128, 128, 64), {}),
     ("fp8 second GEMM", ("f16", "fp8", "f16"), (128, 128, 128), {}),
