@@ -281,8 +281,10 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t plan, int32_t nsets, const void* const* A,
                            void* const* D, hipStream_t stream, int32_t reps);
 
 /* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
-   remap mode, tile, grid, LDS and workspace bytes, kernel launches per run)
-   into buf (NUL-terminated). */
+   remap mode, tile, grid, LDS and workspace bytes, kernel launches per run,
+   whether the kernel pads widths on chip, and whether its widths are compiled
+   in or read at run time) into buf as space-separated key=value pairs,
+   NUL-terminated and cut to len - 1 characters. */
 b2b_status_t b2b_gemm_get_info(b2b_gemm_t plan, char* buf, size_t len);
 
 /* ------------------------------------------------------------------------- */
