@@ -865,13 +865,13 @@ b2b_status_t b2b_gemm_get_info(b2b_gemm_t p, char* buf, size_t len) {
     std::snprintf(buf, len,
                   "path=%s dtype=%s batch=%lld M=%lld dims=%s mfma=%s orient=%s remap=%s mt=%d "
                   "waves=%d rows_per_wg=%d lds_bytes=%d grid=%d workspace_bytes=%lld launches=%d tail=%d "
-                  "widths=%s",
+                  "widths=%s bound=%d",
                   p->unfused ? "unfused" : "fused", dts_s.c_str(), (long long)p->batch,
                   (long long)p->M, dims.c_str(), mfma,
                   p->orn ? "N" : "T", p->unfused ? "none" : modes[p->mode], k->mt, k->waves,
                   k->rows_wg, lds_bytes, p->grid[0],
                   (long long)work, p->unfused ? p->nst : 1, k->tail,
-                  (!k->rtw || k->dims[0]) ? "compiled" : "runtime");
+                  (!k->rtw || k->dims[0]) ? "compiled" : "runtime", k->rtw ? k->maxd : 0);
     return B2B_SUCCESS;
 }
 

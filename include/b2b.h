@@ -282,8 +282,9 @@ b2b_status_t b2b_gemm_tune(b2b_gemm_t plan, int32_t nsets, const void* const* A,
 
 /* Writes a one-line description of the plan (kernel, MFMA shape, orientation,
    remap mode, tile, grid, LDS and workspace bytes, kernel launches per run,
-   whether the kernel pads widths on chip, and whether its widths are compiled
-   in or read at run time) into buf as space-separated key=value pairs,
+   whether the kernel pads widths on chip, whether its widths are compiled
+   in or read at run time, and the width bound of a run-time-width kernel,
+   0 for the fixed-width ones) into buf as space-separated key=value pairs,
    NUL-terminated and cut to len - 1 characters. */
 b2b_status_t b2b_gemm_get_info(b2b_gemm_t plan, char* buf, size_t len);
 

@@ -542,3 +542,19 @@ def test_tail_bounds():
     assert _create(K=250, N1=250, N2=250)[0] == 2          # 2 x 256 x 256 x 2 bytes of weights
     assert _create(dtype=2, K=60, N1=60, N2=60)[0] == 0
     assert _create(dtype=2, K=60, N1=70, N2=60)[0] == 2    # 70 pads to 80 > 64
+
+
+@pytest.mark.parametrize("kw,bound", [
+    (dict(dtype=0, widths=(192, 160, 192)), "192"),        # instances bounded at 192 hold an A tile ahead
+    (dict(dtype=0, widths=(96, 160, 64)), "192"),
+    (dict(dtype=1, widths=(256, 128, 256)), "256"),
+    (dict(dtype=0, widths=(192, 64, 192, 64, 192)), "192"),
+    (dict(dtype=0, widths=(128, 128, 128)), "0"),          # the fixed-width kernel
+    (dict(dtype=2, widths=(96, 96, 96)), "96"),            # fp64, two GEMMs up to 96
+    (dict(dtype=2, widths=(96, 48, 112)), "128"),
+    (dict(dtype=2, widths=(64, 64, 64, 64, 64)), "64"),
+])
+def test_width_bound_selection(kw, bound):
+    """The planner takes the run-time-width instance with the smallest bound
+    that holds every width (the fixed-width kernels report 0)."""
+    assert _chain_info(**kw)["bound"] == bound
