@@ -24,16 +24,22 @@ const MfmaShape& shape_info(Shape s) { return kShapes[s]; }
 // A operand: lane owns one row (lane mod m); lanes are split into groups
 // along k, each holding a contiguous run of a_elems k values.
 void a_coord(Shape s, int lane, int e, int* row, int* k) {
+    B2B_CHECK(s >= 0 && s < SH_COUNT && lane >= 0 && lane < kLanes);
     const MfmaShape& sh = kShapes[s];
+    B2B_CHECK(e >= 0 && e < sh.a_elems);
     *row = lane % sh.m;
     *k = (lane / sh.m) * sh.a_elems + e;
+    B2B_CHECK(*k < sh.k);
 }
 
 // B operand: the mirror image, lane owns one column.
 void b_coord(Shape s, int lane, int e, int* k, int* col) {
+    B2B_CHECK(s >= 0 && s < SH_COUNT && lane >= 0 && lane < kLanes);
     const MfmaShape& sh = kShapes[s];
+    B2B_CHECK(e >= 0 && e < sh.a_elems);
     *col = lane % sh.n;
     *k = (lane / sh.n) * sh.a_elems + e;
+    B2B_CHECK(*k < sh.k);
 }
 
 // Accumulator: lane owns one column.  float32 accumulators: rows come in
@@ -41,15 +47,18 @@ void b_coord(Shape s, int lane, int e, int* k, int* col) {
 // 8 rows.  fp64 16x16x4: rows are interleaved, register e of lane group g
 // holding row g + 4e (measured on gfx950 with a one-instruction probe).
 void c_coord(Shape s, int lane, int e, int* row, int* col) {
+    B2B_CHECK(s >= 0 && s < SH_COUNT && lane >= 0 && lane < kLanes);
     const MfmaShape& sh = kShapes[s];
+    B2B_CHECK(e >= 0 && e < sh.c_elems);
     *col = lane % sh.n;
     int group = lane / sh.n;            // 4 groups of 16 lanes, or 2 of 32
     int groups = kLanes / sh.n;
     if (s == SH_F64_16x16x4) {
         *row = group + groups * e;
-        return;
+    } else {
+        *row = (e / 4) * (4 * groups) + group * 4 + (e % 4);
     }
-    *row = (e / 4) * (4 * groups) + group * 4 + (e % 4);
+    B2B_CHECK(*row < sh.m);
 }
 
 static int gcd_i(int a, int b) { while (b) { int t = a % b; a = b; b = t; } return a; }
@@ -89,8 +98,11 @@ bool build_relation(Shape s, bool orient_n, Relation* out) {
                 auto it = where.find(std::make_pair(m, KW * c + k));
                 if (it == where.end() || used[it->second]) return false;
                 used[it->second] = 1;
+                B2B_CHECK(l * E + c * sh.a_elems + u < (int)out->src_of.size());
                 out->src_of[l * E + c * sh.a_elems + u] = it->second;
             }
+    // every source element feeds exactly one destination
+    B2B_CHECK(std::find(used.begin(), used.end(), 0) == used.end());
     return true;
 }
 

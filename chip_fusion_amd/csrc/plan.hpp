@@ -13,6 +13,25 @@
 #include <cstdint>
 #include <vector>
 
+// Bounds and invariant checks of the planner, compiled in with -DB2B_DEBUG
+// (the CPU sanitizer build turns them on): a failed check names the file,
+// the line and the condition on stderr and aborts.  Without B2B_DEBUG they
+// compile to nothing.
+#ifdef B2B_DEBUG
+#include <cstdio>
+#include <cstdlib>
+#define B2B_CHECK(cond)                                                                  \
+    do {                                                                                 \
+        if (!(cond)) {                                                                   \
+            std::fprintf(stderr, "%s:%d: B2B_DEBUG check failed: %s\n", __FILE__, __LINE__, \
+                         #cond);                                                         \
+            std::abort();                                                                \
+        }                                                                                \
+    } while (0)
+#else
+#define B2B_CHECK(cond) ((void)0)
+#endif
+
 namespace b2b {
 
 enum Shape : int {
